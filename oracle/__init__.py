@@ -1,0 +1,173 @@
+"""CPU oracle for MoE dispatch, reduce-once combine and the fused epilogue.
+
+TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the
+benchmark's CPU-baseline leg are its only users; the product path never
+imports it.  The arithmetic lives in ``moe_oracle.c`` (plain scalar C); this
+module builds it with gcc and wraps it over numpy arrays.  ``brute`` holds a
+second, pure-Python rendering for tiny inputs; ``compare`` holds the
+comparators and the double-reduce detector.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "moe_oracle.c")
+LIBRARY = os.path.join(HERE, "libmoe_oracle.so")
+# -ffp-contract=off: every fused multiply-add in the oracle is an explicit fmaf.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math"]
+
+STATUS_OVERFLOW = 1
+STATUS_BAD_ID = 2
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the oracle with gcc; returns the path of the shared library."""
+    tmp = output + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, source, "-lm"], check=True)
+    os.replace(tmp, output)
+    return output
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    lib.oracle_dispatch.argtypes = [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P]
+    lib.oracle_dispatch.restype = ctypes.c_int
+    lib.oracle_combine.argtypes = [_P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P]
+    lib.oracle_combine.restype = ctypes.c_int
+    lib.oracle_combine_residual_rmsnorm.argtypes = [
+        _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, _P, ctypes.c_float, _P, _P, _P, _P]
+    lib.oracle_combine_residual_rmsnorm.restype = ctypes.c_int
+    for name in ("oracle_bf16_to_f32_array", "oracle_f32_to_bf16_array",
+                 "oracle_f64_to_bf16_array"):
+        getattr(lib, name).argtypes = [_P, _P, _I64]
+        getattr(lib, name).restype = None
+    return lib
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library."""
+
+    def __init__(self, path: str):
+        self.path = path
+        self.lib = _declare(ctypes.CDLL(path))
+
+    # -- codec -----------------------------------------------------------
+    def bf16_to_f32(self, u: np.ndarray) -> np.ndarray:
+        u = np.ascontiguousarray(u, dtype=np.uint16)
+        out = np.empty(u.shape, dtype=np.float32)
+        self.lib.oracle_bf16_to_f32_array(u.ctypes.data, out.ctypes.data, u.size)
+        return out
+
+    def f32_to_bf16(self, a: np.ndarray) -> np.ndarray:
+        a = np.ascontiguousarray(a, dtype=np.float32)
+        out = np.empty(a.shape, dtype=np.uint16)
+        self.lib.oracle_f32_to_bf16_array(a.ctypes.data, out.ctypes.data, a.size)
+        return out
+
+    def f64_to_bf16(self, a: np.ndarray) -> np.ndarray:
+        a = np.ascontiguousarray(a, dtype=np.float64)
+        out = np.empty(a.shape, dtype=np.uint16)
+        self.lib.oracle_f64_to_bf16_array(a.ctypes.data, out.ctypes.data, a.size)
+        return out
+
+    # -- the method --------------------------------------------------------
+    def dispatch(self, x: np.ndarray, ids: np.ndarray, ep: int, epr: int, cap: int,
+                 ws: Optional[np.ndarray] = None, src_fill: int = -1) -> "DispatchResult":
+        """Route every copy into the padded workspace.
+
+        ``ws`` may be passed in (e.g. pre-filled with canaries); otherwise an
+        uninitialised [ep, cap, H] array is allocated, whose padding rows stay
+        untouched (so never committed to memory by the OS).
+        """
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        T, H = x.shape
+        k = ids.shape[1] if ids.ndim == 2 else (ids.size // T if T else 0)
+        if ws is None:
+            ws = np.empty((ep, cap, H), dtype=np.uint16)
+        assert ws.dtype == np.uint16 and ws.flags.c_contiguous and ws.size == ep * cap * H
+        counts = np.zeros(ep, dtype=np.int32)
+        slot_index = np.empty(T * k, dtype=np.int32)
+        src_index = np.full(ep * cap, src_fill, dtype=np.int32)
+        status = self.lib.oracle_dispatch(
+            x.ctypes.data, ids.ctypes.data, T, H, k, ep, epr, cap, ws.ctypes.data,
+            counts.ctypes.data, slot_index.ctypes.data, src_index.ctypes.data)
+        return DispatchResult(ws=ws, counts=counts, slot_index=slot_index.reshape(T, k),
+                              src_index=src_index.reshape(ep, cap), status=status)
+
+    def combine(self, y: np.ndarray, slot_index: np.ndarray, weights: Optional[np.ndarray],
+                weighted: bool, H: int) -> np.ndarray:
+        y = np.ascontiguousarray(y, dtype=np.uint16)
+        slot_index = np.ascontiguousarray(slot_index, dtype=np.int32)
+        T, k = slot_index.shape
+        w = np.ascontiguousarray(weights if weights is not None else np.zeros((T, k)),
+                                 dtype=np.float32)
+        out = np.empty((T, H), dtype=np.uint16)
+        self.lib.oracle_combine(y.ctypes.data, slot_index.ctypes.data, w.ctypes.data,
+                                int(bool(weighted)), T, H, k, out.ctypes.data)
+        return out
+
+    def combine_residual_rmsnorm(self, y, slot_index, weights, weighted: bool,
+                                 residual: np.ndarray, gamma: np.ndarray, eps: float,
+                                 want_f64: bool = False):
+        """Returns (residual_out, normed[, normed_f64])."""
+        y = np.ascontiguousarray(y, dtype=np.uint16)
+        slot_index = np.ascontiguousarray(slot_index, dtype=np.int32)
+        residual = np.ascontiguousarray(residual, dtype=np.uint16)
+        gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+        T, k = slot_index.shape
+        H = residual.shape[1]
+        w = np.ascontiguousarray(weights if weights is not None else np.zeros((T, k)),
+                                 dtype=np.float32)
+        res_out = np.empty((T, H), dtype=np.uint16)
+        normed = np.empty((T, H), dtype=np.uint16)
+        nf64 = np.empty((T, H), dtype=np.float64) if want_f64 else None
+        scratch = np.empty(H, dtype=np.float32)
+        self.lib.oracle_combine_residual_rmsnorm(
+            y.ctypes.data, slot_index.ctypes.data, w.ctypes.data, int(bool(weighted)),
+            T, H, k, residual.ctypes.data, gamma.ctypes.data, float(eps),
+            res_out.ctypes.data, normed.ctypes.data,
+            nf64.ctypes.data if want_f64 else None, scratch.ctypes.data)
+        return (res_out, normed, nf64) if want_f64 else (res_out, normed)
+
+
+@dataclass
+class DispatchResult:
+    ws: np.ndarray           # uint16 [ep, cap, H]
+    counts: np.ndarray       # int32 [ep]
+    slot_index: np.ndarray   # int32 [T, k]
+    src_index: np.ndarray    # int32 [ep, cap]
+    status: int
+
+
+_DEFAULT: Optional[Oracle] = None
+
+
+def load(rebuild: bool = False) -> Oracle:
+    """The oracle built from ``moe_oracle.c`` (compiled on first use)."""
+    global _DEFAULT
+    if _DEFAULT is None or rebuild:
+        stale = (not os.path.exists(LIBRARY)
+                 or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE))
+        if rebuild or stale:
+            build()
+        _DEFAULT = Oracle(LIBRARY)
+    return _DEFAULT
+
+
+def place_expert_outputs(ws: np.ndarray, slot_index: np.ndarray, y_rows: np.ndarray) -> None:
+    """Expert stage: write each copy's output row into the row it was routed to."""
+    flat = ws.reshape(-1, ws.shape[-1])
+    s = slot_index.reshape(-1)
+    valid = s >= 0
+    flat[s[valid]] = y_rows[valid]

@@ -1,0 +1,225 @@
+/*
+ * CPU oracle for MoE token dispatch, reduce-once combine, and the fused
+ * residual-add + RMSNorm epilogue.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or helper with
+ * the HIP library; it is plain scalar C, slow on purpose, written so that each
+ * loop can be checked against the pages by eye.
+ *
+ * Sources (web pages; the build cites them by title and section):
+ *  [A2A]  InferenceX PR #2450, "CollectiveX: add FlashInfer one-sided NVLink
+ *         EP for the GB SKUs".  Sections used: "The adapter" table (padded
+ *         [ep_size, runtime_max_tokens_per_rank, hidden] receive, valid slots
+ *         only, workspace sized once), "Verified: per-rank permutation"
+ *         (slot order inside a region is the implementation's choice),
+ *         "Kernel arithmetic read from source" (nearest-even narrowing, one
+ *         narrowing store), "Update -- the correctness failures are resolved"
+ *         (the combine accumulates in fp32 and narrows once; a bf16
+ *         accumulator was the defect).
+ *  [DR]   vLLM PR #41382, "[Bugfix] Fix double reduce in
+ *         flashinfer_nvlink_two_sided and flashinfer_nvlink_one_sided
+ *         backends", description and review thread: the all-to-all combine
+ *         already sums over the experts dimension, so its output is final and
+ *         must not be reduced a second time.
+ *  [FUSE] magik.net, "Fusing the Allreduce: A Precision Investigation into
+ *         FlashInfer's Verify-Path Optimization", section "The Message
+ *         Itself: Explanation and Probe": residual add and RMSNorm fused onto
+ *         the reduction that produces the hidden state.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - one workspace row per routed copy (t, j); region of expert e = e / epr;
+ *  - rows fill a region in increasing flat index f = t*k + j (stable order);
+ *  - expert id -1 means "no expert" (no row, contributes nothing); any other
+ *    id outside [0, E) is an error and is likewise skipped;
+ *  - a copy whose region is already full is an overflow error, not written;
+ *    counts[r] still reports how many copies region r was sent;
+ *  - weighted combine term: fmaf(w, y, acc); unweighted: acc + y; terms taken
+ *    in j = 0..k-1 order, fp32 accumulator, single nearest-even narrowing;
+ *  - fused epilogue: s = acc + residual in fp32 (the accumulator is not
+ *    narrowed first); residual_out = bf16(s); the mean of squares, the
+ *    reciprocal square root and the scaling by gamma in fp64 (the oracle is
+ *    the more precise side), eps inside the square root, mean over H.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_STATUS_OVERFLOW 1
+#define ORACLE_STATUS_BAD_ID 2
+
+/* ---- bf16 codec, from the IEEE 754 definition -------------------------------
+ * bfloat16 is binary32 with the low 16 fraction bits dropped: 1 sign bit,
+ * 8 exponent bits (bias 127), 7 stored fraction bits.  Decoding is exact: the
+ * 16 stored bits are the high half of the binary32 pattern.  Encoding rounds
+ * a real value to the nearest bfloat16, ties to the even significand:
+ * normal numbers in [2^(e-1), 2^e) are spaced 2^(e-8); subnormals (below
+ * 2^-126) are spaced 2^-133; magnitudes that round beyond the largest finite
+ * value (2 - 2^-7) * 2^127 become infinity. */
+
+float oracle_bf16_to_f32(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+uint16_t oracle_f64_to_bf16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7FC0u);
+    double a = fabs(v);
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7F80u);
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);                      /* a in [2^(e-1), 2^e) */
+    int qexp = e - 8;                  /* spacing of 8-significant-bit values */
+    if (qexp < -133)
+        qexp = -133;                   /* subnormal spacing */
+    double q = nearbyint(ldexp(a, -qexp));   /* default mode: ties to even */
+    double r = ldexp(q, qexp);
+    if (r >= ldexp(1.0, 128))
+        return (uint16_t)(sign | 0x7F80u);
+    float rf = (float)r;               /* exact: r has <= 8 significant bits */
+    uint32_t bits;
+    memcpy(&bits, &rf, sizeof bits);
+    return (uint16_t)(sign | (bits >> 16));
+}
+
+uint16_t oracle_f32_to_bf16(float v)
+{
+    return oracle_f64_to_bf16((double)v);    /* float -> double is exact */
+}
+
+/* ---- dispatch ([A2A] "The adapter" table) -----------------------------------
+ * x         [T, H] bf16, ids [T, k] int32 (flat index f = t*k + j)
+ * ws        [ep, cap, H] bf16; row (r, s) receives copy number s of region r
+ * counts    [ep]   copies sent to each region (not clamped to cap)
+ * slot_index[T*k]  r*cap + s of the row holding copy f, or -1
+ * src_index [ep*cap] f of the copy held by row (r, s), for s < min(counts, cap);
+ *           entries past the valid prefix are left untouched, as are the
+ *           padding rows of ws.
+ * Returns a bit set of ORACLE_STATUS_* flags. */
+int oracle_dispatch(const uint16_t *x, const int32_t *ids,
+                    int64_t T, int64_t H, int64_t k, int64_t ep, int64_t epr,
+                    int64_t cap, uint16_t *ws, int32_t *counts,
+                    int32_t *slot_index, int32_t *src_index)
+{
+    int status = 0;
+    int64_t E = ep * epr;
+    for (int64_t r = 0; r < ep; ++r)
+        counts[r] = 0;
+    for (int64_t f = 0; f < T * k; ++f) {
+        int32_t e = ids[f];
+        slot_index[f] = -1;
+        if (e == -1)
+            continue;
+        if (e < 0 || e >= E) {
+            status |= ORACLE_STATUS_BAD_ID;
+            continue;
+        }
+        int64_t r = e / epr;
+        int64_t s = counts[r];
+        counts[r] += 1;
+        if (s >= cap) {
+            status |= ORACLE_STATUS_OVERFLOW;
+            continue;
+        }
+        int64_t row = r * cap + s;
+        slot_index[f] = (int32_t)row;
+        src_index[row] = (int32_t)f;
+        memcpy(ws + row * H, x + (f / k) * H, (size_t)H * sizeof(uint16_t));
+    }
+    return status;
+}
+
+/* ---- combine: reduce exactly once ([A2A] "Update -- ... resolved", [DR]) ----
+ * out[t, h] = bf16( sum over j = 0..k-1 with slot_index[t,j] >= 0 of
+ *                   c_j * f32(y[slot_index[t,j], h]) )
+ * accumulated in fp32 in j order; c_j = w[t, j] (weighted) or 1 (unweighted).
+ * out is overwritten, never accumulated into. */
+static float combine_accumulate(const uint16_t *y, const int32_t *slot_index,
+                                const float *w, int weighted, int64_t t,
+                                int64_t h, int64_t H, int64_t k)
+{
+    float acc = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+        int32_t row = slot_index[t * k + j];
+        if (row < 0)
+            continue;
+        float v = oracle_bf16_to_f32(y[(int64_t)row * H + h]);
+        if (weighted)
+            acc = fmaf(w[t * k + j], v, acc);
+        else
+            acc = acc + v;
+    }
+    return acc;
+}
+
+int oracle_combine(const uint16_t *y, const int32_t *slot_index, const float *w,
+                   int weighted, int64_t T, int64_t H, int64_t k, uint16_t *out)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h)
+            out[t * H + h] = oracle_f32_to_bf16(
+                combine_accumulate(y, slot_index, w, weighted, t, h, H, k));
+    return 0;
+}
+
+/* ---- combine + residual add + RMSNorm ([FUSE]) ------------------------------
+ * s[h]            = acc[h] + f32(residual[t, h])          (fp32)
+ * residual_out    = bf16(s)
+ * normed[t, h]    = bf16( s[h] / sqrt(mean_h(s^2) + eps) * f32(gamma[h]) )
+ * residual_out may alias residual (each element is read before it is written).
+ * normed_f64, if not NULL, receives the unrounded fp64 normed values.
+ * s_scratch is caller memory of H floats. */
+int oracle_combine_residual_rmsnorm(const uint16_t *y, const int32_t *slot_index,
+                                    const float *w, int weighted, int64_t T,
+                                    int64_t H, int64_t k, const uint16_t *residual,
+                                    const uint16_t *gamma, float eps,
+                                    uint16_t *residual_out, uint16_t *normed,
+                                    double *normed_f64, float *s_scratch)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        double sumsq = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            float acc = combine_accumulate(y, slot_index, w, weighted, t, h, H, k);
+            float s = acc + oracle_bf16_to_f32(residual[t * H + h]);
+            s_scratch[h] = s;
+            sumsq += (double)s * (double)s;
+        }
+        double inv = 1.0 / sqrt(sumsq / (double)H + (double)eps);
+        for (int64_t h = 0; h < H; ++h) {
+            double n = (double)s_scratch[h] * inv * (double)oracle_bf16_to_f32(gamma[h]);
+            residual_out[t * H + h] = oracle_f32_to_bf16(s_scratch[h]);
+            normed[t * H + h] = oracle_f64_to_bf16(n);
+            if (normed_f64)
+                normed_f64[t * H + h] = n;
+        }
+    }
+    return 0;
+}
+
+/* ---- array forms of the codec, for the test suite ---------------------------- */
+void oracle_bf16_to_f32_array(const uint16_t *in, float *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_to_f32(in[i]);
+}
+
+void oracle_f32_to_bf16_array(const float *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f32_to_bf16(in[i]);
+}
+
+void oracle_f64_to_bf16_array(const double *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f64_to_bf16(in[i]);
+}

@@ -1,0 +1,13 @@
+"""Seeded synthetic workloads shared by the oracle-side tests and the HIP path.
+
+Holds shapes, random draws and the synthetic expert stage only.
+"""
+from .configs import ALL, BY_NAME, DECODE, FUSED, PREFILL, SKEWED, TINY, Workload
+from .inputs import (Inputs, bf16_bits_to_f32, draw_routing, draw_softmax_weights,
+                     expert_outputs, f32_to_bf16_bits, make_inputs)
+
+__all__ = [
+    "ALL", "BY_NAME", "DECODE", "FUSED", "PREFILL", "SKEWED", "TINY", "Workload",
+    "Inputs", "bf16_bits_to_f32", "draw_routing", "draw_softmax_weights",
+    "expert_outputs", "f32_to_bf16_bits", "make_inputs",
+]

@@ -1,0 +1,114 @@
+"""Plant plausible mistakes in copies of the oracle and check the pins catch each.
+
+Every mutation rewrites one expression of ``oracle/moe_oracle.c`` (a dropped
+term, a wrong index or operand, a bf16 accumulator, a wrong rounding mode, a
+misplaced epsilon ...), compiles the copy with gcc into a temporary folder and
+runs the whole pin battery against it.  The unmodified oracle passes every
+pin; each mutant must fail at least one.  Mutations are chosen to stay inside
+the buffers, so a broken copy can only compute wrong values.
+"""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+MUTATIONS = [
+    # combine
+    ("drop_last_term",
+     "for (int64_t j = 0; j < k; ++j) {\n        int32_t row = slot_index[t * k + j];",
+     "for (int64_t j = 0; j < k - 1; ++j) {\n        int32_t row = slot_index[t * k + j];"),
+    ("bf16_accumulator",
+     "acc = acc + v;",
+     "acc = oracle_bf16_to_f32(oracle_f32_to_bf16(acc + v));"),
+    ("bf16_accumulator_weighted",
+     "acc = fmaf(w[t * k + j], v, acc);",
+     "acc = oracle_bf16_to_f32(oracle_f32_to_bf16(fmaf(w[t * k + j], v, acc)));"),
+    ("gates_ignored",
+     "acc = fmaf(w[t * k + j], v, acc);",
+     "acc = fmaf(1.0f, v, acc);"),
+    ("gates_reversed",
+     "acc = fmaf(w[t * k + j], v, acc);",
+     "acc = fmaf(w[t * k + (k - 1 - j)], v, acc);"),
+    ("subtract_term",
+     "acc = acc + v;",
+     "acc = acc - v;"),
+    ("weighted_sum_reduced_twice",
+     "acc = fmaf(w[t * k + j], v, acc);",
+     "acc = fmaf(w[t * k + j], v, acc) + fmaf(w[t * k + j], v, 0.0f) * (j == k - 1);"),
+    # codec
+    ("truncate_instead_of_round",
+     "double q = nearbyint(ldexp(a, -qexp));",
+     "double q = floor(ldexp(a, -qexp));"),
+    ("ties_away_from_zero",
+     "double q = nearbyint(ldexp(a, -qexp));",
+     "double q = round(ldexp(a, -qexp));"),
+    ("no_subnormal_floor",
+     "if (qexp < -133)\n        qexp = -133;",
+     "if (qexp < -160)\n        qexp = -160;"),
+    ("decode_wrong_shift",
+     "uint32_t bits = (uint32_t)h << 16;",
+     "uint32_t bits = (uint32_t)h << 15;"),
+    # dispatch
+    ("region_by_modulo",
+     "int64_t r = e / epr;",
+     "int64_t r = e % ep;"),
+    ("src_index_holds_token",
+     "src_index[row] = (int32_t)f;",
+     "src_index[row] = (int32_t)(f / k);"),
+    ("copy_wrong_row",
+     "memcpy(ws + row * H, x + (f / k) * H, (size_t)H * sizeof(uint16_t));",
+     "memcpy(ws + row * H, x + (f % k) * H, (size_t)H * sizeof(uint16_t));"),
+    ("rows_fill_from_the_end",
+     "int64_t row = r * cap + s;",
+     "int64_t row = r * cap + (cap - 1 - s);"),
+    ("all_negative_ids_silent",
+     "if (e == -1)\n            continue;",
+     "if (e < 0)\n            continue;"),
+    ("counts_clamped",
+     "status |= ORACLE_STATUS_OVERFLOW;",
+     "status |= ORACLE_STATUS_OVERFLOW; counts[r] -= 1;"),
+    # fused epilogue
+    ("eps_outside_sqrt",
+     "double inv = 1.0 / sqrt(sumsq / (double)H + (double)eps);",
+     "double inv = 1.0 / (sqrt(sumsq / (double)H) + (double)eps);"),
+    ("sum_not_mean",
+     "double inv = 1.0 / sqrt(sumsq / (double)H + (double)eps);",
+     "double inv = 1.0 / sqrt(sumsq + (double)eps);"),
+    ("gamma_dropped",
+     "double n = (double)s_scratch[h] * inv * (double)oracle_bf16_to_f32(gamma[h]);",
+     "double n = (double)s_scratch[h] * inv;"),
+    ("residual_not_added",
+     "float s = acc + oracle_bf16_to_f32(residual[t * H + h]);",
+     "float s = acc;"),
+    ("residual_out_from_combine_only",
+     "residual_out[t * H + h] = oracle_f32_to_bf16(s_scratch[h]);",
+     "residual_out[t * H + h] = oracle_f32_to_bf16(s_scratch[h] - oracle_bf16_to_f32(residual[t * H + h]));"),
+]
+
+
+def _failed_pins(o):
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(o)
+        except AssertionError:
+            failed.append(pin.__name__)
+    return failed
+
+
+def test_unmodified_oracle_passes_every_pin(orc):
+    assert _failed_pins(orc) == []
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(tmp_path, name, old, new):
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mutated = os.path.join(tmp_path, "mutant.c")
+    with open(mutated, "w") as fh:
+        fh.write(src.replace(old, new))
+    lib = oracle.build(mutated, os.path.join(tmp_path, f"libmutant_{name}.so"))
+    failed = _failed_pins(oracle.Oracle(lib))
+    assert failed, f"mutation {name} passed every pin"
