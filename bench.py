@@ -1,0 +1,253 @@
+"""Benchmark of the MoE dispatch + combine hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+
+A step is one pass of the hot path over one batch of synthetic input already
+resident in HBM: dispatch (route + stable scan + row copies) -> identity
+expert stage (the expert outputs are the dispatched rows, in place) ->
+combine (reduce once).  On the fused workload the combine is the fused
+combine + residual add + RMSNorm.  W untimed steps, then K timed steps
+bracketed by device synchronisation; one JSON line is printed.
+
+``value`` is tokens/s of the headline workload (prefill: 4096 tokens,
+hidden 7168, top-8 of 256 experts over 8 regions, unweighted combine).  The
+line also carries:
+  roofline      the dominant kernel (the combine kernel: one launch per
+                moe_combine call, timed with HIP events on the launch stream
+                inside the timed steps) against MI355X's 8 TB/s HBM peak,
+                algorithmic bytes per launch / mean launch time; ``traffic``
+                is the measured HBM bytes per launch from the committed
+                rocprofv3 counter summary, or null if the kernel source has
+                changed since those counters were taken
+  cpu_baseline  the CPU oracle (plain scalar C, one thread) timed on the
+                same workload, repeated for about 10 s
+  workloads     the same step on the skewed, decode and fused workloads
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+PROFILE = os.path.join(ROOT, "profiles", "combine_prefill_counters.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "combine_moe_dispatch_03_amd", "csrc", "kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per combine launch from the committed counter summary, if
+    the kernels are unchanged since it was taken."""
+    if not os.path.exists(PROFILE):
+        return None
+    fields = {}
+    with open(PROFILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def describe(wl, cap) -> str:
+    mode = {"weighted": "weighted combine", "unweighted": "unweighted combine",
+            "both": "weighted combine", "fused": "weighted combine + residual + RMSNorm"}[wl.combine]
+    return (f"{wl.name}: T={wl.T} H={wl.H} E={wl.E} top-{wl.k} ep={wl.ep} cap={cap} "
+            f"rung={wl.R} {wl.routing} routing, {mode}")
+
+
+def measure(wl, steps: int, warmup: int, seed: int = 0) -> dict:
+    import numpy as np
+    import torch
+
+    import combine_moe_dispatch_03_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    inp = synth.make_inputs(wl, seed)
+    x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    ids = torch.from_numpy(inp.ids).to(dev)
+    weighted = wl.combine in ("weighted", "both", "fused")
+    w = torch.from_numpy(inp.weights).to(dev) if weighted else None
+    cap = wl.cap
+    if cap is None:                              # size the regions from the routing itself
+        probe = moe.MoeA2A(wl.T, wl.H, wl.k, wl.E, wl.ep, 1, device=dev)
+        cap = int(moe.moe_route_counts(probe, ids).max().item())
+        del probe
+    h = moe.MoeA2A(wl.R, wl.H, wl.k, wl.E, wl.ep, cap, device=dev)
+    ws = h.new_workspace()
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+    fused = wl.combine == "fused"
+    if fused:
+        res = torch.from_numpy(inp.residual.view(np.int16)).to(dev).view(torch.bfloat16)
+        gamma = torch.from_numpy(inp.gamma.view(np.int16)).to(dev).view(torch.bfloat16)
+        res_out = torch.empty_like(res)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        moe.moe_dispatch(h, x, ids, wl.R, ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if fused:
+            moe.moe_combine_residual_rmsnorm(h, ws, w, True, res, gamma, wl.eps,
+                                             residual_out=res_out, normed=out, stream=stream)
+        else:
+            moe.moe_combine(h, ws, w, weighted, out=out, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    code, bits = moe.moe_sync_status(h, stream)
+    if code != moe.MOE_OK:
+        raise RuntimeError(f"device status {bits} after warmup: {moe.moe_strerror(code)}")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(events[s])
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    code, bits = moe.moe_sync_status(h, stream)
+    if code != moe.MOE_OK:
+        raise RuntimeError(f"device status {bits} after timing: {moe.moe_strerror(code)}")
+    d_ms = [e[0].elapsed_time(e[1]) for e in events]
+    c_ms = [e[1].elapsed_time(e[2]) for e in events]
+    b = wl.algorithmic_bytes()
+    comb_bytes = b["fused"] if fused else b["combine"]
+    ms = elapsed * 1e3 / steps
+    res_d = {
+        "workload": describe(wl, cap),
+        "ms_per_step": ms,
+        "tokens_per_s": wl.T / (ms / 1e3),
+        "step_gbs": (b["dispatch"] + comb_bytes) / (ms / 1e3) / 1e9,
+        "dispatch_ms_mean": float(np.mean(d_ms)), "dispatch_ms_p50": float(np.median(d_ms)),
+        "combine_ms_mean": float(np.mean(c_ms)), "combine_ms_p50": float(np.median(c_ms)),
+        "dispatch_bytes": b["dispatch"], "combine_bytes": comb_bytes,
+    }
+    res_d["dispatch_gbs"] = b["dispatch"] / (res_d["dispatch_ms_mean"] / 1e3) / 1e9
+    res_d["combine_gbs"] = comb_bytes / (res_d["combine_ms_mean"] / 1e3) / 1e9
+    res_d["step_hbm_frac"] = res_d["step_gbs"] / HBM_PEAK_GBS
+    del ws, h
+    torch.cuda.empty_cache()
+    return res_d
+
+
+def cpu_baseline(wl, seconds: float = 10.0, seed: int = 0) -> dict:
+    """The CPU oracle (dispatch + identity stage + combine) on the same
+    workload, repeated until about ``seconds`` of CPU work."""
+    import oracle
+    import synth
+
+    orc = oracle.load()
+    inp = synth.make_inputs(wl, seed)
+    weighted = wl.combine in ("weighted", "both", "fused")
+    reps, t_total = 0, 0.0
+    while t_total < seconds:
+        t0 = time.perf_counter()
+        d = orc.dispatch(inp.x, inp.ids, wl.ep, wl.epr, wl.cap)
+        orc.combine(d.ws, d.slot_index, inp.weights, weighted, wl.H)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        del d
+    return {"value": wl.T * reps / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full {wl.name} workload ({wl.T} tokens, dispatch + combine), "
+                      f"{reps} repetition(s), {t_total:.1f} s, single-threaded scalar C"}
+
+
+def calibrate_copy(nbytes: int, reps: int) -> None:
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--extras", default="skewed,decode,fused",
+                    help="comma-separated workloads also measured (empty for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES bytes (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build's workload runs on one GPU's share "
+              "(the destination regions are partitions of local HBM); --gpus must be 1.",
+              file=sys.stderr)
+        return 2
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, max(args.steps, 1))
+        return 0
+
+    import synth
+    wl = synth.BY_NAME[args.workload]
+    main_res = measure(wl, args.steps, args.warmup)
+    extras = {}
+    for name in [n for n in args.extras.split(",") if n and n != wl.name]:
+        extras[name] = measure(synth.BY_NAME[name], max(args.steps // 2, 5), max(args.warmup // 2, 2))
+
+    comb_ms = main_res["combine_ms_mean"]
+    achieved = main_res["combine_bytes"] / (comb_ms / 1e3) / 1e9
+    line = {
+        "metric": "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), H=7168 top-8",
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 tokens, uniform distinct top-8 routing)",
+        "config": {"workload": main_res["workload"], "tokens": wl.T, "hidden": wl.H,
+                   "top_k": wl.k, "experts": wl.E, "ep_size": wl.ep,
+                   "step": "dispatch -> identity expert stage -> combine"},
+        "achieved_gbs": main_res["step_gbs"],
+        "hbm_frac": main_res["step_hbm_frac"],
+        "roofline": {"bound": "hbm", "kernel": "combine_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(),
+                     "algorithmic_bytes_per_launch": main_res["combine_bytes"],
+                     "launch_ms_mean": comb_ms},
+        "kernels": {"dispatch_ms_mean": main_res["dispatch_ms_mean"],
+                    "dispatch_gbs": main_res["dispatch_gbs"],
+                    "combine_ms_mean": comb_ms, "combine_gbs": main_res["combine_gbs"]},
+        "workloads": extras,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,292 @@
+"""MI355X MoE token dispatch / reduce-once combine / fused residual + RMSNorm.
+
+Thin Python binding over the C ABI of ``libmoe_a2a.so`` (declared in
+``include/moe_a2a.h``).  Every step of the path runs in the library's gfx950
+kernels; this module only checks tensor shapes and dtypes, passes raw device
+pointers and the current HIP stream, and turns return codes into exceptions.
+PyTorch provides device memory and streams.  There is no fallback: if the
+library is missing the import of the functions fails loudly.
+
+Functions carry the C names:
+
+  moe_dispatch, moe_combine, moe_combine_residual_rmsnorm, moe_route_counts,
+  moe_sync_status, moe_reset, moe_output_is_reduced, moe_strerror,
+  moe_workspace_bytes, moe_scratch_bytes
+
+and ``MoeA2A`` owns one ``moe_handle`` plus the device buffers it binds.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libmoe_a2a.so")
+
+MOE_OK = 0
+MOE_ERR_ARG = -1
+MOE_ERR_PHASE = -2
+MOE_ERR_OVERFLOW = -3
+MOE_ERR_EXPERT_ID = -4
+MOE_ERR_HIP = -5
+MOE_STATUS_OVERFLOW = 1
+MOE_STATUS_EXPERT_ID = 2
+MOE_MAX_EP = 256
+MOE_MAX_TOP_K = 64
+MOE_MAX_FUSED_HIDDEN = 16384
+
+EXPORTED = (
+    "moe_workspace_bytes", "moe_scratch_bytes", "moe_init", "moe_dispatch", "moe_combine",
+    "moe_combine_residual_rmsnorm", "moe_route_counts", "moe_sync_status", "moe_reset",
+    "moe_output_is_reduced", "moe_strerror",
+)
+
+
+class MoeHandle(ctypes.Structure):
+    """Mirror of ``struct moe_handle``."""
+    _fields_ = [
+        ("max_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+        ("ep_size", ctypes.c_int32), ("experts_per_rank", ctypes.c_int32),
+        ("max_tokens_per_rank", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("counts", ctypes.c_void_p), ("src_index", ctypes.c_void_p),
+        ("slot_index", ctypes.c_void_p), ("status", ctypes.c_void_p),
+        ("scratch", ctypes.c_void_p), ("scratch_bytes", ctypes.c_size_t),
+        ("phase", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+        ("runtime_max_tokens_per_rank", ctypes.c_int32), ("hip_error", ctypes.c_int32),
+    ]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        super().__init__(f"{what}: {moe_strerror(code)} (code {code})" if what else moe_strerror(code))
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"{LIBRARY} is missing: build it with "
+                               "`python -m combine_moe_dispatch_03_amd.build`")
+        lib = ctypes.CDLL(LIBRARY)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        H = ctypes.POINTER(MoeHandle)
+        sig = {
+            "moe_workspace_bytes": (SZ, [I32, I32, I32]),
+            "moe_scratch_bytes": (SZ, [I32, I32, I32]),
+            "moe_init": (ctypes.c_int, [H, I32, I32, I32, I32, I32, I32, P, P, P, P, P, SZ]),
+            "moe_dispatch": (ctypes.c_int, [H, P, P, I32, I32, P, P]),
+            "moe_combine": (ctypes.c_int, [H, P, P, I32, P, P]),
+            "moe_combine_residual_rmsnorm": (ctypes.c_int,
+                                             [H, P, P, I32, P, P, P, ctypes.c_float, P, P]),
+            "moe_route_counts": (ctypes.c_int, [H, P, I32, P]),
+            "moe_sync_status": (ctypes.c_int, [H, P, ctypes.POINTER(I32)]),
+            "moe_reset": (ctypes.c_int, [H]),
+            "moe_output_is_reduced": (ctypes.c_int, []),
+            "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+# ---------------------------------------------------------------- helpers
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None, numel=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+def _check(code: int, what: str) -> None:
+    if code != MOE_OK:
+        raise MoeError(code, what)
+
+
+# ---------------------------------------------------------------- C names
+
+def moe_workspace_bytes(ep_size: int, max_tokens_per_rank: int, hidden: int) -> int:
+    return library().moe_workspace_bytes(ep_size, max_tokens_per_rank, hidden)
+
+
+def moe_scratch_bytes(max_tokens: int, top_k: int, ep_size: int) -> int:
+    return library().moe_scratch_bytes(max_tokens, top_k, ep_size)
+
+
+def moe_output_is_reduced() -> bool:
+    return bool(library().moe_output_is_reduced())
+
+
+def moe_strerror(code: int) -> str:
+    return library().moe_strerror(code).decode()
+
+
+class MoeA2A:
+    """One ``moe_handle`` and the device buffers it binds (allocated once at
+    the ladder maximum)."""
+
+    def __init__(self, max_tokens: int, hidden: int, top_k: int, num_experts: int,
+                 ep_size: int, max_tokens_per_rank: int, device=None):
+        dev = torch.device(device if device is not None else "cuda")
+        lib = library()
+        self.handle = MoeHandle()
+        nbytes = lib.moe_scratch_bytes(max_tokens, top_k, ep_size)
+        if nbytes == 0:
+            raise MoeError(MOE_ERR_ARG, "moe_scratch_bytes")
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.counts = torch.zeros(ep_size, **i32)
+        self.src_index = torch.full((ep_size * max_tokens_per_rank,), -1, **i32)
+        self.slot_index = torch.full((max_tokens * top_k,), -1, **i32)
+        self.status = torch.zeros(1, **i32)
+        self.scratch = torch.zeros((nbytes + 3) // 4, **i32)
+        _check(lib.moe_init(ctypes.byref(self.handle), max_tokens, hidden, top_k, num_experts,
+                            ep_size, max_tokens_per_rank, _ptr(self.counts), _ptr(self.src_index),
+                            _ptr(self.slot_index), _ptr(self.status), _ptr(self.scratch),
+                            self.scratch.numel() * 4), "moe_init")
+        self.device = dev
+
+    # shapes
+    @property
+    def hidden(self) -> int: return self.handle.hidden
+    @property
+    def top_k(self) -> int: return self.handle.top_k
+    @property
+    def ep_size(self) -> int: return self.handle.ep_size
+    @property
+    def cap(self) -> int: return self.handle.max_tokens_per_rank
+    @property
+    def num_tokens(self) -> int: return self.handle.num_tokens
+
+    def new_workspace(self, fill_bits: Optional[int] = None) -> torch.Tensor:
+        """A [ep, cap, H] bf16 workspace; optionally every element set to one
+        bf16 bit pattern (e.g. a NaN canary for the padding)."""
+        shape = (self.ep_size, self.cap, self.hidden)
+        if fill_bits is None:
+            return torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+        w = torch.empty(shape, dtype=torch.int16, device=self.device)
+        w.fill_(fill_bits - 65536 if fill_bits >= 32768 else fill_bits)
+        return w.view(torch.bfloat16)
+
+    def slot_index_view(self) -> torch.Tensor:
+        T, k = self.handle.num_tokens, self.top_k
+        return self.slot_index[: T * k].view(T, k)
+
+    def src_index_view(self) -> torch.Tensor:
+        return self.src_index.view(self.ep_size, self.cap)
+
+
+def moe_dispatch(h: MoeA2A, x: torch.Tensor, topk_ids: torch.Tensor,
+                 runtime_max_tokens_per_rank: int, workspace: torch.Tensor,
+                 stream=None) -> None:
+    """Route every routed copy of x into ``workspace`` ([ep, cap, H] bf16)."""
+    T = x.shape[0] if x.dim() == 2 else 0
+    _need(x, "x", torch.bfloat16, shape=(T, h.hidden))
+    _need(topk_ids, "topk_ids", torch.int32, shape=(T, h.top_k))
+    _need(workspace, "workspace", torch.bfloat16, numel=h.ep_size * h.cap * h.hidden)
+    _check(library().moe_dispatch(ctypes.byref(h.handle), _ptr(x), _ptr(topk_ids), T,
+                                  runtime_max_tokens_per_rank, _ptr(workspace), _stream(stream)),
+           "moe_dispatch")
+
+
+def moe_combine(h: MoeA2A, expert_out: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
+                weighted: Optional[bool] = None, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """out[t] = bf16(sum_j c_j * expert_out[slot(t, j)]), reduced once in fp32."""
+    T = h.handle.num_tokens
+    weighted = (topk_weights is not None) if weighted is None else bool(weighted)
+    _need(expert_out, "expert_out", torch.bfloat16, numel=h.ep_size * h.cap * h.hidden)
+    if weighted:
+        _need(topk_weights, "topk_weights", torch.float32, shape=(T, h.top_k))
+    if out is None:
+        out = torch.empty((T, h.hidden), dtype=torch.bfloat16, device=expert_out.device)
+    _need(out, "out", torch.bfloat16, shape=(T, h.hidden))
+    _check(library().moe_combine(ctypes.byref(h.handle), _ptr(expert_out),
+                                 _ptr(topk_weights) if weighted else None, int(weighted),
+                                 _ptr(out), _stream(stream)), "moe_combine")
+    return out
+
+
+def moe_combine_residual_rmsnorm(h: MoeA2A, expert_out: torch.Tensor,
+                                 topk_weights: Optional[torch.Tensor], weighted: bool,
+                                 residual: torch.Tensor, gamma: torch.Tensor, eps: float,
+                                 residual_out: Optional[torch.Tensor] = None,
+                                 normed: Optional[torch.Tensor] = None,
+                                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Combine, add the residual and RMSNorm in one pass.
+
+    Returns (residual_out, normed); ``residual_out`` may be ``residual``."""
+    T, H = h.handle.num_tokens, h.hidden
+    _need(expert_out, "expert_out", torch.bfloat16, numel=h.ep_size * h.cap * H)
+    if weighted:
+        _need(topk_weights, "topk_weights", torch.float32, shape=(T, h.top_k))
+    _need(residual, "residual", torch.bfloat16, shape=(T, H))
+    _need(gamma, "gamma", torch.bfloat16, shape=(H,))
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    if normed is None:
+        normed = torch.empty_like(residual)
+    _need(residual_out, "residual_out", torch.bfloat16, shape=(T, H))
+    _need(normed, "normed", torch.bfloat16, shape=(T, H))
+    _check(library().moe_combine_residual_rmsnorm(
+        ctypes.byref(h.handle), _ptr(expert_out), _ptr(topk_weights) if weighted else None,
+        int(bool(weighted)), _ptr(residual), _ptr(residual_out), _ptr(gamma), float(eps),
+        _ptr(normed), _stream(stream)), "moe_combine_residual_rmsnorm")
+    return residual_out, normed
+
+
+def moe_route_counts(h: MoeA2A, topk_ids: torch.Tensor, stream=None) -> torch.Tensor:
+    """Per-region copy counts of a routing (for sizing max_tokens_per_rank)."""
+    T = topk_ids.shape[0]
+    _need(topk_ids, "topk_ids", torch.int32, shape=(T, h.top_k))
+    _check(library().moe_route_counts(ctypes.byref(h.handle), _ptr(topk_ids), T,
+                                      _stream(stream)), "moe_route_counts")
+    return h.counts
+
+
+def moe_sync_status(h: MoeA2A, stream=None) -> Tuple[int, int]:
+    """Wait for the stream; returns (code, status bits) and clears the bits."""
+    bits = ctypes.c_int32(0)
+    code = library().moe_sync_status(ctypes.byref(h.handle), _stream(stream), ctypes.byref(bits))
+    if code == MOE_ERR_HIP or code == MOE_ERR_ARG:
+        raise MoeError(code, "moe_sync_status")
+    return code, bits.value
+
+
+def moe_reset(h: MoeA2A) -> None:
+    _check(library().moe_reset(ctypes.byref(h.handle)), "moe_reset")
+
+
+__all__ = [
+    "MoeA2A", "MoeError", "MoeHandle", "library", "moe_dispatch", "moe_combine",
+    "moe_combine_residual_rmsnorm", "moe_route_counts", "moe_sync_status", "moe_reset",
+    "moe_output_is_reduced", "moe_strerror", "moe_workspace_bytes", "moe_scratch_bytes",
+]

@@ -1,0 +1,55 @@
+"""Build the gfx950 shared library ``libmoe_a2a.so`` in-tree with hipcc.
+
+Run ``python -m combine_moe_dispatch_03_amd.build`` (or call ``build()``).
+Compiles for gfx950 only.  Flags:
+  -ffp-contract=off     every fused multiply-add in a kernel is written out;
+                        no other add/multiply pair is contracted, so the fp32
+                        accumulation order is exactly the one in the source
+  -packed-fp32-ops off  keep the compiler from emitting packed fp32 ops
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIBRARY = os.path.join(PKG, "libmoe_a2a.so")
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.hip")]
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+    "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    path = os.path.join(rocm, "bin", "hipcc")
+    return path if os.path.exists(path) else "hipcc"
+
+
+def build(output: str = LIBRARY, verbose: bool = False) -> str:
+    tmp = output + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, output)
+    return output
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

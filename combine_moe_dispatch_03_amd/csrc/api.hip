@@ -1,0 +1,263 @@
+// C ABI of the MoE dispatch / combine library: argument and phase checks on
+// the host, then kernel launches on the caller's stream.  The phase contract
+// (dispatch twice -> error, combine without dispatch -> error, combine
+// returns the handle to idle) follows the "The adapter" table of InferenceX
+// PR #2450, "CollectiveX: add FlashInfer one-sided NVLink EP for the GB SKUs".
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "launch.h"
+#include "moe_a2a.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool dev_ok(const void *p, uintptr_t a) { return p != nullptr && aligned(p, a); }
+
+int hip_fail(moe_handle *h, hipError_t e) {
+    h->hip_error = static_cast<int32_t>(e);
+    return MOE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(int32_t ep_size, int32_t max_tokens_per_rank, int32_t hidden) {
+    if (ep_size <= 0 || max_tokens_per_rank <= 0 || hidden <= 0) return 0;
+    return (size_t)ep_size * (size_t)max_tokens_per_rank * (size_t)hidden * sizeof(uint16_t);
+}
+
+size_t moe_scratch_bytes(int32_t max_tokens, int32_t top_k, int32_t ep_size) {
+    if (max_tokens < 1 || top_k < 1 || top_k > MOE_MAX_TOP_K || ep_size < 1 || ep_size > MOE_MAX_EP)
+        return 0;
+    const int64_t items = (int64_t)max_tokens * top_k;
+    if (items > INT32_MAX) return 0;
+    const size_t bytes = (size_t)(items + (int64_t)moe::kMaxChunks * ep_size) * sizeof(int32_t);
+    return (bytes + 255) & ~(size_t)255;
+}
+
+int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
+             int32_t num_experts, int32_t ep_size, int32_t max_tokens_per_rank,
+             int32_t *counts, int32_t *src_index, int32_t *slot_index,
+             int32_t *status, void *scratch, size_t scratch_bytes) {
+    if (h == nullptr) return MOE_ERR_ARG;
+    if (max_tokens < 1 || hidden < 8 || hidden % 8 != 0) return MOE_ERR_ARG;
+    if (top_k < 1 || top_k > MOE_MAX_TOP_K) return MOE_ERR_ARG;
+    if (ep_size < 1 || ep_size > MOE_MAX_EP) return MOE_ERR_ARG;
+    if (num_experts < ep_size || num_experts % ep_size != 0) return MOE_ERR_ARG;
+    if (max_tokens_per_rank < 1) return MOE_ERR_ARG;
+    if ((int64_t)ep_size * max_tokens_per_rank > INT32_MAX) return MOE_ERR_ARG;
+    if ((int64_t)max_tokens * top_k > INT32_MAX) return MOE_ERR_ARG;
+    if (!dev_ok(counts, 4) || !dev_ok(src_index, 4) || !dev_ok(slot_index, 4) ||
+        !dev_ok(status, 4) || !dev_ok(scratch, 4))
+        return MOE_ERR_ARG;
+    const size_t need = moe_scratch_bytes(max_tokens, top_k, ep_size);
+    if (need == 0 || scratch_bytes < need) return MOE_ERR_ARG;
+
+    memset(h, 0, sizeof *h);
+    h->max_tokens = max_tokens;
+    h->hidden = hidden;
+    h->top_k = top_k;
+    h->num_experts = num_experts;
+    h->ep_size = ep_size;
+    h->experts_per_rank = num_experts / ep_size;
+    h->max_tokens_per_rank = max_tokens_per_rank;
+    h->counts = counts;
+    h->src_index = src_index;
+    h->slot_index = slot_index;
+    h->status = status;
+    h->scratch = scratch;
+    h->scratch_bytes = scratch_bytes;
+    return MOE_OK;
+}
+
+static int route(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens, hipStream_t s,
+                 moe::RoutePlan *plan_out) {
+    const moe::RoutePlan plan = moe::plan_route(num_tokens);
+    moe::RouteArgs ra;
+    ra.ids = topk_ids;
+    ra.rank = moe::scratch_rank(h->scratch);
+    ra.hist = moe::scratch_hist(h->scratch, (int64_t)h->max_tokens * h->top_k);
+    ra.status = h->status;
+    ra.n_items = (int64_t)num_tokens * h->top_k;
+    ra.items_per_chunk = plan.tokens_per_chunk * h->top_k;
+    ra.ep = h->ep_size;
+    ra.epr = h->experts_per_rank;
+    ra.n_experts = h->num_experts;
+    hipError_t e = moe::launch_route(ra, plan.n_chunks, s);
+    if (e != hipSuccess) return hip_fail(h, e);
+    *plan_out = plan;
+    return MOE_OK;
+}
+
+static moe::DispatchArgs dispatch_args(moe_handle *h, const uint16_t *x, const int32_t *ids,
+                                       int32_t T, uint16_t *ws, const moe::RoutePlan &plan,
+                                       int32_t count_only) {
+    moe::DispatchArgs da;
+    da.x = x;
+    da.ids = ids;
+    da.rank = moe::scratch_rank(h->scratch);
+    da.hist = moe::scratch_hist(h->scratch, (int64_t)h->max_tokens * h->top_k);
+    da.ws = ws;
+    da.counts = h->counts;
+    da.slot_index = h->slot_index;
+    da.src_index = h->src_index;
+    da.status = h->status;
+    da.T = T;
+    da.H = h->hidden;
+    da.k = h->top_k;
+    da.ep = h->ep_size;
+    da.epr = h->experts_per_rank;
+    da.n_experts = h->num_experts;
+    da.cap = h->max_tokens_per_rank;
+    da.tokens_per_chunk = plan.tokens_per_chunk;
+    da.n_chunks = plan.n_chunks;
+    da.count_only = count_only;
+    return da;
+}
+
+int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
+                 int32_t num_tokens, int32_t runtime_max_tokens_per_rank,
+                 uint16_t *workspace, void *stream) {
+    if (h == nullptr || h->max_tokens < 1) return MOE_ERR_ARG;
+    if (h->phase != 0) return MOE_ERR_PHASE;
+    const int32_t R = runtime_max_tokens_per_rank;
+    if (R < 1 || R > h->max_tokens || num_tokens < 0 || num_tokens > R) return MOE_ERR_ARG;
+    if (!dev_ok(workspace, 16)) return MOE_ERR_ARG;
+    if (num_tokens > 0 && (!dev_ok(x, 16) || !dev_ok(topk_ids, 4))) return MOE_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    moe::RoutePlan plan;
+    int rc = route(h, topk_ids, num_tokens, s, &plan);
+    if (rc != MOE_OK) return rc;
+    const moe::DispatchArgs da = dispatch_args(h, x, topk_ids, num_tokens, workspace, plan, 0);
+    hipError_t e = moe::launch_dispatch_copy(da, s);
+    if (e != hipSuccess) return hip_fail(h, e);
+
+    h->phase = 1;
+    h->num_tokens = num_tokens;
+    h->runtime_max_tokens_per_rank = R;
+    return MOE_OK;
+}
+
+int moe_route_counts(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens, void *stream) {
+    if (h == nullptr || h->max_tokens < 1) return MOE_ERR_ARG;
+    if (h->phase != 0) return MOE_ERR_PHASE;
+    if (num_tokens < 0 || num_tokens > h->max_tokens) return MOE_ERR_ARG;
+    if (num_tokens > 0 && !dev_ok(topk_ids, 4)) return MOE_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    moe::RoutePlan plan;
+    int rc = route(h, topk_ids, num_tokens, s, &plan);
+    if (rc != MOE_OK) return rc;
+    const moe::DispatchArgs da = dispatch_args(h, nullptr, topk_ids, num_tokens, nullptr, plan, 1);
+    hipError_t e = moe::launch_dispatch_copy(da, s);
+    if (e != hipSuccess) return hip_fail(h, e);
+    return MOE_OK;
+}
+
+static int combine_common(moe_handle *h, const uint16_t *expert_out, const float *topk_weights,
+                          int32_t weighted) {
+    if (h == nullptr || h->max_tokens < 1) return MOE_ERR_ARG;
+    if (h->phase != 1) return MOE_ERR_PHASE;
+    if (h->num_tokens > 0) {
+        if (!dev_ok(expert_out, 16)) return MOE_ERR_ARG;
+        if (weighted && !dev_ok(topk_weights, 4)) return MOE_ERR_ARG;
+    }
+    return MOE_OK;
+}
+
+static moe::CombineArgs combine_args(moe_handle *h, const uint16_t *expert_out,
+                                     const float *topk_weights, int32_t weighted) {
+    moe::CombineArgs ca;
+    memset(&ca, 0, sizeof ca);
+    ca.y = expert_out;
+    ca.slot_index = h->slot_index;
+    ca.w = topk_weights;
+    ca.T = h->num_tokens;
+    ca.H = h->hidden;
+    ca.k = h->top_k;
+    ca.weighted = weighted ? 1 : 0;
+    return ca;
+}
+
+int moe_combine(moe_handle *h, const uint16_t *expert_out, const float *topk_weights,
+                int32_t weighted, uint16_t *out, void *stream) {
+    int rc = combine_common(h, expert_out, topk_weights, weighted);
+    if (rc != MOE_OK) return rc;
+    if (h->num_tokens > 0 && !dev_ok(out, 16)) return MOE_ERR_ARG;
+    moe::CombineArgs ca = combine_args(h, expert_out, topk_weights, weighted);
+    ca.out = out;
+    hipError_t e = moe::launch_combine(ca, false, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(h, e);
+    h->phase = 0;
+    return MOE_OK;
+}
+
+int moe_combine_residual_rmsnorm(moe_handle *h, const uint16_t *expert_out,
+                                 const float *topk_weights, int32_t weighted,
+                                 const uint16_t *residual, uint16_t *residual_out,
+                                 const uint16_t *gamma, float eps, uint16_t *normed,
+                                 void *stream) {
+    int rc = combine_common(h, expert_out, topk_weights, weighted);
+    if (rc != MOE_OK) return rc;
+    if (h->hidden > MOE_MAX_FUSED_HIDDEN) return MOE_ERR_ARG;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return MOE_ERR_ARG;
+    if (h->num_tokens > 0 && (!dev_ok(residual, 16) || !dev_ok(residual_out, 16) ||
+                              !dev_ok(gamma, 16) || !dev_ok(normed, 16)))
+        return MOE_ERR_ARG;
+    moe::CombineArgs ca = combine_args(h, expert_out, topk_weights, weighted);
+    ca.residual = residual;
+    ca.residual_out = residual_out;
+    ca.gamma = gamma;
+    ca.normed = normed;
+    ca.eps = eps;
+    hipError_t e = moe::launch_combine(ca, true, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(h, e);
+    h->phase = 0;
+    return MOE_OK;
+}
+
+int moe_sync_status(moe_handle *h, void *stream, int32_t *bits) {
+    if (h == nullptr || h->status == nullptr) return MOE_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t host = 0;
+    hipError_t e = hipMemcpyAsync(&host, h->status, sizeof host, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(h, e);
+    if (host != 0) {
+        e = hipMemsetAsync(h->status, 0, sizeof host, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(h, e);
+    }
+    if (bits) *bits = host;
+    if (host & MOE_STATUS_EXPERT_ID) return MOE_ERR_EXPERT_ID;
+    if (host & MOE_STATUS_OVERFLOW) return MOE_ERR_OVERFLOW;
+    return MOE_OK;
+}
+
+int moe_reset(moe_handle *h) {
+    if (h == nullptr) return MOE_ERR_ARG;
+    h->phase = 0;
+    return MOE_OK;
+}
+
+int moe_output_is_reduced(void) { return 1; }
+
+const char *moe_strerror(int code) {
+    switch (code) {
+        case MOE_OK: return "success";
+        case MOE_ERR_ARG: return "invalid argument (size, null or misaligned pointer)";
+        case MOE_ERR_PHASE: return "phase error (dispatch twice, or combine without dispatch)";
+        case MOE_ERR_OVERFLOW: return "a destination region received more copies than max_tokens_per_rank";
+        case MOE_ERR_EXPERT_ID: return "expert id outside [-1, num_experts)";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        default: return "unknown error code";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,410 @@
+// gfx950 kernels of the MoE dispatch / combine path.
+//
+// Nothing here is a dense contraction, so nothing uses MFMA: the path is
+// bound by HBM bandwidth.  Three kernels:
+//
+//  route_rank_kernel     per chunk of tokens: each routed copy's rank among
+//                        the chunk's copies to the same region (a stable
+//                        wave-ballot scan), and the chunk's region histogram.
+//  dispatch_copy_kernel  per token (x column block): the slot of each copy
+//                        (chunk prefix + rank), the index maps, and the
+//                        16-byte row copies x[t] -> workspace rows.  The
+//                        source row is read once and written k times.
+//  combine_kernel        per token (x column block): gathers the k rows,
+//                        accumulates in fp32 in j order, narrows once to
+//                        bf16 (nearest-even); optionally adds the residual
+//                        and applies RMSNorm with a block-reduced sum of
+//                        squares (the whole row stays in registers).
+//
+// Sources: InferenceX PR #2450 "CollectiveX: add FlashInfer one-sided NVLink
+// EP for the GB SKUs" ("The adapter" table; "Kernel arithmetic read from
+// source": 16-byte stores, nearest-even narrowing; "Update -- the correctness
+// failures are resolved": fp32 accumulator, single narrowing); vLLM PR #41382
+// "[Bugfix] Fix double reduce ..." (one reduction over the experts); magik.net
+// "Fusing the Allreduce: ..." section "The Message Itself: Explanation and
+// Probe" (residual + RMSNorm fused onto the producing reduction).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "moe_a2a.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;            // 4 wave64 per workgroup
+constexpr int kWaves = kThreads / 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bf16 is the high half of a binary32 pattern: widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two fp32 -> packed bf16 pair, nearest-even (gfx950 v_cvt_pk_bf16_f32).
+// The element at the lower address goes to the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ void unpack8(const u32x4 &r, float (&f)[8]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        f[2 * q] = bf16_lo(r[q]);
+        f[2 * q + 1] = bf16_hi(r[q]);
+    }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = pack_bf16(f[2 * q], f[2 * q + 1]);
+    return r;
+}
+
+__device__ __forceinline__ u32x4 load16(const uint16_t *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ void store16(uint16_t *p, const u32x4 &v) {
+    *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// ---------------------------------------------------------------------------
+// route_rank_kernel: grid = n_chunks, one workgroup per chunk of whole tokens.
+// Items of the chunk are taken 256 at a time (one per thread, flat order).
+// Within a wave, lanes with the same region are found by intersecting one
+// ballot per bit of the region number; a lane's rank is the number of such
+// lanes below it.  Per-wave counts go through LDS to give wave offsets, and a
+// per-region carry runs across tiles, so ranks follow the flat order f.
+__global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
+    __shared__ int32_t wave_cnt[kWaves * MOE_MAX_EP];
+    __shared__ int32_t carry[MOE_MAX_EP];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int ep = a.ep;
+    const int64_t begin = (int64_t)blockIdx.x * a.items_per_chunk;
+    const int64_t end = min(begin + (int64_t)a.items_per_chunk, a.n_items);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    int region_bits = 0;
+    while ((1 << region_bits) < ep) ++region_bits;
+
+    for (int r = tid; r < ep; r += kThreads) carry[r] = 0;
+    bool bad = false;
+
+    for (int64_t tile = begin; tile < end; tile += kThreads) {
+        for (int r = tid; r < kWaves * ep; r += kThreads) wave_cnt[r] = 0;
+        __syncthreads();
+
+        const int64_t i = tile + tid;
+        int d = -1;
+        if (i < end) {
+            const int e = a.ids[i];
+            if (e >= 0 && e < a.n_experts)
+                d = e / a.epr;
+            else if (e != -1)
+                bad = true;
+        }
+        uint64_t same = __ballot(d >= 0);
+        for (int b = 0; b < region_bits; ++b) {
+            const bool bit = d >= 0 && ((d >> b) & 1);
+            const uint64_t m = __ballot(bit);
+            same &= bit ? m : ~m;
+        }
+        const int lane_rank = __popcll(same & below);
+        if (d >= 0 && (same >> lane) == 1ull)          // highest lane of its group
+            wave_cnt[wave * ep + d] = __popcll(same);
+        __syncthreads();
+
+        if (d >= 0) {
+            int off = carry[d];
+            for (int w = 0; w < wave; ++w) off += wave_cnt[w * ep + d];
+            a.rank[i] = off + lane_rank;
+        }
+        __syncthreads();
+        for (int r = tid; r < ep; r += kThreads) {
+            int add = 0;
+            for (int w = 0; w < kWaves; ++w) add += wave_cnt[w * ep + r];
+            carry[r] += add;
+        }
+        __syncthreads();
+    }
+
+    if (bad) atomicOr(a.status, MOE_STATUS_EXPERT_ID);
+    for (int r = tid; r < ep; r += kThreads)
+        a.hist[(int64_t)blockIdx.x * ep + r] = carry[r];
+}
+
+// ---------------------------------------------------------------------------
+// dispatch_copy_kernel<VPT>: grid = (T, column blocks); each thread moves VPT
+// 16-byte vectors of the token's row, vector v of block cb at
+// (cb*VPT + v)*256 + tid, so every vector step is one coalesced 4 KB stripe.
+template <int VPT>
+__global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a) {
+    __shared__ int32_t base[MOE_MAX_EP];
+    __shared__ int32_t rows[MOE_MAX_TOP_K];
+
+    const int tid = threadIdx.x;
+    const int t = blockIdx.x;
+    const int cb = blockIdx.y;
+    const int ep = a.ep;
+
+    if (t == 0 && cb == 0) {                    // region totals over all chunks
+        for (int r = tid; r < ep; r += kThreads) base[r] = 0;
+        __syncthreads();
+        for (int i = tid; i < a.n_chunks * ep; i += kThreads) atomicAdd(&base[i % ep], a.hist[i]);
+        __syncthreads();
+        for (int r = tid; r < ep; r += kThreads) a.counts[r] = base[r];
+        __syncthreads();
+    }
+    if (a.count_only || t >= a.T) return;
+
+    // Slots of this token's copies: copies of earlier chunks come first.
+    for (int r = tid; r < ep; r += kThreads) base[r] = 0;
+    __syncthreads();
+    const int chunk = t / a.tokens_per_chunk;
+    for (int i = tid; i < chunk * ep; i += kThreads) atomicAdd(&base[i % ep], a.hist[i]);
+    __syncthreads();
+    if (tid < a.k) {
+        const int64_t f = (int64_t)t * a.k + tid;
+        const int e = a.ids[f];
+        int row = -1;
+        if (e >= 0 && e < a.n_experts) {
+            const int d = e / a.epr;
+            const int s = base[d] + a.rank[f];
+            if (s < a.cap)
+                row = d * a.cap + s;
+            else if (cb == 0)
+                atomicOr(a.status, MOE_STATUS_OVERFLOW);
+        }
+        rows[tid] = row;
+        if (cb == 0) {
+            a.slot_index[f] = row;
+            if (row >= 0) a.src_index[row] = (int32_t)f;
+        }
+    }
+    __syncthreads();
+
+    const int vpr = a.H >> 3;                   // 16-byte vectors per row
+    const uint16_t *src = a.x + (int64_t)t * a.H;
+    u32x4 v[VPT];
+    int col[VPT];
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+        col[q] = ((cb * VPT + q) * kThreads + tid);
+        if (col[q] < vpr) v[q] = load16(src + (int64_t)col[q] * 8);
+    }
+    for (int j = 0; j < a.k; ++j) {
+        const int row = uniform(rows[j]);
+        if (row < 0) continue;
+        uint16_t *dst = a.ws + (int64_t)row * a.H;
+#pragma unroll
+        for (int q = 0; q < VPT; ++q)
+            if (col[q] < vpr) store16(dst + (int64_t)col[q] * 8, v[q]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// combine_kernel<VPT, WEIGHTED, FUSED>: grid = (T, column blocks); FUSED runs
+// with one column block so the whole row is in the workgroup.  Copies are
+// fetched JU at a time (all loads issued before the adds) and added in j
+// order, so the fp32 sum is the same sequence of roundings for every layout.
+template <int VPT, bool WEIGHTED, bool FUSED>
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+    constexpr int JU = 4;
+    __shared__ int32_t rows[MOE_MAX_TOP_K];
+    __shared__ float gates[MOE_MAX_TOP_K];
+    __shared__ float partial[kWaves];
+
+    const int tid = threadIdx.x;
+    const int t = blockIdx.x;
+    const int cb = blockIdx.y;
+    const int k = a.k;
+
+    if (tid < k) {
+        rows[tid] = a.slot_index[(int64_t)t * k + tid];
+        gates[tid] = WEIGHTED ? a.w[(int64_t)t * k + tid] : 1.0f;
+    }
+    __syncthreads();
+
+    const int vpr = a.H >> 3;
+    int col[VPT];
+    float acc[VPT][8];
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+        col[q] = (cb * VPT + q) * kThreads + tid;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[q][e] = 0.0f;
+    }
+
+    for (int j0 = 0; j0 < k; j0 += JU) {
+        u32x4 raw[JU][VPT];
+        int rj[JU];
+#pragma unroll
+        for (int u = 0; u < JU; ++u) {
+            rj[u] = (j0 + u < k) ? uniform(rows[j0 + u]) : -1;
+            if (rj[u] >= 0) {
+                const uint16_t *src = a.y + (int64_t)rj[u] * a.H;
+#pragma unroll
+                for (int q = 0; q < VPT; ++q)
+                    if (col[q] < vpr) raw[u][q] = load16(src + (int64_t)col[q] * 8);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < JU; ++u) {
+            if (rj[u] < 0) continue;
+            const float g = gates[j0 + u];
+#pragma unroll
+            for (int q = 0; q < VPT; ++q) {
+                if (col[q] >= vpr) continue;
+                float f[8];
+                unpack8(raw[u][q], f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[q][e] = WEIGHTED ? __builtin_fmaf(g, f[e], acc[q][e]) : acc[q][e] + f[e];
+            }
+        }
+    }
+
+    const int64_t row_off = (int64_t)t * a.H;
+    if constexpr (!FUSED) {
+#pragma unroll
+        for (int q = 0; q < VPT; ++q)
+            if (col[q] < vpr) store16(a.out + row_off + (int64_t)col[q] * 8, pack8(acc[q]));
+        return;
+    } else {
+        // s = sum + residual (fp32); residual_out = bf16(s); sum of squares.
+        float ss = 0.0f;
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) {
+            if (col[q] >= vpr) continue;
+            float r[8];
+            unpack8(load16(a.residual + row_off + (int64_t)col[q] * 8), r);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                acc[q][e] = acc[q][e] + r[e];
+                ss = __builtin_fmaf(acc[q][e], acc[q][e], ss);
+            }
+            store16(a.residual_out + row_off + (int64_t)col[q] * 8, pack8(acc[q]));
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+        if ((tid & 63) == 0) partial[tid >> 6] = ss;
+        __syncthreads();
+        float total = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) total += partial[w];
+        const float inv = 1.0f / __builtin_sqrtf(total / (float)a.H + a.eps);
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) {
+            if (col[q] >= vpr) continue;
+            float g[8];
+            unpack8(load16(a.gamma + (int64_t)col[q] * 8), g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[q][e] = (acc[q][e] * inv) * g[e];
+            store16(a.normed + row_off + (int64_t)col[q] * 8, pack8(acc[q]));
+        }
+    }
+}
+
+// Smallest power-of-two vectors-per-thread (<= 8) covering a row in one block.
+int full_row_vpt(int32_t H) {
+    const int vpr = H / 8;
+    int vpt = 1;
+    while (vpt < 8 && vpt * kThreads < vpr) vpt *= 2;
+    return vpt;
+}
+
+// Vectors per thread for the streaming kernels: a whole row per block when
+// there are enough tokens to fill the chip, smaller blocks otherwise.
+int streaming_vpt(int32_t T, int32_t H) {
+    constexpr int64_t kWantBlocks = 1024;      // 256 CUs x 4
+    const int vpr = H / 8;
+    int vpt = full_row_vpt(H);
+    while (vpt > 1) {
+        const int64_t blocks = (int64_t)T * ((vpr + vpt * kThreads - 1) / (vpt * kThreads));
+        if (blocks >= kWantBlocks) break;
+        vpt /= 2;
+    }
+    return vpt;
+}
+
+int column_blocks(int32_t H, int vpt) {
+    const int vpr = H / 8;
+    return (vpr + vpt * kThreads - 1) / (vpt * kThreads);
+}
+
+template <int VPT>
+void launch_copy_vpt(const DispatchArgs &a, dim3 grid, hipStream_t s) {
+    hipLaunchKernelGGL(dispatch_copy_kernel<VPT>, grid, dim3(kThreads), 0, s, a);
+}
+
+template <int VPT, bool FUSED>
+void launch_combine_vpt(const CombineArgs &a, dim3 grid, hipStream_t s) {
+    if (a.weighted)
+        hipLaunchKernelGGL((combine_kernel<VPT, true, FUSED>), grid, dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((combine_kernel<VPT, false, FUSED>), grid, dim3(kThreads), 0, s, a);
+}
+
+}  // namespace
+
+RoutePlan plan_route(int32_t num_tokens) {
+    RoutePlan p;
+    p.tokens_per_chunk = num_tokens > 0 ? (num_tokens + kMaxChunks - 1) / kMaxChunks : 1;
+    p.n_chunks = num_tokens > 0 ? (num_tokens + p.tokens_per_chunk - 1) / p.tokens_per_chunk : 0;
+    return p;
+}
+
+hipError_t launch_route(const RouteArgs &a, int32_t n_chunks, hipStream_t s) {
+    if (n_chunks > 0)
+        hipLaunchKernelGGL(route_rank_kernel, dim3(n_chunks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_copy(const DispatchArgs &a, hipStream_t s) {
+    const int vpt = streaming_vpt(a.T, a.H);
+    const dim3 grid(a.T > 0 && !a.count_only ? a.T : 1,
+                    a.T > 0 && !a.count_only ? column_blocks(a.H, vpt) : 1);
+    switch (vpt) {
+        case 1: launch_copy_vpt<1>(a, grid, s); break;
+        case 2: launch_copy_vpt<2>(a, grid, s); break;
+        case 4: launch_copy_vpt<4>(a, grid, s); break;
+        default: launch_copy_vpt<8>(a, grid, s); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs &a, bool fused, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    const int vpt = fused ? full_row_vpt(a.H) : streaming_vpt(a.T, a.H);
+    const dim3 grid(a.T, fused ? 1 : column_blocks(a.H, vpt));
+    if (fused) {
+        switch (vpt) {
+            case 1: launch_combine_vpt<1, true>(a, grid, s); break;
+            case 2: launch_combine_vpt<2, true>(a, grid, s); break;
+            case 4: launch_combine_vpt<4, true>(a, grid, s); break;
+            default: launch_combine_vpt<8, true>(a, grid, s); break;
+        }
+    } else {
+        switch (vpt) {
+            case 1: launch_combine_vpt<1, false>(a, grid, s); break;
+            case 2: launch_combine_vpt<2, false>(a, grid, s); break;
+            case 4: launch_combine_vpt<4, false>(a, grid, s); break;
+            default: launch_combine_vpt<8, false>(a, grid, s); break;
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,70 @@
+// Internal interface between the C ABI (api.hip) and the gfx950 kernels
+// (kernels.hip).  Not installed; the public surface is include/moe_a2a.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Routing is split into at most this many chunks of whole tokens.  Each
+// dispatch block adds up the region histograms of the chunks before its own,
+// so the bound keeps that prefix small (<= kMaxChunks * ep integers).
+constexpr int kMaxChunks = 64;
+
+struct RoutePlan {
+    int32_t tokens_per_chunk;
+    int32_t n_chunks;
+};
+
+RoutePlan plan_route(int32_t num_tokens);
+
+// Scratch layout: rank[max_tokens * k] then hist[kMaxChunks * ep].
+inline int32_t *scratch_rank(void *scratch) { return static_cast<int32_t *>(scratch); }
+inline int32_t *scratch_hist(void *scratch, int64_t max_items) {
+    return static_cast<int32_t *>(scratch) + max_items;
+}
+
+struct RouteArgs {
+    const int32_t *ids;      // [T*k]
+    int32_t *rank;           // [T*k] rank of the copy among its chunk's copies to the same region
+    int32_t *hist;           // [n_chunks * ep] copies per (chunk, region)
+    int32_t *status;         // MOE_STATUS_* bits
+    int64_t n_items;         // T*k
+    int32_t items_per_chunk;
+    int32_t ep, epr, n_experts;
+};
+
+struct DispatchArgs {
+    const uint16_t *x;       // [T, H]
+    const int32_t *ids;      // [T, k]
+    const int32_t *rank;
+    const int32_t *hist;
+    uint16_t *ws;            // [ep, cap, H]
+    int32_t *counts;         // [ep]
+    int32_t *slot_index;     // [T*k]
+    int32_t *src_index;      // [ep*cap]
+    int32_t *status;
+    int32_t T, H, k, ep, epr, n_experts, cap;
+    int32_t tokens_per_chunk, n_chunks;
+    int32_t count_only;      // 1: only write counts
+};
+
+struct CombineArgs {
+    const uint16_t *y;       // [ep, cap, H] expert outputs in the dispatch layout
+    const int32_t *slot_index;
+    const float *w;          // [T, k] gates (weighted only)
+    uint16_t *out;           // [T, H] (plain combine)
+    const uint16_t *residual;     // [T, H] (fused)
+    uint16_t *residual_out;       // [T, H] (fused; may alias residual)
+    const uint16_t *gamma;        // [H]    (fused)
+    uint16_t *normed;             // [T, H] (fused)
+    float eps;
+    int32_t T, H, k, weighted;
+};
+
+hipError_t launch_route(const RouteArgs &a, int32_t n_chunks, hipStream_t s);
+hipError_t launch_dispatch_copy(const DispatchArgs &a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, bool fused, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,227 @@
+/*
+ * moe_a2a.h -- C ABI of the MI355X MoE token dispatch / combine library.
+ *
+ * One GPU holds the whole exchange: the ep_size destination regions of the
+ * all-to-all are partitions of one workspace in local HBM.  Dispatch routes
+ * every routed copy of a token into its region; combine gathers each token's
+ * k expert outputs back and reduces them exactly once; the fused variant adds
+ * the residual and applies RMSNorm in the same pass.
+ *
+ * Sources, cited by page title and section:
+ *  [A2A]  InferenceX PR #2450, "CollectiveX: add FlashInfer one-sided NVLink
+ *         EP for the GB SKUs": "The adapter" table (dispatch / combine phase
+ *         contract, padded receive [ep_size, runtime_max_tokens_per_rank,
+ *         hidden] read at valid slots only, workspace sized once from the
+ *         ladder maximum with each call passing its rung); the on-metal probe
+ *         comment (init / dispatch / combine signatures, the caller-provided
+ *         output buffer of newer versions); "Update -- the correctness
+ *         failures are resolved" (fp32 accumulation, one nearest-even
+ *         narrowing store, expert outputs written in place in the workspace).
+ *  [DR]   vLLM PR #41382, "[Bugfix] Fix double reduce in
+ *         flashinfer_nvlink_two_sided and flashinfer_nvlink_one_sided
+ *         backends": the all-to-all combine already sums over the experts
+ *         dimension, so callers must not reduce its output again.
+ *  [FUSE] magik.net, "Fusing the Allreduce: A Precision Investigation into
+ *         FlashInfer's Verify-Path Optimization", section "The Message Itself:
+ *         Explanation and Probe": residual add + RMSNorm fused onto the
+ *         reduction that produces the hidden state.
+ *
+ * Conventions (all calls):
+ *  - bf16 tensors are passed as uint16_t bit patterns; fp32 as float.
+ *  - "device" pointers are HIP device memory of the GPU current when the call
+ *    is made; "host" pointers are ordinary process memory.
+ *  - Every buffer is allocated and freed by the caller.  The library never
+ *    allocates, frees or synchronises, except moe_sync_status.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    dispatch and the combines only enqueue kernels on it and return.
+ *  - Arguments are checked on the host before anything is enqueued; a
+ *    failed check returns a negative MOE_ERR_* code and changes nothing.
+ *  - Layout, symbols: T tokens, H hidden, k top-k, E experts, ep regions,
+ *    epr = E / ep experts per region, cap = max_tokens_per_rank rows per
+ *    region, f = t*k + j the flat index of token t's j-th routed copy.
+ *  - Region of expert e is e / epr.  Expert id -1 means "no expert".
+ *  - Row order inside a region is stable: region r holds its copies in
+ *    increasing f.  ([A2A] "Verified: per-rank permutation" shows the order
+ *    is the implementation's choice; this library fixes the stable one.)
+ */
+#ifndef MOE_A2A_H
+#define MOE_A2A_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes -------------------------------------------------------- */
+#define MOE_OK             0
+#define MOE_ERR_ARG       (-1)  /* bad size, null or misaligned pointer      */
+#define MOE_ERR_PHASE     (-2)  /* dispatch twice, or combine without dispatch */
+#define MOE_ERR_OVERFLOW  (-3)  /* a region received more than cap copies    */
+#define MOE_ERR_EXPERT_ID (-4)  /* an expert id outside [-1, E)              */
+#define MOE_ERR_HIP       (-5)  /* a HIP runtime call failed (see hip_error) */
+
+/* bits of the device status word (moe_sync_status) */
+#define MOE_STATUS_OVERFLOW  1
+#define MOE_STATUS_EXPERT_ID 2
+
+/* ---- limits ---------------------------------------------------------------- */
+#define MOE_MAX_EP          256     /* destination regions                     */
+#define MOE_MAX_TOP_K        64     /* routed copies per token                 */
+#define MOE_MAX_FUSED_HIDDEN 16384  /* hidden size of the fused epilogue       */
+
+/*
+ * moe_handle -- host memory, owned by the caller.  Filled by moe_init; the
+ * phase fields are updated by dispatch and the combines.  One handle serves
+ * one stream at a time: calls on one handle must not overlap.
+ */
+typedef struct moe_handle {
+    /* configuration (moe_init) */
+    int32_t max_tokens;          /* ladder maximum: largest T of any call      */
+    int32_t hidden;              /* H, multiple of 8                           */
+    int32_t top_k;               /* k                                          */
+    int32_t num_experts;         /* E                                          */
+    int32_t ep_size;             /* ep                                         */
+    int32_t experts_per_rank;    /* epr = E / ep                               */
+    int32_t max_tokens_per_rank; /* cap: allocated rows per region             */
+    int32_t reserved0;
+    /* device buffers owned by the caller (moe_init) */
+    int32_t *counts;             /* [ep]          copies sent to each region   */
+    int32_t *src_index;          /* [ep * cap]    f held by row (r, s)         */
+    int32_t *slot_index;         /* [max_tokens * k] row r*cap+s of copy f, or -1 */
+    int32_t *status;             /* [1]           MOE_STATUS_* bits, sticky    */
+    void    *scratch;            /* moe_scratch_bytes(max_tokens, k, ep) bytes */
+    size_t   scratch_bytes;
+    /* per-call state */
+    int32_t phase;               /* 0 idle, 1 dispatched                       */
+    int32_t num_tokens;          /* T of the last dispatch                     */
+    int32_t runtime_max_tokens_per_rank; /* R of the last dispatch             */
+    int32_t hip_error;           /* hipError_t behind the last MOE_ERR_HIP     */
+} moe_handle;
+
+/* Bytes of the padded workspace [ep, cap, H] bf16. */
+size_t moe_workspace_bytes(int32_t ep_size, int32_t max_tokens_per_rank, int32_t hidden);
+
+/* Bytes of routing scratch a handle needs (per-copy ranks and per-chunk
+ * region histograms); returns 0 for arguments outside the limits. */
+size_t moe_scratch_bytes(int32_t max_tokens, int32_t top_k, int32_t ep_size);
+
+/*
+ * moe_init -- validate the configuration and bind the caller's buffers.
+ * [A2A] on-metal probe: init(mapping, max_num_tokens, top_k, num_experts,
+ * workspace_size_per_rank, hidden_size); the workspace is sized once from
+ * the ladder maximum.
+ *   h                    host, caller-owned; overwritten
+ *   max_tokens           >= 1, largest T any dispatch may pass
+ *   hidden               >= 8 and a multiple of 8
+ *   top_k                1 .. MOE_MAX_TOP_K
+ *   num_experts          multiple of ep_size
+ *   ep_size              1 .. MOE_MAX_EP
+ *   max_tokens_per_rank  >= 1; ep * cap and max_tokens * k must fit int32
+ *   counts, src_index, slot_index, status, scratch: device, 4-byte aligned,
+ *                        sized as in moe_handle; *status must be 0 before
+ *                        the first dispatch (zero-filled memory)
+ *   scratch_bytes        >= moe_scratch_bytes(max_tokens, top_k, ep_size)
+ * Returns MOE_OK or MOE_ERR_ARG.  No HIP call is made.
+ */
+int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
+             int32_t num_experts, int32_t ep_size, int32_t max_tokens_per_rank,
+             int32_t *counts, int32_t *src_index, int32_t *slot_index,
+             int32_t *status, void *scratch, size_t scratch_bytes);
+
+/*
+ * moe_dispatch -- route every copy into its region.  [A2A] "The adapter":
+ * dispatch(token_selected_experts, input_payloads, runtime_max_tokens_per_rank,
+ * invalid_token_expert_id) into a padded receive; one-sided, each copy is
+ * written straight into its destination region.
+ *   x          device [T, H] bf16, 16-byte aligned
+ *   topk_ids   device [T, k] int32 expert ids; -1 = no expert
+ *   num_tokens T, 0 <= T <= runtime_max_tokens_per_rank
+ *   runtime_max_tokens_per_rank  R, the rung of this call, R <= max_tokens
+ *   workspace  device [ep, cap, H] bf16, 16-byte aligned
+ * Writes: workspace rows (r, s) for s < min(counts[r], cap) with the source
+ * token's row (bit copies); counts[r] = copies routed to region r (not
+ * clamped to cap); slot_index[f]; src_index[r*cap + s] for valid rows.
+ * Padding rows and src_index entries past the valid prefix are not touched.
+ * Copies past cap are dropped (slot_index -1) and set MOE_STATUS_OVERFLOW;
+ * ids outside [-1, E) are dropped and set MOE_STATUS_EXPERT_ID; both are
+ * reported by moe_sync_status.
+ * Returns MOE_OK, MOE_ERR_ARG, MOE_ERR_PHASE (already dispatched) or
+ * MOE_ERR_HIP (launch failed).  On success the handle is "dispatched".
+ */
+int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
+                 int32_t num_tokens, int32_t runtime_max_tokens_per_rank,
+                 uint16_t *workspace, void *stream);
+
+/*
+ * moe_combine -- reduce each token's k expert outputs exactly once.
+ * [A2A] "Update -- the correctness failures are resolved": fp32
+ * accumulation, one nearest-even narrowing store; [DR]: the result is final.
+ *   expert_out   device [ep, cap, H] bf16, 16-byte aligned; the expert
+ *                outputs in the dispatch layout (may be the workspace itself)
+ *   topk_weights device [T, k] fp32 gates; read only when weighted != 0
+ *   weighted     0: out = bf16(sum_j y_j); else out = bf16(sum_j w_j * y_j)
+ *   out          device [T, H] bf16, 16-byte aligned; overwritten
+ * Sum over j = 0..k-1 in order in fp32 (weighted terms as fused
+ * multiply-adds), skipping copies with slot_index -1; padding rows are never
+ * read.  A token with no valid copy gets +0.
+ * Returns MOE_OK, MOE_ERR_ARG, MOE_ERR_PHASE (not dispatched) or MOE_ERR_HIP.
+ * On success the handle returns to idle.
+ */
+int moe_combine(moe_handle *h, const uint16_t *expert_out, const float *topk_weights,
+                int32_t weighted, uint16_t *out, void *stream);
+
+/*
+ * moe_combine_residual_rmsnorm -- combine, residual add and RMSNorm in one
+ * pass ([FUSE]).  With s = (fp32 combine sum) + residual, in fp32:
+ *   residual_out = bf16(s)
+ *   normed       = bf16( s / sqrt(mean_h(s^2) + eps) * gamma )
+ *   residual     device [T, H] bf16, 16-byte aligned
+ *   residual_out device [T, H] bf16; may be the same buffer as residual
+ *   gamma        device [H] bf16, 16-byte aligned
+ *   eps          finite, >= 0
+ *   normed       device [T, H] bf16, 16-byte aligned
+ * Other arguments as moe_combine.  Requires H <= MOE_MAX_FUSED_HIDDEN.
+ */
+int moe_combine_residual_rmsnorm(moe_handle *h, const uint16_t *expert_out,
+                                 const float *topk_weights, int32_t weighted,
+                                 const uint16_t *residual, uint16_t *residual_out,
+                                 const uint16_t *gamma, float eps, uint16_t *normed,
+                                 void *stream);
+
+/*
+ * moe_route_counts -- only the per-region copy counts of a routing, so a
+ * caller can size max_tokens_per_rank before allocating the workspace.
+ * Writes counts (and routing scratch); leaves the phase idle.
+ *   topk_ids   device [T, k] int32;  0 <= num_tokens <= max_tokens
+ * Returns MOE_OK, MOE_ERR_ARG, MOE_ERR_PHASE (a dispatch is pending) or
+ * MOE_ERR_HIP.  Bad ids set MOE_STATUS_EXPERT_ID.
+ */
+int moe_route_counts(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens,
+                     void *stream);
+
+/*
+ * moe_sync_status -- wait for `stream`, read and clear the device status.
+ *   bits  host, optional: receives the MOE_STATUS_* bits that were set
+ * Returns MOE_ERR_EXPERT_ID or MOE_ERR_OVERFLOW if a kernel flagged one since
+ * the last call (expert id first), MOE_OK otherwise, MOE_ERR_HIP on a
+ * runtime failure.  The only call that synchronises.
+ */
+int moe_sync_status(moe_handle *h, void *stream, int32_t *bits);
+
+/* moe_reset -- return a dispatched handle to idle without combining. */
+int moe_reset(moe_handle *h);
+
+/* moe_output_is_reduced -- always 1: the combine output is final and must not
+ * be summed over experts again ([DR]). */
+int moe_output_is_reduced(void);
+
+/* moe_strerror -- static text for a return code. */
+const char *moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_A2A_H */

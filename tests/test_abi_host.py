@@ -1,0 +1,175 @@
+"""The C ABI on the host, no GPU needed.
+
+* the shared library loads and exports every function include/moe_a2a.h
+  declares;
+* the ctypes mirror of ``moe_handle`` and the constants match the header
+  (checked by compiling the header with gcc);
+* every argument and phase check returns its documented code before any HIP
+  call is made (fake, aligned device addresses are never dereferenced on
+  these paths).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import combine_moe_dispatch_03_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_a2a.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIBRARY):
+        from combine_moe_dispatch_03_amd import build
+        build.build()
+    return moe.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (moe_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_handle_layout_and_constants_match_header(tmp_path):
+    fields = [f for f, _ in moe.MoeHandle._fields_]
+    prog = ["#include <stdio.h>", "#include <stddef.h>", '#include "moe_a2a.h"',
+            "int main(void){", 'printf("%zu\\n", sizeof(moe_handle));']
+    prog += [f'printf("%zu\\n", offsetof(moe_handle, {f}));' for f in fields]
+    consts = ["MOE_OK", "MOE_ERR_ARG", "MOE_ERR_PHASE", "MOE_ERR_OVERFLOW", "MOE_ERR_EXPERT_ID",
+              "MOE_ERR_HIP", "MOE_STATUS_OVERFLOW", "MOE_STATUS_EXPERT_ID", "MOE_MAX_EP",
+              "MOE_MAX_TOP_K", "MOE_MAX_FUSED_HIDDEN"]
+    prog += [f'printf("%d\\n", (int){c});' for c in consts]
+    prog += ["return 0;}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(prog))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), "-o", str(exe), str(src)], check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(moe.MoeHandle)
+    for f, off in zip(fields, vals[1:1 + len(fields)]):
+        assert getattr(moe.MoeHandle, f).offset == off, f
+    for c, v in zip(consts, vals[1 + len(fields):]):
+        assert getattr(moe, c) == v, c
+
+
+FAKE = 0x100000   # aligned, never dereferenced by the validation paths
+
+
+def make_handle(lib, max_tokens=64, H=128, k=2, E=8, ep=4, cap=128):
+    h = moe.MoeHandle()
+    rc = lib.moe_init(ctypes.byref(h), max_tokens, H, k, E, ep, cap, FAKE, FAKE, FAKE, FAKE,
+                      FAKE, lib.moe_scratch_bytes(max_tokens, k, ep))
+    assert rc == moe.MOE_OK
+    return h
+
+
+def test_sizes(lib):
+    assert lib.moe_workspace_bytes(8, 32768, 7168) == 8 * 32768 * 7168 * 2
+    assert lib.moe_workspace_bytes(0, 1, 8) == 0
+    assert lib.moe_scratch_bytes(4096, 8, 8) >= (4096 * 8 + 64 * 8) * 4
+    assert lib.moe_scratch_bytes(4096, 8, 8) % 256 == 0
+    assert lib.moe_scratch_bytes(0, 8, 8) == 0
+    assert lib.moe_scratch_bytes(16, 65, 8) == 0
+    assert lib.moe_scratch_bytes(16, 8, 257) == 0
+    assert lib.moe_scratch_bytes(1 << 30, 8, 8) == 0      # T*k beyond int32
+
+
+@pytest.mark.parametrize("args", [
+    dict(max_tokens=0), dict(H=0), dict(H=12), dict(H=4), dict(k=0), dict(k=65),
+    dict(ep=0), dict(ep=257), dict(E=7), dict(E=2), dict(cap=0),
+    dict(ep=8, E=8, cap=1 << 29),
+])
+def test_init_rejects(lib, args):
+    p = dict(max_tokens=64, H=128, k=2, E=8, ep=4, cap=128)
+    p.update(args)
+    h = moe.MoeHandle()
+    sb = lib.moe_scratch_bytes(max(p["max_tokens"], 1), max(min(p["k"], 64), 1),
+                               max(min(p["ep"], 256), 1))
+    rc = lib.moe_init(ctypes.byref(h), p["max_tokens"], p["H"], p["k"], p["E"], p["ep"],
+                      p["cap"], FAKE, FAKE, FAKE, FAKE, FAKE, sb)
+    assert rc == moe.MOE_ERR_ARG
+
+
+def test_init_rejects_pointers_and_scratch(lib):
+    h = moe.MoeHandle()
+    sb = lib.moe_scratch_bytes(64, 2, 4)
+    args = [64, 128, 2, 8, 4, 128]
+    assert lib.moe_init(ctypes.byref(h), *args, None, FAKE, FAKE, FAKE, FAKE, sb) == moe.MOE_ERR_ARG
+    assert lib.moe_init(ctypes.byref(h), *args, FAKE, FAKE, FAKE, FAKE + 2, FAKE, sb) == moe.MOE_ERR_ARG
+    assert lib.moe_init(ctypes.byref(h), *args, FAKE, FAKE, FAKE, FAKE, FAKE, sb - 4) == moe.MOE_ERR_ARG
+    assert lib.moe_init(None, *args, FAKE, FAKE, FAKE, FAKE, FAKE, sb) == moe.MOE_ERR_ARG
+    assert lib.moe_init(ctypes.byref(h), *args, FAKE, FAKE, FAKE, FAKE, FAKE, sb) == moe.MOE_OK
+    assert h.experts_per_rank == 2 and h.phase == 0
+
+
+def test_dispatch_argument_checks(lib):
+    h = make_handle(lib)
+    d = lambda x, ids, T, R, ws: lib.moe_dispatch(ctypes.byref(h), x, ids, T, R, ws, None)
+    assert d(FAKE, FAKE, 65, 65, FAKE) == moe.MOE_ERR_ARG          # R > max_tokens
+    assert d(FAKE, FAKE, 33, 32, FAKE) == moe.MOE_ERR_ARG          # T > R
+    assert d(FAKE, FAKE, 8, 0, FAKE) == moe.MOE_ERR_ARG            # R < 1
+    assert d(FAKE, FAKE, -1, 8, FAKE) == moe.MOE_ERR_ARG
+    assert d(FAKE + 8, FAKE, 8, 8, FAKE) == moe.MOE_ERR_ARG        # x not 16-byte aligned
+    assert d(FAKE, FAKE + 2, 8, 8, FAKE) == moe.MOE_ERR_ARG        # ids not 4-byte aligned
+    assert d(FAKE, FAKE, 8, 8, FAKE + 4) == moe.MOE_ERR_ARG        # workspace misaligned
+    assert d(None, FAKE, 8, 8, FAKE) == moe.MOE_ERR_ARG
+    assert d(FAKE, None, 8, 8, FAKE) == moe.MOE_ERR_ARG
+    assert d(FAKE, FAKE, 8, 8, None) == moe.MOE_ERR_ARG
+    assert h.phase == 0
+    h.phase = 1                                                    # already dispatched
+    assert d(FAKE, FAKE, 8, 8, FAKE) == moe.MOE_ERR_PHASE
+    assert lib.moe_route_counts(ctypes.byref(h), FAKE, 8, None) == moe.MOE_ERR_PHASE
+    assert lib.moe_reset(ctypes.byref(h)) == moe.MOE_OK and h.phase == 0
+    assert lib.moe_route_counts(ctypes.byref(h), FAKE, 65, None) == moe.MOE_ERR_ARG
+    assert lib.moe_route_counts(ctypes.byref(h), FAKE + 1, 8, None) == moe.MOE_ERR_ARG
+
+
+def test_combine_argument_and_phase_checks(lib):
+    h = make_handle(lib)
+    c = lambda y, w, weighted, out: lib.moe_combine(ctypes.byref(h), y, w, weighted, out, None)
+    assert c(FAKE, FAKE, 1, FAKE) == moe.MOE_ERR_PHASE              # no dispatch yet
+    h.phase, h.num_tokens = 1, 8
+    assert c(FAKE + 8, FAKE, 1, FAKE) == moe.MOE_ERR_ARG            # expert_out misaligned
+    assert c(FAKE, None, 1, FAKE) == moe.MOE_ERR_ARG                # weighted without gates
+    assert c(FAKE, FAKE + 2, 1, FAKE) == moe.MOE_ERR_ARG
+    assert c(FAKE, FAKE, 1, FAKE + 8) == moe.MOE_ERR_ARG            # out misaligned
+    assert c(FAKE, None, 0, None) == moe.MOE_ERR_ARG
+    assert h.phase == 1                                             # failed checks change nothing
+    f = lambda res, res_out, gamma, eps, normed: lib.moe_combine_residual_rmsnorm(
+        ctypes.byref(h), FAKE, None, 0, res, res_out, gamma, eps, normed, None)
+    assert f(FAKE, FAKE, FAKE, float("nan"), FAKE) == moe.MOE_ERR_ARG
+    assert f(FAKE, FAKE, FAKE, -1e-6, FAKE) == moe.MOE_ERR_ARG
+    assert f(FAKE, FAKE, FAKE, float("inf"), FAKE) == moe.MOE_ERR_ARG
+    assert f(FAKE + 8, FAKE, FAKE, 1e-6, FAKE) == moe.MOE_ERR_ARG
+    assert f(FAKE, None, FAKE, 1e-6, FAKE) == moe.MOE_ERR_ARG
+    assert f(FAKE, FAKE, FAKE + 2, 1e-6, FAKE) == moe.MOE_ERR_ARG
+    assert f(FAKE, FAKE, FAKE, 1e-6, None) == moe.MOE_ERR_ARG
+    big = make_handle(lib, H=16392)
+    big.phase, big.num_tokens = 1, 8
+    assert lib.moe_combine_residual_rmsnorm(ctypes.byref(big), FAKE, None, 0, FAKE, FAKE, FAKE,
+                                            1e-6, FAKE, None) == moe.MOE_ERR_ARG
+
+
+def test_strerror_and_reduced_flag(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert moe.moe_strerror(code) and moe.moe_strerror(code) != moe.moe_strerror(99)
+    assert moe.moe_output_is_reduced() is True
+    assert lib.moe_reset(None) == moe.MOE_ERR_ARG
+    assert lib.moe_sync_status(None, None, None) == moe.MOE_ERR_ARG
