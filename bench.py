@@ -7,14 +7,17 @@ resident in HBM: dispatch (route + stable scan + row copies) -> identity
 expert stage (the expert outputs are the dispatched rows, in place) ->
 combine (reduce once).  On the fused workload the combine is the fused
 combine + residual add + RMSNorm.  W untimed steps, then K timed steps
-bracketed by device synchronisation; one JSON line is printed.
+bracketed by device synchronisation (``value``, ``ms_per_step``), then K more
+steps with HIP events recorded around every launch (the per-kernel
+durations; ``ms_per_step_instrumented`` shows what the events themselves
+cost).  One JSON line is printed.
 
 ``value`` is tokens/s of the headline workload (prefill: 4096 tokens,
 hidden 7168, top-8 of 256 experts over 8 regions, unweighted combine).  The
 line also carries:
   roofline      the dominant kernel (the combine kernel: one launch per
                 moe_combine call, timed with HIP events on the launch stream
-                inside the timed steps) against MI355X's 8 TB/s HBM peak,
+                in the instrumented steps) against MI355X's 8 TB/s HBM peak,
                 algorithmic bytes per launch / mean launch time; ``traffic``
                 is the measured HBM bytes per launch from the committed
                 rocprofv3 counter summary, or null if the kernel source has
@@ -26,6 +29,7 @@ line also carries:
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -64,6 +68,48 @@ def measured_traffic():
         return None
 
 
+class HipEvents:
+    """HIP events on the runtime torch already loaded, created with
+    hipEventDisableSystemFence: recording one then writes a timestamp without
+    the system-scope cache writeback a default event performs, which would
+    otherwise stall the queue for several microseconds at every record."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        path = next(line.split()[-1] for line in open("/proc/self/maps")
+                    if "libamdhip64" in line.split()[-1])
+        lib = ctypes.CDLL(path)
+        lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib = lib
+
+    def create(self) -> ctypes.c_void_p:
+        ev = ctypes.c_void_p()
+        rc = self.lib.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        return ev
+
+    def record(self, ev, stream_handle: int) -> None:
+        rc = self.lib.hipEventRecord(ev, ctypes.c_void_p(stream_handle))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, ev) -> None:
+        self.lib.hipEventDestroy(ev)
+
+
 def describe(wl, cap) -> str:
     mode = {"weighted": "weighted combine", "unweighted": "unweighted combine",
             "both": "weighted combine", "fused": "weighted combine + residual + RMSNorm"}[wl.combine]
@@ -98,44 +144,61 @@ def measure(wl, steps: int, warmup: int, seed: int = 0) -> dict:
         gamma = torch.from_numpy(inp.gamma.view(np.int16)).to(dev).view(torch.bfloat16)
         res_out = torch.empty_like(res)
     stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    hev = HipEvents()
 
     def step(ev=None):
         if ev is not None:
-            ev[0].record(stream)
+            hev.record(ev[0], sh)
         moe.moe_dispatch(h, x, ids, wl.R, ws, stream=stream)
         if ev is not None:
-            ev[1].record(stream)
+            hev.record(ev[1], sh)
         if fused:
             moe.moe_combine_residual_rmsnorm(h, ws, w, True, res, gamma, wl.eps,
                                              residual_out=res_out, normed=out, stream=stream)
         else:
             moe.moe_combine(h, ws, w, weighted, out=out, stream=stream)
         if ev is not None:
-            ev[2].record(stream)
+            hev.record(ev[2], sh)
+
+    def check_status(when):
+        code, bits = moe.moe_sync_status(h, stream)
+        if code != moe.MOE_OK:
+            raise RuntimeError(f"device status {bits} {when}: {moe.moe_strerror(code)}")
 
     for _ in range(warmup):
         step()
-    code, bits = moe.moe_sync_status(h, stream)
-    if code != moe.MOE_OK:
-        raise RuntimeError(f"device status {bits} after warmup: {moe.moe_strerror(code)}")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    check_status("after warmup")
+    # timed steps (the headline figure): nothing but the path itself is enqueued
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    check_status("after timing")
+    # the same number of steps again with HIP events around each launch, for
+    # the per-kernel durations
+    events = [[hev.create() for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for s in range(steps):
         step(events[s])
     torch.cuda.synchronize(dev)
-    elapsed = time.perf_counter() - t0
-    code, bits = moe.moe_sync_status(h, stream)
-    if code != moe.MOE_OK:
-        raise RuntimeError(f"device status {bits} after timing: {moe.moe_strerror(code)}")
-    d_ms = [e[0].elapsed_time(e[1]) for e in events]
-    c_ms = [e[1].elapsed_time(e[2]) for e in events]
+    elapsed_ev = time.perf_counter() - t0
+    check_status("after the instrumented steps")
+    d_ms = [hev.elapsed_ms(e[0], e[1]) for e in events]
+    c_ms = [hev.elapsed_ms(e[1], e[2]) for e in events]
+    for e in events:
+        for ev in e:
+            hev.destroy(ev)
     b = wl.algorithmic_bytes()
     comb_bytes = b["fused"] if fused else b["combine"]
     ms = elapsed * 1e3 / steps
     res_d = {
         "workload": describe(wl, cap),
         "ms_per_step": ms,
+        "ms_per_step_instrumented": elapsed_ev * 1e3 / steps,
         "tokens_per_s": wl.T / (ms / 1e3),
         "step_gbs": (b["dispatch"] + comb_bytes) / (ms / 1e3) / 1e9,
         "dispatch_ms_mean": float(np.mean(d_ms)), "dispatch_ms_p50": float(np.median(d_ms)),
@@ -156,13 +219,19 @@ def cpu_baseline(wl, seconds: float = 10.0, seed: int = 0) -> dict:
     import oracle
     import synth
 
+    import numpy as np
+
     orc = oracle.load()
     inp = synth.make_inputs(wl, seed)
     weighted = wl.combine in ("weighted", "both", "fused")
+    cap = wl.cap
+    if cap is None:
+        cap = int(orc.dispatch(np.zeros((wl.T, 1), np.uint16), inp.ids, wl.ep, wl.epr,
+                               wl.T * wl.k).counts.max())
     reps, t_total = 0, 0.0
     while t_total < seconds:
         t0 = time.perf_counter()
-        d = orc.dispatch(inp.x, inp.ids, wl.ep, wl.epr, wl.cap)
+        d = orc.dispatch(inp.x, inp.ids, wl.ep, wl.epr, cap)
         orc.combine(d.ws, d.slot_index, inp.weights, weighted, wl.H)
         t_total += time.perf_counter() - t0
         reps += 1
@@ -223,6 +292,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": main_res["ms_per_step"],
+        "ms_per_step_instrumented": main_res["ms_per_step_instrumented"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -77,6 +77,21 @@ __device__ __forceinline__ void store16(uint16_t *p, const u32x4 &v) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// base[r] += sum of hist[i] over i < n with i % ep == r (LDS, all threads).
+// When ep divides the block size every entry a thread visits belongs to the
+// same region, so the thread adds its entries in a register (loads in flight
+// together) and issues one LDS atomic.
+__device__ __forceinline__ void add_region_sums(int32_t *base, const int32_t *hist, int n, int ep,
+                                                int tid) {
+    if (kThreads % ep == 0) {
+        int sum = 0;
+        for (int i = tid; i < n; i += kThreads) sum += hist[i];
+        if (sum != 0) atomicAdd(&base[tid % ep], sum);
+    } else {
+        for (int i = tid; i < n; i += kThreads) atomicAdd(&base[i % ep], hist[i]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // route_rank_kernel: grid = n_chunks, one workgroup per chunk of whole tokens.
 // Items of the chunk are taken 256 at a time (one per thread, flat order).
@@ -149,8 +164,9 @@ __global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
 // dispatch_copy_kernel<VPT, NT>: grid = (T, column blocks); each thread moves
 // VPT 16-byte vectors of the token's row, vector v of block cb at
 // (cb*VPT + v)*256 + tid, so every vector step is one coalesced 4 KB stripe.
-// The source loads are unconditional (lanes past the row end re-read the
-// row's last vector and store nothing) so they are all in flight together.
+// The source loads are issued first (they do not depend on the slots) and
+// unconditionally (lanes past the row end re-read the row's last vector and
+// store nothing), so they are all in flight while the slots are computed.
 // NT marks the workspace stores non-temporal.
 template <int VPT, bool NT>
 __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a) {
@@ -165,26 +181,46 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
     if (t == 0 && cb == 0) {                    // region totals over all chunks
         for (int r = tid; r < ep; r += kThreads) base[r] = 0;
         __syncthreads();
-        for (int i = tid; i < a.n_chunks * ep; i += kThreads) atomicAdd(&base[i % ep], a.hist[i]);
+        add_region_sums(base, a.hist, a.n_chunks * ep, ep, tid);
         __syncthreads();
         for (int r = tid; r < ep; r += kThreads) a.counts[r] = base[r];
         __syncthreads();
     }
     if (a.count_only || t >= a.T) return;
 
+    // The source row does not depend on the slots: start its loads first so
+    // they overlap the slot computation below.
+    const int vpr = a.H >> 3;                   // 16-byte vectors per row
+    const uint16_t *src = a.x + (int64_t)t * a.H;
+    u32x4 v[VPT];
+    int col[VPT];
+    int64_t off[VPT];
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+        col[q] = (cb * VPT + q) * kThreads + tid;
+        off[q] = (int64_t)min(col[q], vpr - 1) * 8;
+        v[q] = load16(src + off[q]);
+    }
+
+    // This token's ids and in-chunk ranks (independent of the prefix too).
+    int e = -1, rank = 0;
+    const int64_t f = (int64_t)t * a.k + tid;
+    if (tid < a.k) {
+        e = a.ids[f];
+        rank = a.rank[f];                       // meaningful only for a valid id
+    }
+
     // Slots of this token's copies: copies of earlier chunks come first.
     for (int r = tid; r < ep; r += kThreads) base[r] = 0;
     __syncthreads();
     const int chunk = t / a.tokens_per_chunk;
-    for (int i = tid; i < chunk * ep; i += kThreads) atomicAdd(&base[i % ep], a.hist[i]);
+    add_region_sums(base, a.hist, chunk * ep, ep, tid);
     __syncthreads();
     if (tid < a.k) {
-        const int64_t f = (int64_t)t * a.k + tid;
-        const int e = a.ids[f];
         int row = -1;
         if (e >= 0 && e < a.n_experts) {
             const int d = e / a.epr;
-            const int s = base[d] + a.rank[f];
+            const int s = base[d] + rank;
             if (s < a.cap)
                 row = d * a.cap + s;
             else if (cb == 0)
@@ -198,17 +234,6 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
     }
     __syncthreads();
 
-    const int vpr = a.H >> 3;                   // 16-byte vectors per row
-    const uint16_t *src = a.x + (int64_t)t * a.H;
-    u32x4 v[VPT];
-    int col[VPT];
-    int64_t off[VPT];
-#pragma unroll
-    for (int q = 0; q < VPT; ++q) {
-        col[q] = (cb * VPT + q) * kThreads + tid;
-        off[q] = (int64_t)min(col[q], vpr - 1) * 8;
-        v[q] = load16(src + off[q]);
-    }
     for (int j = 0; j < a.k; ++j) {
         const int row = uniform(rows[j]);
         if (row < 0) continue;
