@@ -24,6 +24,8 @@ line also carries:
                 changed since those counters were taken
   cpu_baseline  the CPU oracle (plain scalar C, one thread) timed on the
                 same workload, repeated for about 10 s
+  cold          per-kernel p50 / mean over --cold-iters launches, each after
+                an untimed 1 GiB read that evicts the 256 MB Infinity Cache
   workloads     the same step on the skewed, decode and fused workloads
 """
 from __future__ import annotations
@@ -117,7 +119,7 @@ def describe(wl, cap) -> str:
             f"rung={wl.R} {wl.routing} routing, {mode}")
 
 
-def measure(wl, steps: int, warmup: int, seed: int = 0) -> dict:
+def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0) -> dict:
     import numpy as np
     import torch
 
@@ -192,6 +194,33 @@ def measure(wl, steps: int, warmup: int, seed: int = 0) -> dict:
     for e in events:
         for ev in e:
             hev.destroy(ev)
+    # cold launches: an untimed read of a 1 GiB buffer before every dispatch
+    # and every combine, so MI355X's 256 MB Infinity Cache holds none of the
+    # working set.  The flush reads rather than writes: a written buffer would
+    # leave dirty lines whose write-back then lands inside the timed kernel.
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev) if cold_iters > 0 else None
+    cold = [[hev.create() for _ in range(4)] for _ in range(cold_iters)]
+    for ev in cold:
+        flush.max()
+        hev.record(ev[0], sh)
+        moe.moe_dispatch(h, x, ids, wl.R, ws, stream=stream)
+        hev.record(ev[1], sh)
+        flush.max()
+        hev.record(ev[2], sh)
+        if fused:
+            moe.moe_combine_residual_rmsnorm(h, ws, w, True, res, gamma, wl.eps,
+                                             residual_out=res_out, normed=out, stream=stream)
+        else:
+            moe.moe_combine(h, ws, w, weighted, out=out, stream=stream)
+        hev.record(ev[3], sh)
+    torch.cuda.synchronize(dev)
+    check_status("after the cold launches")
+    cd_ms = [hev.elapsed_ms(e[0], e[1]) for e in cold]
+    cc_ms = [hev.elapsed_ms(e[2], e[3]) for e in cold]
+    for e in cold:
+        for ev in e:
+            hev.destroy(ev)
+    del flush
     b = wl.algorithmic_bytes()
     comb_bytes = b["fused"] if fused else b["combine"]
     ms = elapsed * 1e3 / steps
@@ -208,9 +237,26 @@ def measure(wl, steps: int, warmup: int, seed: int = 0) -> dict:
     res_d["dispatch_gbs"] = b["dispatch"] / (res_d["dispatch_ms_mean"] / 1e3) / 1e9
     res_d["combine_gbs"] = comb_bytes / (res_d["combine_ms_mean"] / 1e3) / 1e9
     res_d["step_hbm_frac"] = res_d["step_gbs"] / HBM_PEAK_GBS
+    res_d["cold"] = None
+    if cold_iters > 0:
+        res_d["cold"] = cold_stats(cd_ms, cc_ms, cold_iters, wl.T, b["dispatch"], comb_bytes)
     del ws, h
     torch.cuda.empty_cache()
     return res_d
+
+
+def cold_stats(cd_ms, cc_ms, iters, T, disp_bytes, comb_bytes) -> dict:
+    import numpy as np
+    d50, c50 = float(np.median(cd_ms)), float(np.median(cc_ms))
+    return {
+        "iters": iters, "flush_bytes": 1 << 30,
+        "dispatch_ms_p50": d50, "dispatch_ms_mean": float(np.mean(cd_ms)),
+        "combine_ms_p50": c50, "combine_ms_mean": float(np.mean(cc_ms)),
+        "dispatch_gbs_p50": disp_bytes / (d50 / 1e3) / 1e9,
+        "combine_gbs_p50": comb_bytes / (c50 / 1e3) / 1e9,
+        "tokens_per_s_p50": T / ((d50 + c50) / 1e3),
+        "hbm_frac_p50": (disp_bytes + comb_bytes) / ((d50 + c50) / 1e3) / 1e9 / HBM_PEAK_GBS,
+    }
 
 
 def cpu_baseline(wl, seconds: float = 10.0, seed: int = 0) -> dict:
@@ -260,6 +306,8 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--extras", default="skewed,decode,fused",
                     help="comma-separated workloads also measured (empty for none)")
+    ap.add_argument("--cold-iters", type=int, default=100,
+                    help="launches timed after an untimed 1 GiB cache-evicting read, per kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -277,10 +325,11 @@ def main() -> int:
 
     import synth
     wl = synth.BY_NAME[args.workload]
-    main_res = measure(wl, args.steps, args.warmup)
+    main_res = measure(wl, args.steps, args.warmup, args.cold_iters)
     extras = {}
     for name in [n for n in args.extras.split(",") if n and n != wl.name]:
-        extras[name] = measure(synth.BY_NAME[name], max(args.steps // 2, 5), max(args.warmup // 2, 2))
+        extras[name] = measure(synth.BY_NAME[name], max(args.steps // 2, 5),
+                               max(args.warmup // 2, 2), args.cold_iters)
 
     comb_ms = main_res["combine_ms_mean"]
     achieved = main_res["combine_bytes"] / (comb_ms / 1e3) / 1e9
@@ -309,8 +358,11 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": main_res["combine_bytes"],
                      "launch_ms_mean": comb_ms},
         "kernels": {"dispatch_ms_mean": main_res["dispatch_ms_mean"],
+                    "dispatch_ms_p50": main_res["dispatch_ms_p50"],
                     "dispatch_gbs": main_res["dispatch_gbs"],
-                    "combine_ms_mean": comb_ms, "combine_gbs": main_res["combine_gbs"]},
+                    "combine_ms_mean": comb_ms, "combine_ms_p50": main_res["combine_ms_p50"],
+                    "combine_gbs": main_res["combine_gbs"]},
+        "cold": main_res["cold"],
         "workloads": extras,
     }
     if not args.no_cpu_baseline:

@@ -132,9 +132,11 @@ int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
     if (num_tokens > 0 && (!dev_ok(x, 16) || !dev_ok(topk_ids, 4))) return MOE_ERR_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    moe::RoutePlan plan;
-    int rc = route(h, topk_ids, num_tokens, s, &plan);
-    if (rc != MOE_OK) return rc;
+    moe::RoutePlan plan = moe::plan_route(num_tokens);
+    if (!moe::dispatch_is_small(num_tokens, h->top_k)) {   // small batches need no routing kernel
+        int rc = route(h, topk_ids, num_tokens, s, &plan);
+        if (rc != MOE_OK) return rc;
+    }
     const moe::DispatchArgs da = dispatch_args(h, x, topk_ids, num_tokens, workspace, plan, 0);
     hipError_t e = moe::launch_dispatch_copy(da, s);
     if (e != hipSuccess) return hip_fail(h, e);

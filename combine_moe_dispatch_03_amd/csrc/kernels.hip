@@ -270,6 +270,123 @@ __device__ __forceinline__ void accumulate(float (&acc)[VPT][8], const u32x4 (&r
 }
 
 // ---------------------------------------------------------------------------
+// dispatch_small_kernel<VPT, NT>: the whole dispatch in one launch, for
+// batches of at most kSmallItems routed copies (decode).  Each block counts,
+// per region, the copies of all earlier tokens itself (at most kSmallItems
+// ids, read from L2), adds the rank among its own token's earlier copies,
+// and copies its row like dispatch_copy_kernel.  Block (0, 0) also counts
+// every copy for `counts` and flags bad ids.  Same stable slot order as the
+// two-kernel path: copies fill a region in increasing flat index.
+// Within a wave, lanes bound for the same region are grouped with one ballot
+// per bit of the region number (as in route_rank_kernel) so each group adds
+// its size to the LDS counter with one atomic.
+__device__ __forceinline__ void count_regions(int32_t *cnt, const int32_t *ids, int64_t n, int epr,
+                                              int n_experts, int region_bits, int tid,
+                                              bool *bad) {
+    const int lane = tid & 63;
+    for (int64_t base = 0; base < n; base += kThreads) {
+        const int64_t i = base + tid;
+        int d = -1;
+        if (i < n) {
+            const int e = ids[i];
+            if (e >= 0 && e < n_experts)
+                d = e / epr;
+            else if (e != -1)
+                *bad = true;
+        }
+        uint64_t same = __ballot(d >= 0);
+        for (int b = 0; b < region_bits; ++b) {
+            const bool bit = d >= 0 && ((d >> b) & 1);
+            const uint64_t m = __ballot(bit);
+            same &= bit ? m : ~m;
+        }
+        if (d >= 0 && (same >> lane) == 1ull) atomicAdd(&cnt[d], __popcll(same));
+    }
+}
+
+template <int VPT, bool NT>
+__global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a) {
+    __shared__ int32_t cnt[MOE_MAX_EP];
+    __shared__ int32_t dests[MOE_MAX_TOP_K];
+    __shared__ int32_t rows[MOE_MAX_TOP_K];
+
+    const int tid = threadIdx.x;
+    const int t = blockIdx.x;
+    const int cb = blockIdx.y;
+    const int ep = a.ep;
+    int region_bits = 0;
+    while ((1 << region_bits) < ep) ++region_bits;
+
+    if (t == 0 && cb == 0) {                    // totals and the bad-id flag
+        for (int r = tid; r < ep; r += kThreads) cnt[r] = 0;
+        __syncthreads();
+        bool bad = false;
+        count_regions(cnt, a.ids, (int64_t)a.T * a.k, a.epr, a.n_experts, region_bits, tid, &bad);
+        if (bad) atomicOr(a.status, MOE_STATUS_EXPERT_ID);
+        __syncthreads();
+        for (int r = tid; r < ep; r += kThreads) a.counts[r] = cnt[r];
+        __syncthreads();
+    }
+    if (t >= a.T) return;
+
+    const int vpr = a.H >> 3;
+    const uint16_t *src = a.x + (int64_t)t * a.H;
+    u32x4 v[VPT];
+    int col[VPT];
+    int64_t off[VPT];
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+        col[q] = (cb * VPT + q) * kThreads + tid;
+        off[q] = (int64_t)min(col[q], vpr - 1) * 8;
+        v[q] = load16(src + off[q]);
+    }
+
+    const int64_t f = (int64_t)t * a.k + tid;
+    for (int r = tid; r < ep; r += kThreads) cnt[r] = 0;
+    if (tid < a.k) {
+        const int e = a.ids[f];
+        dests[tid] = (e >= 0 && e < a.n_experts) ? e / a.epr : -1;
+    }
+    __syncthreads();
+    bool unused = false;
+    count_regions(cnt, a.ids, (int64_t)t * a.k, a.epr, a.n_experts, region_bits, tid, &unused);
+    __syncthreads();
+    if (tid < a.k) {
+        const int d = dests[tid];
+        int row = -1;
+        if (d >= 0) {
+            int s = cnt[d];
+            for (int j = 0; j < tid; ++j) s += (dests[j] == d);
+            if (s < a.cap)
+                row = d * a.cap + s;
+            else if (cb == 0)
+                atomicOr(a.status, MOE_STATUS_OVERFLOW);
+        }
+        rows[tid] = row;
+        if (cb == 0) {
+            a.slot_index[f] = row;
+            if (row >= 0) a.src_index[row] = (int32_t)f;
+        }
+    }
+    __syncthreads();
+
+    for (int j = 0; j < a.k; ++j) {
+        const int row = uniform(rows[j]);
+        if (row < 0) continue;
+        uint16_t *dst = a.ws + (int64_t)row * a.H;
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) {
+            if (col[q] >= vpr) continue;
+            u32x4 *p = reinterpret_cast<u32x4 *>(dst + off[q]);
+            if (NT)
+                __builtin_nontemporal_store(v[q], p);
+            else
+                *p = v[q];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // combine_kernel<VPT, JU, WEIGHTED, FUSED, NT>: grid = (T, column blocks);
 // FUSED runs with one column block so the whole row is in the workgroup.
 //
@@ -433,8 +550,11 @@ constexpr bool kCombineNT = true;
 template <int VPT> constexpr int combine_group() { return VPT >= 8 ? 4 : 8; }
 
 template <int VPT>
-void launch_copy_vpt(const DispatchArgs &a, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT>), grid, dim3(kThreads), 0, s, a);
+void launch_copy_vpt(const DispatchArgs &a, dim3 grid, hipStream_t s, bool small) {
+    if (small)
+        hipLaunchKernelGGL((dispatch_small_kernel<VPT, kCopyNT>), grid, dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT>), grid, dim3(kThreads), 0, s, a);
 }
 
 template <int VPT, bool FUSED>
@@ -463,15 +583,20 @@ hipError_t launch_route(const RouteArgs &a, int32_t n_chunks, hipStream_t s) {
     return hipGetLastError();
 }
 
+bool dispatch_is_small(int32_t num_tokens, int32_t top_k) {
+    return (int64_t)num_tokens * top_k <= kSmallItems;
+}
+
 hipError_t launch_dispatch_copy(const DispatchArgs &a, hipStream_t s) {
     const int vpt = streaming_vpt(a.T, a.H);
     const dim3 grid(a.T > 0 && !a.count_only ? a.T : 1,
                     a.T > 0 && !a.count_only ? column_blocks(a.H, vpt) : 1);
+    const bool small = !a.count_only && dispatch_is_small(a.T, a.k);
     switch (vpt) {
-        case 1: launch_copy_vpt<1>(a, grid, s); break;
-        case 2: launch_copy_vpt<2>(a, grid, s); break;
-        case 4: launch_copy_vpt<4>(a, grid, s); break;
-        default: launch_copy_vpt<8>(a, grid, s); break;
+        case 1: launch_copy_vpt<1>(a, grid, s, small); break;
+        case 2: launch_copy_vpt<2>(a, grid, s, small); break;
+        case 4: launch_copy_vpt<4>(a, grid, s, small); break;
+        default: launch_copy_vpt<8>(a, grid, s, small); break;
     }
     return hipGetLastError();
 }

@@ -12,6 +12,14 @@ namespace moe {
 // so the bound keeps that prefix small (<= kMaxChunks * ep integers).
 constexpr int kMaxChunks = 64;
 
+// Batches of at most this many routed copies dispatch in one launch: each
+// block counts the regions of all earlier copies itself (see
+// dispatch_small_kernel), so no separate routing kernel runs.
+constexpr int kSmallItems = 2048;
+
+// True when dispatch uses the single-launch path.
+bool dispatch_is_small(int32_t num_tokens, int32_t top_k);
+
 struct RoutePlan {
     int32_t tokens_per_chunk;
     int32_t n_chunks;
@@ -64,6 +72,8 @@ struct CombineArgs {
 };
 
 hipError_t launch_route(const RouteArgs &a, int32_t n_chunks, hipStream_t s);
+// Launches dispatch_small_kernel when dispatch_is_small(T, k) (no routing
+// kernel needed), dispatch_copy_kernel otherwise (after launch_route).
 hipError_t launch_dispatch_copy(const DispatchArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, bool fused, hipStream_t s);
 

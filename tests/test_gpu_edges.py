@@ -77,6 +77,8 @@ def roundtrip(x, ids, w, y, E, ep, cap, R=None, fused=False, eps=1e-6, seed=0):
     ("odd_hidden", 7, 9000, 5, 40, 5),
     ("max_regions_max_topk", 24, 64, 64, 512, 256),
     ("many_chunks_ragged", 4099, 24, 6, 36, 6),
+    ("single_launch_limit", 256, 128, 8, 64, 8),     # 2048 copies: one-launch dispatch
+    ("two_kernel_threshold", 257, 128, 8, 64, 8),    # 2056 copies: routing kernel + copy
 ])
 def test_roundtrip_shapes(case):
     name, T, H, k, E, ep = case
