@@ -47,6 +47,13 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_combine_residual_rmsnorm.argtypes = [
         _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, _P, ctypes.c_float, _P, _P, _P, _P]
     lib.oracle_combine_residual_rmsnorm.restype = ctypes.c_int
+    lib.oracle_dispatch_region.argtypes = lib.oracle_dispatch.argtypes
+    lib.oracle_dispatch_region.restype = ctypes.c_int
+    lib.oracle_combine_region.argtypes = [_P, _P, _I64, _I64, _I64, _P]
+    lib.oracle_combine_region.restype = ctypes.c_int
+    lib.oracle_combine_residual_rmsnorm_region.argtypes = [
+        _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_float, _P, _P, _P, _P]
+    lib.oracle_combine_residual_rmsnorm_region.restype = ctypes.c_int
     for name in ("oracle_bf16_to_f32_array", "oracle_f32_to_bf16_array",
                  "oracle_f64_to_bf16_array"):
         getattr(lib, name).argtypes = [_P, _P, _I64]
@@ -82,12 +89,15 @@ class Oracle:
 
     # -- the method --------------------------------------------------------
     def dispatch(self, x: np.ndarray, ids: np.ndarray, ep: int, epr: int, cap: int,
-                 ws: Optional[np.ndarray] = None, src_fill: int = -1) -> "DispatchResult":
+                 ws: Optional[np.ndarray] = None, src_fill: int = -1,
+                 layout: str = "copy") -> "DispatchResult":
         """Route every copy into the padded workspace.
 
-        ``ws`` may be passed in (e.g. pre-filled with canaries); otherwise an
-        uninitialised [ep, cap, H] array is allocated, whose padding rows stay
-        untouched (so never committed to memory by the OS).
+        ``layout`` is "copy" (one row per routed copy) or "region" (one row
+        per token and destination region).  ``ws`` may be passed in (e.g.
+        pre-filled with canaries); otherwise an uninitialised [ep, cap, H]
+        array is allocated, whose padding rows stay untouched (so never
+        committed to memory by the OS).
         """
         x = np.ascontiguousarray(x, dtype=np.uint16)
         ids = np.ascontiguousarray(ids, dtype=np.int32)
@@ -99,17 +109,24 @@ class Oracle:
         counts = np.zeros(ep, dtype=np.int32)
         slot_index = np.empty(T * k, dtype=np.int32)
         src_index = np.full(ep * cap, src_fill, dtype=np.int32)
-        status = self.lib.oracle_dispatch(
+        fn = {"copy": self.lib.oracle_dispatch, "region": self.lib.oracle_dispatch_region}[layout]
+        status = fn(
             x.ctypes.data, ids.ctypes.data, T, H, k, ep, epr, cap, ws.ctypes.data,
             counts.ctypes.data, slot_index.ctypes.data, src_index.ctypes.data)
         return DispatchResult(ws=ws, counts=counts, slot_index=slot_index.reshape(T, k),
                               src_index=src_index.reshape(ep, cap), status=status)
 
     def combine(self, y: np.ndarray, slot_index: np.ndarray, weights: Optional[np.ndarray],
-                weighted: bool, H: int) -> np.ndarray:
+                weighted: bool, H: int, layout: str = "copy") -> np.ndarray:
         y = np.ascontiguousarray(y, dtype=np.uint16)
         slot_index = np.ascontiguousarray(slot_index, dtype=np.int32)
         T, k = slot_index.shape
+        if layout == "region":
+            assert not weighted, "the per-region combine is unweighted"
+            out = np.empty((T, H), dtype=np.uint16)
+            self.lib.oracle_combine_region(y.ctypes.data, slot_index.ctypes.data, T, H, k,
+                                           out.ctypes.data)
+            return out
         w = np.ascontiguousarray(weights if weights is not None else np.zeros((T, k)),
                                  dtype=np.float32)
         out = np.empty((T, H), dtype=np.uint16)
@@ -119,7 +136,7 @@ class Oracle:
 
     def combine_residual_rmsnorm(self, y, slot_index, weights, weighted: bool,
                                  residual: np.ndarray, gamma: np.ndarray, eps: float,
-                                 want_f64: bool = False):
+                                 want_f64: bool = False, layout: str = "copy"):
         """Returns (residual_out, normed[, normed_f64])."""
         y = np.ascontiguousarray(y, dtype=np.uint16)
         slot_index = np.ascontiguousarray(slot_index, dtype=np.int32)
@@ -133,11 +150,18 @@ class Oracle:
         normed = np.empty((T, H), dtype=np.uint16)
         nf64 = np.empty((T, H), dtype=np.float64) if want_f64 else None
         scratch = np.empty(H, dtype=np.float32)
-        self.lib.oracle_combine_residual_rmsnorm(
-            y.ctypes.data, slot_index.ctypes.data, w.ctypes.data, int(bool(weighted)),
-            T, H, k, residual.ctypes.data, gamma.ctypes.data, float(eps),
-            res_out.ctypes.data, normed.ctypes.data,
-            nf64.ctypes.data if want_f64 else None, scratch.ctypes.data)
+        if layout == "region":
+            assert not weighted, "the per-region combine is unweighted"
+            self.lib.oracle_combine_residual_rmsnorm_region(
+                y.ctypes.data, slot_index.ctypes.data, T, H, k, residual.ctypes.data,
+                gamma.ctypes.data, float(eps), res_out.ctypes.data, normed.ctypes.data,
+                nf64.ctypes.data if want_f64 else None, scratch.ctypes.data)
+        else:
+            self.lib.oracle_combine_residual_rmsnorm(
+                y.ctypes.data, slot_index.ctypes.data, w.ctypes.data, int(bool(weighted)),
+                T, H, k, residual.ctypes.data, gamma.ctypes.data, float(eps),
+                res_out.ctypes.data, normed.ctypes.data,
+                nf64.ctypes.data if want_f64 else None, scratch.ctypes.data)
         return (res_out, normed, nf64) if want_f64 else (res_out, normed)
 
 
@@ -166,8 +190,14 @@ def load(rebuild: bool = False) -> Oracle:
 
 
 def place_expert_outputs(ws: np.ndarray, slot_index: np.ndarray, y_rows: np.ndarray) -> None:
-    """Expert stage: write each copy's output row into the row it was routed to."""
+    """Expert stage: write each copy's output row into the row it was routed to.
+
+    Under the per-region layout pass one message per first copy (rows of the
+    other copies are ignored: they share the first copy's row)."""
     flat = ws.reshape(-1, ws.shape[-1])
     s = slot_index.reshape(-1)
     valid = s >= 0
-    flat[s[valid]] = y_rows[valid]
+    _, first = np.unique(s, return_index=True)     # first copy naming each row
+    first = first[s[first] >= 0]
+    flat[s[first]] = y_rows[first]
+    assert valid.sum() >= first.size

@@ -162,3 +162,61 @@ def combine_residual_rmsnorm(y_rows, slot_index, weights, weighted: bool, residu
         normed.append([round_to_bf16_bits(v * inv * bf16_value(int(gamma_bits[h])))
                        for h, v in enumerate(s)])
     return res_out, normed
+
+
+def dispatch_region(x_bits: np.ndarray, ids: np.ndarray, ep: int, epr: int, cap: int):
+    """Per-region layout: one row per (token, region) for the token's first
+    copy to that region; later copies to the same region share its row.
+    Returns (rows, counts, slot_index, src_index, status) like ``dispatch``."""
+    T, H = x_bits.shape
+    k = ids.shape[1]
+    E = ep * epr
+    regions: List[List[int]] = [[] for _ in range(ep)]
+    slot_index = [[-1] * k for _ in range(T)]
+    status = 0
+    for t in range(T):
+        seen = {}                                  # region -> slot of the token's first copy
+        for j in range(k):
+            e = int(ids[t][j])
+            if e == -1:
+                continue
+            if not (0 <= e < E):
+                status |= 2
+                continue
+            r = e // epr
+            if r in seen:
+                slot_index[t][j] = seen[r]
+                continue
+            s = len(regions[r])
+            regions[r].append(t * k + j)
+            slot = r * cap + s if s < cap else -1
+            if s >= cap:
+                status |= 1
+            seen[r] = slot
+            slot_index[t][j] = slot
+    counts = [len(g) for g in regions]
+    src_index, rows = {}, {}
+    for r in range(ep):
+        for s, f in enumerate(regions[r][:cap]):
+            src_index[(r, s)] = f
+            rows[(r, s)] = [int(v) for v in x_bits[f // k]]
+    return rows, counts, slot_index, src_index, status
+
+
+def combine_region(y_rows, slot_index, T: int, H: int, cap: int) -> List[List[int]]:
+    """Each distinct row of a token added once (order of first copies), fp32,
+    narrowed once."""
+    out = []
+    for t in range(T):
+        distinct = []
+        for row in slot_index[t]:
+            if row >= 0 and row not in distinct:
+                distinct.append(row)
+        line = []
+        for h in range(H):
+            acc = Fraction(0)
+            for row in distinct:
+                acc = round_binary(acc + bf16_value(int(y_rows[(row // cap, row % cap)][h])), FP32)
+            line.append(round_to_bf16_bits(acc))
+        out.append(line)
+    return out

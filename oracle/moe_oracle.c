@@ -40,7 +40,11 @@
  *  - fused epilogue: s = acc + residual in fp32 (the accumulator is not
  *    narrowed first); residual_out = bf16(s); the mean of squares, the
  *    reciprocal square root and the scaling by gamma in fp64 (the oracle is
- *    the more precise side), eps inside the square root, mean over H.
+ *    the more precise side), eps inside the square root, mean over H;
+ *  - per-region layout (the FlashInfer form): one row per (token, region),
+ *    taken by the token's first copy to that region; the row's message (the
+ *    region's gated, fp32-summed, once-narrowed expert outputs) is added once,
+ *    in the order of first copies, unweighted.
  */
 #include <math.h>
 #include <stdint.h>
@@ -138,6 +142,80 @@ int oracle_dispatch(const uint16_t *x, const int32_t *ids,
     return status;
 }
 
+/* ---- per-region layout ([A2A] "Update -- the correctness failures are
+ * resolved": the FlashInfer dispatch sends a token once per destination
+ * rank and blanks the duplicate-rank top-k slots; "Bring-up progress":
+ * about 5.3 distinct ranks per token for top-8 over 8 ranks; "Synthesis":
+ * duplicate experts on one rank are read once; the combine is an unweighted
+ * sum of one message per rank).
+ * One row per (token, region): the first copy f = t*k + j of token t bound
+ * for region r takes the next row of r; later copies of t bound for r share
+ * that row (slot_index equal, src_index holds the first copy).  Rows fill a
+ * region in increasing f of their first copy.  Overflow, bad ids and -1 as in
+ * oracle_dispatch. */
+static int first_copy_to_region(const int32_t *ids, int64_t t, int64_t j, int64_t k,
+                                int64_t epr, int64_t E, int64_t *first_j)
+{
+    int64_t r = ids[t * k + j] / epr;
+    for (int64_t i = 0; i < j; ++i) {
+        int32_t e = ids[t * k + i];
+        if (e >= 0 && e < E && e / epr == r) {
+            *first_j = i;
+            return 0;
+        }
+    }
+    *first_j = j;
+    return 1;
+}
+
+int oracle_dispatch_region(const uint16_t *x, const int32_t *ids,
+                           int64_t T, int64_t H, int64_t k, int64_t ep, int64_t epr,
+                           int64_t cap, uint16_t *ws, int32_t *counts,
+                           int32_t *slot_index, int32_t *src_index)
+{
+    int status = 0;
+    int64_t E = ep * epr;
+    for (int64_t r = 0; r < ep; ++r)
+        counts[r] = 0;
+    for (int64_t f = 0; f < T * k; ++f) {
+        int32_t e = ids[f];
+        slot_index[f] = -1;
+        if (e == -1)
+            continue;
+        if (e < 0 || e >= E) {
+            status |= ORACLE_STATUS_BAD_ID;
+            continue;
+        }
+        int64_t t = f / k, j = f % k, first_j;
+        if (!first_copy_to_region(ids, t, j, k, epr, E, &first_j)) {
+            slot_index[f] = slot_index[t * k + first_j];
+            continue;
+        }
+        int64_t r = e / epr;
+        int64_t s = counts[r];
+        counts[r] += 1;
+        if (s >= cap) {
+            status |= ORACLE_STATUS_OVERFLOW;
+            continue;
+        }
+        int64_t row = r * cap + s;
+        slot_index[f] = (int32_t)row;
+        src_index[row] = (int32_t)f;
+        memcpy(ws + row * H, x + t * H, (size_t)H * sizeof(uint16_t));
+    }
+    return status;
+}
+
+/* True if an earlier copy of token t already names the same row: under the
+ * per-region layout that row's message has been added, so it is skipped. */
+static int row_seen_before(const int32_t *slot_index, int64_t t, int64_t j, int64_t k)
+{
+    for (int64_t i = 0; i < j; ++i)
+        if (slot_index[t * k + i] == slot_index[t * k + j])
+            return 1;
+    return 0;
+}
+
 /* ---- combine: reduce exactly once ([A2A] "Update -- ... resolved", [DR]) ----
  * out[t, h] = bf16( sum over j = 0..k-1 with slot_index[t,j] >= 0 of
  *                   c_j * f32(y[slot_index[t,j], h]) )
@@ -145,12 +223,14 @@ int oracle_dispatch(const uint16_t *x, const int32_t *ids,
  * out is overwritten, never accumulated into. */
 static float combine_accumulate(const uint16_t *y, const int32_t *slot_index,
                                 const float *w, int weighted, int64_t t,
-                                int64_t h, int64_t H, int64_t k)
+                                int64_t h, int64_t H, int64_t k, int once_per_row)
 {
     float acc = 0.0f;
     for (int64_t j = 0; j < k; ++j) {
         int32_t row = slot_index[t * k + j];
         if (row < 0)
+            continue;
+        if (once_per_row && row_seen_before(slot_index, t, j, k))
             continue;
         float v = oracle_bf16_to_f32(y[(int64_t)row * H + h]);
         if (weighted)
@@ -161,13 +241,29 @@ static float combine_accumulate(const uint16_t *y, const int32_t *slot_index,
     return acc;
 }
 
-int oracle_combine(const uint16_t *y, const int32_t *slot_index, const float *w,
-                   int weighted, int64_t T, int64_t H, int64_t k, uint16_t *out)
+static void combine_rows(const uint16_t *y, const int32_t *slot_index, const float *w,
+                         int weighted, int64_t T, int64_t H, int64_t k, int once_per_row,
+                         uint16_t *out)
 {
     for (int64_t t = 0; t < T; ++t)
         for (int64_t h = 0; h < H; ++h)
             out[t * H + h] = oracle_f32_to_bf16(
-                combine_accumulate(y, slot_index, w, weighted, t, h, H, k));
+                combine_accumulate(y, slot_index, w, weighted, t, h, H, k, once_per_row));
+}
+
+int oracle_combine(const uint16_t *y, const int32_t *slot_index, const float *w,
+                   int weighted, int64_t T, int64_t H, int64_t k, uint16_t *out)
+{
+    combine_rows(y, slot_index, w, weighted, T, H, k, 0, out);
+    return 0;
+}
+
+/* Per-region layout: each distinct row of a token is added once, in the order
+ * of its first copy; the messages already carry the gates (unweighted). */
+int oracle_combine_region(const uint16_t *y, const int32_t *slot_index,
+                          int64_t T, int64_t H, int64_t k, uint16_t *out)
+{
+    combine_rows(y, slot_index, NULL, 0, T, H, k, 1, out);
     return 0;
 }
 
@@ -178,17 +274,16 @@ int oracle_combine(const uint16_t *y, const int32_t *slot_index, const float *w,
  * residual_out may alias residual (each element is read before it is written).
  * normed_f64, if not NULL, receives the unrounded fp64 normed values.
  * s_scratch is caller memory of H floats. */
-int oracle_combine_residual_rmsnorm(const uint16_t *y, const int32_t *slot_index,
-                                    const float *w, int weighted, int64_t T,
-                                    int64_t H, int64_t k, const uint16_t *residual,
-                                    const uint16_t *gamma, float eps,
-                                    uint16_t *residual_out, uint16_t *normed,
-                                    double *normed_f64, float *s_scratch)
+static void fused_rows(const uint16_t *y, const int32_t *slot_index, const float *w,
+                       int weighted, int once_per_row, int64_t T, int64_t H, int64_t k,
+                       const uint16_t *residual, const uint16_t *gamma, float eps,
+                       uint16_t *residual_out, uint16_t *normed, double *normed_f64,
+                       float *s_scratch)
 {
     for (int64_t t = 0; t < T; ++t) {
         double sumsq = 0.0;
         for (int64_t h = 0; h < H; ++h) {
-            float acc = combine_accumulate(y, slot_index, w, weighted, t, h, H, k);
+            float acc = combine_accumulate(y, slot_index, w, weighted, t, h, H, k, once_per_row);
             float s = acc + oracle_bf16_to_f32(residual[t * H + h]);
             s_scratch[h] = s;
             sumsq += (double)s * (double)s;
@@ -202,6 +297,29 @@ int oracle_combine_residual_rmsnorm(const uint16_t *y, const int32_t *slot_index
                 normed_f64[t * H + h] = n;
         }
     }
+}
+
+int oracle_combine_residual_rmsnorm(const uint16_t *y, const int32_t *slot_index,
+                                    const float *w, int weighted, int64_t T,
+                                    int64_t H, int64_t k, const uint16_t *residual,
+                                    const uint16_t *gamma, float eps,
+                                    uint16_t *residual_out, uint16_t *normed,
+                                    double *normed_f64, float *s_scratch)
+{
+    fused_rows(y, slot_index, w, weighted, 0, T, H, k, residual, gamma, eps, residual_out,
+               normed, normed_f64, s_scratch);
+    return 0;
+}
+
+int oracle_combine_residual_rmsnorm_region(const uint16_t *y, const int32_t *slot_index,
+                                           int64_t T, int64_t H, int64_t k,
+                                           const uint16_t *residual, const uint16_t *gamma,
+                                           float eps, uint16_t *residual_out,
+                                           uint16_t *normed, double *normed_f64,
+                                           float *s_scratch)
+{
+    fused_rows(y, slot_index, NULL, 0, 1, T, H, k, residual, gamma, eps, residual_out, normed,
+               normed_f64, s_scratch);
     return 0;
 }
 

@@ -117,3 +117,33 @@ def expert_outputs(wl: Workload, inp: Inputs) -> np.ndarray:
         y = (y * inp.weights.reshape(-1)[:, None]).astype(np.float32)
         return f32_to_bf16_bits(y)
     raise ValueError(f"unknown expert stage {wl.expert!r}")
+
+
+def region_messages(ids: np.ndarray, weights: np.ndarray, y_rows: np.ndarray, epr: int,
+                    gated: bool = True) -> np.ndarray:
+    """The expert side's message under the per-region layout, uint16 [T*k, H].
+
+    Region r's experts return, for token t, one row: the sum of the token's
+    copies local to r, each gated (w_j * y_j, fp32 product) when ``gated``,
+    accumulated in fp32 in j order and rounded to bf16 once.  The message sits
+    at the flat index of the token's first copy to r; other rows are zero.
+    """
+    T, k = ids.shape
+    H = y_rows.shape[1]
+    region = np.where(ids >= 0, ids // epr, -1)
+    y = bf16_bits_to_f32(y_rows).reshape(T, k, H)
+    w = weights.astype(np.float32) if gated else np.ones((T, k), np.float32)
+    out = np.zeros((T, k, H), dtype=np.uint16)
+    for j in range(k):
+        first = region[:, j] >= 0
+        for i in range(j):
+            first &= region[:, i] != region[:, j]
+        if not first.any():
+            continue
+        acc = np.zeros((int(first.sum()), H), dtype=np.float32)
+        for i in range(j, k):
+            same = (region[first, i] == region[first, j])[:, None]
+            term = (y[first, i] * w[first, i][:, None]).astype(np.float32)
+            acc = np.where(same, (acc + term).astype(np.float32), acc)
+        out[first, j] = f32_to_bf16_bits(acc)
+    return out.reshape(T * k, H)

@@ -496,4 +496,172 @@ def pin_rmsnorm_scale_invariance(o):
     assert np.array_equal(torch_bf16_bits(torch_bf16_value(r1) * 2), r2)
 
 
+# --------------------------------------------------- per-region layout pins
+# The FlashInfer form the pages measure: one row per (token, region), the
+# region's experts return one message per token, the combine adds each
+# region's message once.  InferenceX PR #2450 prints the probes used here:
+# "Synthesis" (duplicate experts on one rank read once -> 1.0; partial routing
+# to two destinations -> 2.0; 2^rank over 8 ranks -> 255), "The oracle was
+# never wrong" (seven staged per-rank messages -> 0.255859375) and "Bring-up
+# progress" (about 5.3 distinct ranks per token for top-8 over 8 ranks).
+
+def _region_combine_of(o, ids, ep, messages, H=8):
+    """Per-region dispatch of ids (expert = region, epr = 1) with region r's
+    rows holding messages[r], then the per-region combine."""
+    x = np.zeros((ids.shape[0], H), np.uint16)
+    d = o.dispatch(x, ids, ep, 1, ids.shape[0], layout="region")
+    flat = d.ws.reshape(-1, H)
+    for r in range(ep):
+        for s in range(int(d.counts[r])):
+            flat[r * ids.shape[0] + s] = printed_bits(messages[r])
+    return d, o.combine(d.ws, d.slot_index, None, False, H, layout="region")
+
+
+def pin_region_duplicates_read_once(o):
+    ids = np.array([[0, 0]], np.int32)               # both experts on region 0
+    d, out = _region_combine_of(o, ids, 1, [1.0])
+    assert list(d.counts) == [1]
+    assert d.slot_index[0, 0] == d.slot_index[0, 1] == 0
+    assert (out == exact_bits(1.0)).all()            # read once, not 2.0
+
+
+def pin_region_partial_routing(o):
+    ids = np.array([[0, 1, 0, 1], [1, 1, 0, 0], [0, 0, 0, 1], [1, 0, 1, 1]], np.int32)
+    d, out = _region_combine_of(o, ids, 2, [1.0, 1.0])
+    assert list(d.counts) == [4, 4]
+    assert (out == exact_bits(2.0)).all()
+
+
+def pin_region_power_of_two(o):
+    g = read_golden("power_of_two_probe.txt")
+    msgs = [float(v) for v in g["contributions"][0]]
+    ids = np.array([[3, 0, 1, 2, 4, 5, 7, 6, 0, 3]], np.int32)   # 8 regions, 2 duplicates
+    d, out = _region_combine_of(o, ids, 8, msgs)
+    assert (out == exact_bits(float(g["expected"][0][0]))).all(), hex(out[0, 0])
+
+
+def pin_region_staged_sum(o):
+    g = read_golden("staged_sum.txt")
+    msgs = [0.0] * 8
+    for r, v in g["contribution"]:
+        msgs[int(r)] = float(v)
+    ids = np.array([[0, 1, 2, 4, 5, 6, 7, 0]], np.int32)   # region 3 hosts none; 0 hosts two
+    d, out = _region_combine_of(o, ids, 8, msgs)
+    assert d.counts[3] == 0 and d.counts.sum() == 7
+    assert (out == exact_bits(float(g["expected"][0][0]))).all(), hex(out[0, 0])
+
+
+def pin_region_counts_distinct(o):
+    rng = np.random.default_rng(17)
+    for (T, k, E, ep) in [(200, 8, 64, 8), (97, 4, 12, 3), (50, 6, 6, 6), (33, 3, 20, 1)]:
+        epr = E // ep
+        ids = _random_routing(rng, T, k, E, p_missing=0.1)
+        d = o.dispatch(random_bf16(rng, (T, 8)), ids, ep, epr, T, layout="region")
+        reg = np.where(ids >= 0, ids // epr, -1)
+        want = [int((reg == r).any(axis=1).sum()) for r in range(ep)]
+        assert list(d.counts) == want, (d.counts, want)
+        assert d.status == 0
+
+
+def pin_region_layout(o):
+    rng = np.random.default_rng(19)
+    T, H, k, E, ep = 150, 16, 6, 24, 4
+    epr = E // ep
+    ids = _random_routing(rng, T, k, E, p_missing=0.05)
+    x = random_bf16(rng, (T, H))
+    ws = np.full((ep, T, H), CANARY, dtype=np.uint16)
+    d = o.dispatch(x, ids, ep, epr, T, ws=ws, layout="region")
+    reg = np.where(ids >= 0, ids // epr, -1)
+    for r in range(ep):
+        n = int(d.counts[r])
+        src = d.src_index[r, :n]
+        assert (np.diff(src) > 0).all()
+        toks = src // k
+        assert np.array_equal(toks, np.nonzero((reg == r).any(axis=1))[0])
+        # the row's copy is the token's first copy to r
+        assert all(reg[t, :f % k].tolist().count(r) == 0 and reg[t, f % k] == r
+                   for t, f in zip(toks, src))
+        assert np.array_equal(ws[r, :n], x[toks])
+        assert (ws[r, n:] == CANARY).all()
+    for t in range(T):                         # copies to one region share its row
+        for j in range(k):
+            if reg[t, j] < 0:
+                assert d.slot_index[t, j] == -1
+            else:
+                row = d.slot_index[t, j]
+                assert row // T == reg[t, j] and d.src_index.reshape(-1)[row] // k == t
+
+
+def pin_region_full_routing_token_order(o):
+    rng = np.random.default_rng(23)
+    T, k = 5, 8
+    ids = np.stack([rng.permutation(8) for _ in range(T)]).astype(np.int32)
+    x = np.stack([np.full(8, exact_bits(float(t)), np.uint16) for t in range(T)])
+    d = o.dispatch(x, ids, 8, 1, T, layout="region")
+    assert (d.counts == T).all()
+    for r in range(8):
+        assert np.array_equal(d.src_index[r] // k, np.arange(T))
+
+
+def pin_region_matches_copy_combine_without_duplicates(o):
+    # skipping a duplicate row is the same as that copy being unrouted: the
+    # per-region combine equals the (pinned) per-copy combine and fused
+    # epilogue on a slot map whose duplicates are set to -1
+    rng = np.random.default_rng(29)
+    T, H, k, E, ep = 40, 64, 6, 12, 4
+    ids = _random_routing(rng, T, k, E, p_missing=0.1)
+    d = o.dispatch(random_bf16(rng, (T, H)), ids, ep, E // ep, T, layout="region")
+    d.ws[...] = random_bf16(rng, d.ws.shape)
+    masked = d.slot_index.copy()
+    for t in range(T):
+        for j in range(k):
+            if masked[t, j] >= 0 and masked[t, j] in d.slot_index[t, :j]:
+                masked[t, j] = -1
+    assert (masked != d.slot_index).any()
+    got = o.combine(d.ws, d.slot_index, None, False, H, layout="region")
+    assert np.array_equal(got, o.combine(d.ws, masked, None, False, H))
+    res = random_bf16(rng, (T, H))
+    gamma = torch_bf16_bits(rng.uniform(0.5, 1.5, H).astype(np.float32))
+    a = o.combine_residual_rmsnorm(d.ws, d.slot_index, None, False, res, gamma, 1e-6,
+                                   layout="region")
+    b = o.combine_residual_rmsnorm(d.ws, masked, None, False, res, gamma, 1e-6)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def pin_region_brute(o):
+    # every routing of one token x 3 copies with ids in -1..4 (4 out of range),
+    # and a seeded sample of two-token routings, over four layouts
+    k, E, H = 3, 4, 3
+    rng = np.random.default_rng(31)
+    y = random_bf16(rng, (8 * 4, H))
+    combos = [c for c in itertools.product(range(-1, 5), repeat=k)]
+    combos += [tuple(rng.integers(-1, 5, size=2 * k)) for _ in range(150)]
+    for ep, cap in [(2, 2), (2, 1), (4, 1), (1, 2)]:
+        epr = E // ep
+        for combo in combos:
+            T = len(combo) // k
+            x = random_bf16(np.random.default_rng(T), (T, H))
+            ids = np.array(combo, dtype=np.int32).reshape(T, k)
+            d = o.dispatch(x, ids, ep, epr, cap, layout="region")
+            rows, counts, slot, src, status = brute.dispatch_region(x, ids, ep, epr, cap)
+            assert (d.status, list(d.counts), d.slot_index.tolist()) == (status, counts, slot), combo
+            for (r, s_), f in src.items():
+                assert d.src_index[r, s_] == f and d.ws[r, s_].tolist() == rows[(r, s_)], combo
+            d.ws[...] = y[: ep * cap].reshape(d.ws.shape)
+            yr = {(r, s_): list(d.ws[r, s_]) for r in range(ep) for s_ in range(cap)}
+            got = o.combine(d.ws, d.slot_index, None, False, H, layout="region")
+            assert got.tolist() == brute.combine_region(yr, d.slot_index.tolist(), T, H, cap), combo
+
+
+def pin_region_distinct_closed_form(o):
+    g = read_golden("routing_statistics.txt")
+    E, k, ep = int(g["E"][0][0]), int(g["k"][0][0]), int(g["ep"][0][0])
+    rng = np.random.default_rng(0)
+    T = 4096
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    d = o.dispatch(np.zeros((T, 1), np.uint16), ids, ep, E // ep, T, layout="region")
+    per_token = d.counts.sum() / T
+    assert abs(per_token - float(g["distinct_regions_closed_form"][0][0])) < 0.03, per_token
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -14,6 +14,10 @@ import pytest
 import oracle
 import pins
 
+# (name, anchor text, replacement[, which occurrence of the anchor]); the
+# per-copy dispatch comes before the per-region one in the source, so shared
+# anchors name the per-copy code with occurrence 0 and the per-region code
+# with occurrence 1.
 MUTATIONS = [
     # combine
     ("drop_last_term",
@@ -51,7 +55,7 @@ MUTATIONS = [
      "uint32_t bits = (uint32_t)h << 16;",
      "uint32_t bits = (uint32_t)h << 15;"),
     # dispatch
-    ("region_by_modulo",
+    ("copy_region_by_modulo",
      "int64_t r = e / epr;",
      "int64_t r = e % ep;"),
     ("src_index_holds_token",
@@ -85,6 +89,22 @@ MUTATIONS = [
     ("residual_out_from_combine_only",
      "residual_out[t * H + h] = oracle_f32_to_bf16(s_scratch[h]);",
      "residual_out[t * H + h] = oracle_f32_to_bf16(s_scratch[h] - oracle_bf16_to_f32(residual[t * H + h]));"),
+    # per-region layout (second occurrences are in oracle_dispatch_region)
+    ("region_by_modulo", "int64_t r = e / epr;", "int64_t r = e % ep;", 1),
+    ("region_src_holds_token", "src_index[row] = (int32_t)f;",
+     "src_index[row] = (int32_t)(f / k);", 1),
+    ("region_rows_fill_from_the_end", "int64_t row = r * cap + s;",
+     "int64_t row = r * cap + (cap - 1 - s);", 1),
+    ("region_no_dedup", "*first_j = i;\n            return 0;",
+     "*first_j = i;\n            return 1;"),
+    ("region_duplicate_added_twice",
+     "if (once_per_row && row_seen_before(slot_index, t, j, k))", "if (0)"),
+    ("region_duplicate_loses_row", "slot_index[f] = slot_index[t * k + first_j];",
+     "slot_index[f] = slot_index[f];"),
+    ("region_copies_wrong_token", "memcpy(ws + row * H, x + t * H,",
+     "memcpy(ws + row * H, x + (t + 1 == T ? 0 : t + 1) * H,"),
+    ("region_first_copy_scan_skips_copy_0", "for (int64_t i = 0; i < j; ++i) {\n        int32_t e = ids[t * k + i];",
+     "for (int64_t i = 1; i < j; ++i) {\n        int32_t e = ids[t * k + i];"),
 ]
 
 
@@ -93,7 +113,7 @@ def _failed_pins(o):
     for pin in pins.ALL_PINS:
         try:
             pin(o)
-        except AssertionError:
+        except Exception:             # a wrong value, or a pin that cannot even index it
             failed.append(pin.__name__)
     return failed
 
@@ -102,13 +122,22 @@ def test_unmodified_oracle_passes_every_pin(orc):
     assert _failed_pins(orc) == []
 
 
-@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_mutation_is_caught(tmp_path, name, old, new):
+def _replace_nth(text, old, new, nth):
+    start = -1
+    for _ in range(nth + 1):
+        start = text.index(old, start + 1)
+    return text[:start] + new + text[start + len(old):]
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(tmp_path, mutation):
+    name, old, new = mutation[:3]
+    nth = mutation[3] if len(mutation) > 3 else 0
     src = open(oracle.SOURCE).read()
-    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    assert src.count(old) > nth, f"mutation anchor for {name} not found"
     mutated = os.path.join(tmp_path, "mutant.c")
     with open(mutated, "w") as fh:
-        fh.write(src.replace(old, new))
+        fh.write(_replace_nth(src, old, new, nth))
     lib = oracle.build(mutated, os.path.join(tmp_path, f"libmutant_{name}.so"))
     failed = _failed_pins(oracle.Oracle(lib))
     assert failed, f"mutation {name} passed every pin"
