@@ -26,7 +26,10 @@ line also carries:
                 same workload, repeated for about 10 s
   cold          per-kernel p50 / mean over --cold-iters launches, each after
                 an untimed 1 GiB read that evicts the 256 MB Infinity Cache
-  workloads     the same step on the skewed, decode and fused workloads
+  workloads     the same step on the skewed, decode and fused workloads, and
+                on prefill and skewed under the per-region layout (one row per
+                token and destination region, the form the FlashInfer pages
+                measure; unweighted combine of per-region messages)
 """
 from __future__ import annotations
 
@@ -119,7 +122,8 @@ def describe(wl, cap) -> str:
             f"rung={wl.R} {wl.routing} routing, {mode}")
 
 
-def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0) -> dict:
+def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0,
+            layout: str = "copy") -> dict:
     import numpy as np
     import torch
 
@@ -130,14 +134,15 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0) -
     inp = synth.make_inputs(wl, seed)
     x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
     ids = torch.from_numpy(inp.ids).to(dev)
-    weighted = wl.combine in ("weighted", "both", "fused")
+    # the per-region layout's combine is an unweighted sum of per-region messages
+    weighted = wl.combine in ("weighted", "both", "fused") and layout == "copy"
     w = torch.from_numpy(inp.weights).to(dev) if weighted else None
-    cap = wl.cap
+    cap = wl.cap if layout == "copy" else wl.R   # a token has at most one row per region
     if cap is None:                              # size the regions from the routing itself
         probe = moe.MoeA2A(wl.T, wl.H, wl.k, wl.E, wl.ep, 1, device=dev)
         cap = int(moe.moe_route_counts(probe, ids).max().item())
         del probe
-    h = moe.MoeA2A(wl.R, wl.H, wl.k, wl.E, wl.ep, cap, device=dev)
+    h = moe.MoeA2A(wl.R, wl.H, wl.k, wl.E, wl.ep, cap, device=dev, layout=layout)
     ws = h.new_workspace()
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
     fused = wl.combine == "fused"
@@ -156,7 +161,7 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0) -
         if ev is not None:
             hev.record(ev[1], sh)
         if fused:
-            moe.moe_combine_residual_rmsnorm(h, ws, w, True, res, gamma, wl.eps,
+            moe.moe_combine_residual_rmsnorm(h, ws, w, weighted, res, gamma, wl.eps,
                                              residual_out=res_out, normed=out, stream=stream)
         else:
             moe.moe_combine(h, ws, w, weighted, out=out, stream=stream)
@@ -208,7 +213,7 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0) -
         flush.max()
         hev.record(ev[2], sh)
         if fused:
-            moe.moe_combine_residual_rmsnorm(h, ws, w, True, res, gamma, wl.eps,
+            moe.moe_combine_residual_rmsnorm(h, ws, w, weighted, res, gamma, wl.eps,
                                              residual_out=res_out, normed=out, stream=stream)
         else:
             moe.moe_combine(h, ws, w, weighted, out=out, stream=stream)
@@ -221,11 +226,15 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0) -
         for ev in e:
             hev.destroy(ev)
     del flush
-    b = wl.algorithmic_bytes()
+    if layout == "copy":
+        b = wl.algorithmic_bytes()
+    else:
+        b = region_bytes(wl, int(h.counts.sum().item()))
     comb_bytes = b["fused"] if fused else b["combine"]
     ms = elapsed * 1e3 / steps
     res_d = {
-        "workload": describe(wl, cap),
+        "workload": describe(wl, cap) + ("" if layout == "copy" else
+                                         ", per-region layout (one row per token and region)"),
         "ms_per_step": ms,
         "ms_per_step_instrumented": elapsed_ev * 1e3 / steps,
         "tokens_per_s": wl.T / (ms / 1e3),
@@ -243,6 +252,20 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0) -
     del ws, h
     torch.cuda.empty_cache()
     return res_d
+
+
+def region_bytes(wl, rows: int) -> dict:
+    """Algorithmic bytes under the per-region layout with ``rows`` rows sent:
+    dispatch reads x and ids, writes the rows, slot_index and src_index;
+    combine reads slot_index and the rows, writes out (fused: + residual in,
+    residual and normed out, gamma once)."""
+    T, H, k = wl.T, wl.H, wl.k
+    row = 2 * H
+    return {
+        "dispatch": T * (row + 8 * k) + rows * (row + 4),
+        "combine": T * (row + 4 * k) + rows * row,
+        "fused": T * (3 * row + 4 * k) + rows * row + row,
+    }
 
 
 def cold_stats(cd_ms, cc_ms, iters, T, disp_bytes, comb_bytes) -> dict:
@@ -304,8 +327,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill")
-    ap.add_argument("--extras", default="skewed,decode,fused",
-                    help="comma-separated workloads also measured (empty for none)")
+    ap.add_argument("--extras", default="skewed,decode,fused,prefill_region,skewed_region",
+                    help="comma-separated workloads also measured (empty for none); a "
+                         "_region suffix runs the per-region layout")
     ap.add_argument("--cold-iters", type=int, default=100,
                     help="launches timed after an untimed 1 GiB cache-evicting read, per kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -328,8 +352,10 @@ def main() -> int:
     main_res = measure(wl, args.steps, args.warmup, args.cold_iters)
     extras = {}
     for name in [n for n in args.extras.split(",") if n and n != wl.name]:
-        extras[name] = measure(synth.BY_NAME[name], max(args.steps // 2, 5),
-                               max(args.warmup // 2, 2), args.cold_iters)
+        base, _, layout = name.partition("_")
+        extras[name] = measure(synth.BY_NAME[base], max(args.steps // 2, 5),
+                               max(args.warmup // 2, 2), args.cold_iters,
+                               layout=layout or "copy")
 
     comb_ms = main_res["combine_ms_mean"]
     achieved = main_res["combine_bytes"] / (comb_ms / 1e3) / 1e9

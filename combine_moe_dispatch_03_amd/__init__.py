@@ -32,6 +32,9 @@ MOE_ERR_PHASE = -2
 MOE_ERR_OVERFLOW = -3
 MOE_ERR_EXPERT_ID = -4
 MOE_ERR_HIP = -5
+MOE_LAYOUT_PER_COPY = 0
+MOE_LAYOUT_PER_REGION = 1
+LAYOUTS = {"copy": MOE_LAYOUT_PER_COPY, "region": MOE_LAYOUT_PER_REGION}
 MOE_STATUS_OVERFLOW = 1
 MOE_STATUS_EXPERT_ID = 2
 MOE_MAX_EP = 256
@@ -51,7 +54,7 @@ class MoeHandle(ctypes.Structure):
         ("max_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
         ("top_k", ctypes.c_int32), ("num_experts", ctypes.c_int32),
         ("ep_size", ctypes.c_int32), ("experts_per_rank", ctypes.c_int32),
-        ("max_tokens_per_rank", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("max_tokens_per_rank", ctypes.c_int32), ("layout", ctypes.c_int32),
         ("counts", ctypes.c_void_p), ("src_index", ctypes.c_void_p),
         ("slot_index", ctypes.c_void_p), ("status", ctypes.c_void_p),
         ("scratch", ctypes.c_void_p), ("scratch_bytes", ctypes.c_size_t),
@@ -82,7 +85,7 @@ def library() -> ctypes.CDLL:
         sig = {
             "moe_workspace_bytes": (SZ, [I32, I32, I32]),
             "moe_scratch_bytes": (SZ, [I32, I32, I32]),
-            "moe_init": (ctypes.c_int, [H, I32, I32, I32, I32, I32, I32, P, P, P, P, P, SZ]),
+            "moe_init": (ctypes.c_int, [H, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, SZ]),
             "moe_dispatch": (ctypes.c_int, [H, P, P, I32, I32, P, P]),
             "moe_combine": (ctypes.c_int, [H, P, P, I32, P, P]),
             "moe_combine_residual_rmsnorm": (ctypes.c_int,
@@ -152,10 +155,11 @@ def moe_strerror(code: int) -> str:
 
 class MoeA2A:
     """One ``moe_handle`` and the device buffers it binds (allocated once at
-    the ladder maximum)."""
+    the ladder maximum).  ``layout`` is "copy" (one workspace row per routed
+    copy) or "region" (one row per token and destination region)."""
 
     def __init__(self, max_tokens: int, hidden: int, top_k: int, num_experts: int,
-                 ep_size: int, max_tokens_per_rank: int, device=None):
+                 ep_size: int, max_tokens_per_rank: int, device=None, layout: str = "copy"):
         dev = torch.device(device if device is not None else "cuda")
         lib = library()
         self.handle = MoeHandle()
@@ -168,8 +172,11 @@ class MoeA2A:
         self.slot_index = torch.full((max_tokens * top_k,), -1, **i32)
         self.status = torch.zeros(1, **i32)
         self.scratch = torch.zeros((nbytes + 3) // 4, **i32)
+        if layout not in LAYOUTS:
+            raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
         _check(lib.moe_init(ctypes.byref(self.handle), max_tokens, hidden, top_k, num_experts,
-                            ep_size, max_tokens_per_rank, _ptr(self.counts), _ptr(self.src_index),
+                            ep_size, max_tokens_per_rank, LAYOUTS[layout],
+                            _ptr(self.counts), _ptr(self.src_index),
                             _ptr(self.slot_index), _ptr(self.status), _ptr(self.scratch),
                             self.scratch.numel() * 4), "moe_init")
         self.device = dev
@@ -185,6 +192,8 @@ class MoeA2A:
     def cap(self) -> int: return self.handle.max_tokens_per_rank
     @property
     def num_tokens(self) -> int: return self.handle.num_tokens
+    @property
+    def layout(self) -> str: return "region" if self.handle.layout == MOE_LAYOUT_PER_REGION else "copy"
 
     def new_workspace(self, fill_bits: Optional[int] = None) -> torch.Tensor:
         """A [ep, cap, H] bf16 workspace; optionally every element set to one

@@ -43,9 +43,10 @@ size_t moe_scratch_bytes(int32_t max_tokens, int32_t top_k, int32_t ep_size) {
 
 int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
              int32_t num_experts, int32_t ep_size, int32_t max_tokens_per_rank,
-             int32_t *counts, int32_t *src_index, int32_t *slot_index,
+             int32_t layout, int32_t *counts, int32_t *src_index, int32_t *slot_index,
              int32_t *status, void *scratch, size_t scratch_bytes) {
     if (h == nullptr) return MOE_ERR_ARG;
+    if (layout != MOE_LAYOUT_PER_COPY && layout != MOE_LAYOUT_PER_REGION) return MOE_ERR_ARG;
     if (max_tokens < 1 || hidden < 8 || hidden % 8 != 0) return MOE_ERR_ARG;
     if (top_k < 1 || top_k > MOE_MAX_TOP_K) return MOE_ERR_ARG;
     if (ep_size < 1 || ep_size > MOE_MAX_EP) return MOE_ERR_ARG;
@@ -67,6 +68,7 @@ int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
     h->ep_size = ep_size;
     h->experts_per_rank = num_experts / ep_size;
     h->max_tokens_per_rank = max_tokens_per_rank;
+    h->layout = layout;
     h->counts = counts;
     h->src_index = src_index;
     h->slot_index = slot_index;
@@ -89,6 +91,8 @@ static int route(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens, hip
     ra.ep = h->ep_size;
     ra.epr = h->experts_per_rank;
     ra.n_experts = h->num_experts;
+    ra.k = h->top_k;
+    ra.per_region = h->layout == MOE_LAYOUT_PER_REGION;
     hipError_t e = moe::launch_route(ra, plan.n_chunks, s);
     if (e != hipSuccess) return hip_fail(h, e);
     *plan_out = plan;
@@ -118,6 +122,7 @@ static moe::DispatchArgs dispatch_args(moe_handle *h, const uint16_t *x, const i
     da.tokens_per_chunk = plan.tokens_per_chunk;
     da.n_chunks = plan.n_chunks;
     da.count_only = count_only;
+    da.per_region = h->layout == MOE_LAYOUT_PER_REGION;
     return da;
 }
 
@@ -166,6 +171,7 @@ static int combine_common(moe_handle *h, const uint16_t *expert_out, const float
                           int32_t weighted) {
     if (h == nullptr || h->max_tokens < 1) return MOE_ERR_ARG;
     if (h->phase != 1) return MOE_ERR_PHASE;
+    if (weighted && h->layout == MOE_LAYOUT_PER_REGION) return MOE_ERR_ARG;
     if (h->num_tokens > 0) {
         if (!dev_ok(expert_out, 16)) return MOE_ERR_ARG;
         if (weighted && !dev_ok(topk_weights, 4)) return MOE_ERR_ARG;
@@ -184,6 +190,7 @@ static moe::CombineArgs combine_args(moe_handle *h, const uint16_t *expert_out,
     ca.H = h->hidden;
     ca.k = h->top_k;
     ca.weighted = weighted ? 1 : 0;
+    ca.per_region = h->layout == MOE_LAYOUT_PER_REGION;
     return ca;
 }
 

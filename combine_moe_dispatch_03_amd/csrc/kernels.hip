@@ -92,9 +92,22 @@ __device__ __forceinline__ void add_region_sums(int32_t *base, const int32_t *hi
     }
 }
 
+// Per-region layout: true if no earlier copy of the same token (flat indices
+// token_base .. i-1) is bound for region d.  Reads the token's ids from L1/L2.
+__device__ __forceinline__ bool first_to_region(const int32_t *ids, int64_t token_base, int64_t i,
+                                                int d, int epr, int n_experts) {
+    for (int64_t q = token_base; q < i; ++q) {
+        const int e = ids[q];
+        if (e >= 0 && e < n_experts && e / epr == d) return false;
+    }
+    return true;
+}
+
 // ---------------------------------------------------------------------------
 // route_rank_kernel: grid = n_chunks, one workgroup per chunk of whole tokens.
 // Items of the chunk are taken 256 at a time (one per thread, flat order).
+// Under the per-region layout only a token's first copy to each region is
+// ranked (later copies share its row).
 // Within a wave, lanes with the same region are found by intersecting one
 // ballot per bit of the region number; a lane's rank is the number of such
 // lanes below it.  Per-wave counts go through LDS to give wave offsets, and a
@@ -129,6 +142,8 @@ __global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
                 d = e / a.epr;
             else if (e != -1)
                 bad = true;
+            if (d >= 0 && a.per_region && !first_to_region(a.ids, i - i % a.k, i, d, a.epr, a.n_experts))
+                d = -1;                          // shares the row of the token's first copy
         }
         uint64_t same = __ballot(d >= 0);
         for (int b = 0; b < region_bits; ++b) {
@@ -168,10 +183,47 @@ __global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
 // unconditionally (lanes past the row end re-read the row's last vector and
 // store nothing), so they are all in flight while the slots are computed.
 // NT marks the workspace stores non-temporal.
+// Rows of token t's copies from the region prefix `base` (copies of earlier
+// tokens) and each copy's rank after them; writes slot_index / src_index
+// (column block 0 only) and, in copy_rows, the rows this block must fill.
+// Under the per-region layout a copy whose region already has a row for this
+// token takes that row and fills nothing.  Ends with a block barrier.
+__device__ __forceinline__ void assign_rows(const DispatchArgs &a, int d, int tid, int cb,
+                                            int64_t f, const int32_t *base, int rank,
+                                            const int32_t *dests, int32_t *rows,
+                                            int32_t *copy_rows) {
+    int first = tid;
+    if (tid < a.k && d >= 0 && a.per_region)
+        for (int j = 0; j < tid; ++j)
+            if (dests[j] == d) { first = j; break; }
+    if (tid < a.k && first == tid) {
+        int row = -1;
+        if (d >= 0) {
+            const int s = base[d] + rank;
+            if (s < a.cap)
+                row = d * a.cap + s;
+            else if (cb == 0)
+                atomicOr(a.status, MOE_STATUS_OVERFLOW);
+        }
+        rows[tid] = row;
+        copy_rows[tid] = row;
+        if (cb == 0 && row >= 0) a.src_index[row] = (int32_t)f;
+    }
+    __syncthreads();
+    if (tid < a.k && first != tid) {
+        rows[tid] = rows[first];
+        copy_rows[tid] = -1;
+    }
+    if (tid < a.k && cb == 0) a.slot_index[f] = rows[tid];
+    __syncthreads();
+}
+
 template <int VPT, bool NT>
 __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a) {
     __shared__ int32_t base[MOE_MAX_EP];
+    __shared__ int32_t dests[MOE_MAX_TOP_K];
     __shared__ int32_t rows[MOE_MAX_TOP_K];
+    __shared__ int32_t copy_rows[MOE_MAX_TOP_K];
 
     const int tid = threadIdx.x;
     const int t = blockIdx.x;
@@ -203,11 +255,13 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
     }
 
     // This token's ids and in-chunk ranks (independent of the prefix too).
-    int e = -1, rank = 0;
+    int d = -1, rank = 0;
     const int64_t f = (int64_t)t * a.k + tid;
     if (tid < a.k) {
-        e = a.ids[f];
-        rank = a.rank[f];                       // meaningful only for a valid id
+        const int e = a.ids[f];
+        rank = a.rank[f];                       // meaningful only for a ranked copy
+        if (e >= 0 && e < a.n_experts) d = e / a.epr;
+        dests[tid] = d;
     }
 
     // Slots of this token's copies: copies of earlier chunks come first.
@@ -216,26 +270,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
     const int chunk = t / a.tokens_per_chunk;
     add_region_sums(base, a.hist, chunk * ep, ep, tid);
     __syncthreads();
-    if (tid < a.k) {
-        int row = -1;
-        if (e >= 0 && e < a.n_experts) {
-            const int d = e / a.epr;
-            const int s = base[d] + rank;
-            if (s < a.cap)
-                row = d * a.cap + s;
-            else if (cb == 0)
-                atomicOr(a.status, MOE_STATUS_OVERFLOW);
-        }
-        rows[tid] = row;
-        if (cb == 0) {
-            a.slot_index[f] = row;
-            if (row >= 0) a.src_index[row] = (int32_t)f;
-        }
-    }
-    __syncthreads();
+    assign_rows(a, d, tid, cb, f, base, rank, dests, rows, copy_rows);
 
     for (int j = 0; j < a.k; ++j) {
-        const int row = uniform(rows[j]);
+        const int row = uniform(copy_rows[j]);
         if (row < 0) continue;
         uint16_t *dst = a.ws + (int64_t)row * a.H;
 #pragma unroll
@@ -280,19 +318,20 @@ __device__ __forceinline__ void accumulate(float (&acc)[VPT][8], const u32x4 (&r
 // Within a wave, lanes bound for the same region are grouped with one ballot
 // per bit of the region number (as in route_rank_kernel) so each group adds
 // its size to the LDS counter with one atomic.
-__device__ __forceinline__ void count_regions(int32_t *cnt, const int32_t *ids, int64_t n, int epr,
-                                              int n_experts, int region_bits, int tid,
-                                              bool *bad) {
+__device__ __forceinline__ void count_regions(int32_t *cnt, const DispatchArgs &a, int64_t n,
+                                              int region_bits, int tid, bool *bad) {
     const int lane = tid & 63;
     for (int64_t base = 0; base < n; base += kThreads) {
         const int64_t i = base + tid;
         int d = -1;
         if (i < n) {
-            const int e = ids[i];
-            if (e >= 0 && e < n_experts)
-                d = e / epr;
+            const int e = a.ids[i];
+            if (e >= 0 && e < a.n_experts)
+                d = e / a.epr;
             else if (e != -1)
                 *bad = true;
+            if (d >= 0 && a.per_region && !first_to_region(a.ids, i - i % a.k, i, d, a.epr, a.n_experts))
+                d = -1;
         }
         uint64_t same = __ballot(d >= 0);
         for (int b = 0; b < region_bits; ++b) {
@@ -309,6 +348,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
     __shared__ int32_t cnt[MOE_MAX_EP];
     __shared__ int32_t dests[MOE_MAX_TOP_K];
     __shared__ int32_t rows[MOE_MAX_TOP_K];
+    __shared__ int32_t copy_rows[MOE_MAX_TOP_K];
 
     const int tid = threadIdx.x;
     const int t = blockIdx.x;
@@ -321,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
         for (int r = tid; r < ep; r += kThreads) cnt[r] = 0;
         __syncthreads();
         bool bad = false;
-        count_regions(cnt, a.ids, (int64_t)a.T * a.k, a.epr, a.n_experts, region_bits, tid, &bad);
+        count_regions(cnt, a, (int64_t)a.T * a.k, region_bits, tid, &bad);
         if (bad) atomicOr(a.status, MOE_STATUS_EXPERT_ID);
         __syncthreads();
         for (int r = tid; r < ep; r += kThreads) a.counts[r] = cnt[r];
@@ -343,35 +383,23 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
 
     const int64_t f = (int64_t)t * a.k + tid;
     for (int r = tid; r < ep; r += kThreads) cnt[r] = 0;
+    int d = -1;
     if (tid < a.k) {
         const int e = a.ids[f];
-        dests[tid] = (e >= 0 && e < a.n_experts) ? e / a.epr : -1;
+        d = (e >= 0 && e < a.n_experts) ? e / a.epr : -1;
+        dests[tid] = d;
     }
     __syncthreads();
     bool unused = false;
-    count_regions(cnt, a.ids, (int64_t)t * a.k, a.epr, a.n_experts, region_bits, tid, &unused);
+    count_regions(cnt, a, (int64_t)t * a.k, region_bits, tid, &unused);
+    int rank = 0;                               // earlier copies of this token to d
+    if (tid < a.k && d >= 0)
+        for (int j = 0; j < tid; ++j) rank += (dests[j] == d);
     __syncthreads();
-    if (tid < a.k) {
-        const int d = dests[tid];
-        int row = -1;
-        if (d >= 0) {
-            int s = cnt[d];
-            for (int j = 0; j < tid; ++j) s += (dests[j] == d);
-            if (s < a.cap)
-                row = d * a.cap + s;
-            else if (cb == 0)
-                atomicOr(a.status, MOE_STATUS_OVERFLOW);
-        }
-        rows[tid] = row;
-        if (cb == 0) {
-            a.slot_index[f] = row;
-            if (row >= 0) a.src_index[row] = (int32_t)f;
-        }
-    }
-    __syncthreads();
+    assign_rows(a, d, tid, cb, f, cnt, rank, dests, rows, copy_rows);
 
     for (int j = 0; j < a.k; ++j) {
-        const int row = uniform(rows[j]);
+        const int row = uniform(copy_rows[j]);
         if (row < 0) continue;
         uint16_t *dst = a.ws + (int64_t)row * a.H;
 #pragma unroll
@@ -386,13 +414,32 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
     }
 }
 
+// G rows starting at compacted copy j0: all G x VPT loads, then the adds in
+// copy order.
+template <int G, int VPT, bool WEIGHTED, bool NT>
+__device__ __forceinline__ void gather_group(float (&acc)[VPT][8], const uint16_t *y, int H,
+                                             const int32_t *rows, const float *gates, int j0,
+                                             const int64_t (&off)[VPT]) {
+    u32x4 raw[G][VPT];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        const uint16_t *src = y + (int64_t)uniform(rows[j0 + u]) * H;
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) raw[u][q] = load_row16<NT>(src + off[q]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < G; ++u) accumulate<VPT, WEIGHTED>(acc, raw[u], gates[j0 + u]);
+}
+
 // ---------------------------------------------------------------------------
 // combine_kernel<VPT, JU, WEIGHTED, FUSED, NT>: grid = (T, column blocks);
 // FUSED runs with one column block so the whole row is in the workgroup.
 //
 // Wave 0 first compacts the token's valid copies (slot_index >= 0) into LDS,
 // keeping j order, so only rows holding valid copies are ever read (padding
-// rows never are).  Rows are then fetched JU at a time with every load of a
+// rows never are).  Under the per-region layout a row named by an earlier
+// copy of the token is dropped: each region's message is added once.  Rows are then fetched JU at a time with every load of a
 // group issued before the first add, and no load under a branch (a branch
 // around a load makes the compiler wait for all outstanding loads).  Lanes
 // past the end of the row load the row's last vector instead and store
@@ -401,6 +448,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
 // is read once).
 template <int VPT, int JU, bool WEIGHTED, bool FUSED, bool NT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+    __shared__ int32_t all_rows[MOE_MAX_TOP_K];
     __shared__ int32_t rows[MOE_MAX_TOP_K];
     __shared__ float gates[MOE_MAX_TOP_K];
     __shared__ int32_t n_valid;
@@ -411,12 +459,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     const int cb = blockIdx.y;
     const int k = a.k;
 
+    if (tid < k) all_rows[tid] = a.slot_index[(int64_t)t * k + tid];
+    __syncthreads();
     if (tid < 64) {                             // wave 0: compact valid copies
         int row = -1;
         float g = 0.0f;
         if (tid < k) {
-            row = a.slot_index[(int64_t)t * k + tid];
+            row = all_rows[tid];
             g = WEIGHTED ? a.w[(int64_t)t * k + tid] : 1.0f;
+            if (row >= 0 && a.per_region)       // a row already added for this token
+                for (int j = 0; j < tid; ++j)
+                    if (all_rows[j] == row) { row = -1; break; }
         }
         const uint64_t valid = __ballot(row >= 0);
         if (row >= 0) {
@@ -441,29 +494,20 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
         for (int e = 0; e < 8; ++e) acc[q][e] = 0.0f;
     }
 
-    // Full groups: JU rows, every load issued before the first add (the
-    // scheduling barrier keeps the compiler from sinking loads to their uses).
+    // Rows in groups of JU, then one group each of 4, 2 and 1 for the rest:
+    // every load of a group is issued before its first add (the scheduling
+    // barrier keeps the compiler from sinking loads to their uses).
     int j0 = 0;
-    for (; j0 + JU <= nv; j0 += JU) {
-        u32x4 raw[JU][VPT];
-#pragma unroll
-        for (int u = 0; u < JU; ++u) {
-            const uint16_t *src = a.y + (int64_t)uniform(rows[j0 + u]) * a.H;
-#pragma unroll
-            for (int q = 0; q < VPT; ++q) raw[u][q] = load_row16<NT>(src + off[q]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < JU; ++u) accumulate<VPT, WEIGHTED>(acc, raw[u], gates[j0 + u]);
+    for (; j0 + JU <= nv; j0 += JU) gather_group<JU, VPT, WEIGHTED, NT>(acc, a.y, a.H, rows, gates, j0, off);
+    if (JU > 4 && j0 + 4 <= nv) {
+        gather_group<4, VPT, WEIGHTED, NT>(acc, a.y, a.H, rows, gates, j0, off);
+        j0 += 4;
     }
-    // Remaining rows one at a time.
-    for (; j0 < nv; ++j0) {
-        u32x4 raw[VPT];
-        const uint16_t *src = a.y + (int64_t)uniform(rows[j0]) * a.H;
-#pragma unroll
-        for (int q = 0; q < VPT; ++q) raw[q] = load_row16<NT>(src + off[q]);
-        accumulate<VPT, WEIGHTED>(acc, raw, gates[j0]);
+    if (JU > 2 && j0 + 2 <= nv) {
+        gather_group<2, VPT, WEIGHTED, NT>(acc, a.y, a.H, rows, gates, j0, off);
+        j0 += 2;
     }
+    if (j0 < nv) gather_group<1, VPT, WEIGHTED, NT>(acc, a.y, a.H, rows, gates, j0, off);
 
     const int64_t row_off = (int64_t)t * a.H;
     if constexpr (!FUSED) {

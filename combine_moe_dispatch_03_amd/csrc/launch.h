@@ -41,6 +41,8 @@ struct RouteArgs {
     int64_t n_items;         // T*k
     int32_t items_per_chunk;
     int32_t ep, epr, n_experts;
+    int32_t k;
+    int32_t per_region;      // 1: only a token's first copy to a region takes a row
 };
 
 struct DispatchArgs {
@@ -56,6 +58,7 @@ struct DispatchArgs {
     int32_t T, H, k, ep, epr, n_experts, cap;
     int32_t tokens_per_chunk, n_chunks;
     int32_t count_only;      // 1: only write counts
+    int32_t per_region;      // 1: one row per (token, region), duplicates share it
 };
 
 struct CombineArgs {
@@ -69,6 +72,7 @@ struct CombineArgs {
     uint16_t *normed;             // [T, H] (fused)
     float eps;
     int32_t T, H, k, weighted;
+    int32_t per_region;      // 1: add each distinct row of a token once
 };
 
 hipError_t launch_route(const RouteArgs &a, int32_t n_chunks, hipStream_t s);

@@ -62,6 +62,10 @@ extern "C" {
 #define MOE_ERR_EXPERT_ID (-4)  /* an expert id outside [-1, E)              */
 #define MOE_ERR_HIP       (-5)  /* a HIP runtime call failed (see hip_error) */
 
+/* workspace layouts (moe_init) */
+#define MOE_LAYOUT_PER_COPY   0     /* one row per routed copy (t, j)          */
+#define MOE_LAYOUT_PER_REGION 1     /* one row per (token, destination region) */
+
 /* bits of the device status word (moe_sync_status) */
 #define MOE_STATUS_OVERFLOW  1
 #define MOE_STATUS_EXPERT_ID 2
@@ -85,7 +89,7 @@ typedef struct moe_handle {
     int32_t ep_size;             /* ep                                         */
     int32_t experts_per_rank;    /* epr = E / ep                               */
     int32_t max_tokens_per_rank; /* cap: allocated rows per region             */
-    int32_t reserved0;
+    int32_t layout;              /* MOE_LAYOUT_PER_COPY or MOE_LAYOUT_PER_REGION */
     /* device buffers owned by the caller (moe_init) */
     int32_t *counts;             /* [ep]          copies sent to each region   */
     int32_t *src_index;          /* [ep * cap]    f held by row (r, s)         */
@@ -119,6 +123,15 @@ size_t moe_scratch_bytes(int32_t max_tokens, int32_t top_k, int32_t ep_size);
  *   num_experts          multiple of ep_size
  *   ep_size              1 .. MOE_MAX_EP
  *   max_tokens_per_rank  >= 1; ep * cap and max_tokens * k must fit int32
+ *   layout               MOE_LAYOUT_PER_COPY: one workspace row per routed
+ *                        copy; MOE_LAYOUT_PER_REGION: one row per (token,
+ *                        destination region), the form [A2A] measures ("Update
+ *                        -- the correctness failures are resolved": a token is
+ *                        sent once per destination rank and its duplicate-rank
+ *                        top-k slots are blanked; "Bring-up progress": about
+ *                        5.3 distinct ranks per token at top-8 over 8 ranks).
+ *                        A token then contributes at most one row per region,
+ *                        so cap = max_tokens always suffices.
  *   counts, src_index, slot_index, status, scratch: device, 4-byte aligned,
  *                        sized as in moe_handle; *status must be 0 before
  *                        the first dispatch (zero-filled memory)
@@ -127,7 +140,7 @@ size_t moe_scratch_bytes(int32_t max_tokens, int32_t top_k, int32_t ep_size);
  */
 int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
              int32_t num_experts, int32_t ep_size, int32_t max_tokens_per_rank,
-             int32_t *counts, int32_t *src_index, int32_t *slot_index,
+             int32_t layout, int32_t *counts, int32_t *src_index, int32_t *slot_index,
              int32_t *status, void *scratch, size_t scratch_bytes);
 
 /*
@@ -141,8 +154,11 @@ int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
  *   runtime_max_tokens_per_rank  R, the rung of this call, R <= max_tokens
  *   workspace  device [ep, cap, H] bf16, 16-byte aligned
  * Writes: workspace rows (r, s) for s < min(counts[r], cap) with the source
- * token's row (bit copies); counts[r] = copies routed to region r (not
- * clamped to cap); slot_index[f]; src_index[r*cap + s] for valid rows.
+ * token's row (bit copies); counts[r] = rows region r was sent (not clamped
+ * to cap); slot_index[f]; src_index[r*cap + s] for valid rows.
+ * Per-region layout: the token's first copy to region r takes the row
+ * (src_index holds that copy's f); its later copies to r get the same
+ * slot_index and write nothing.
  * Padding rows and src_index entries past the valid prefix are not touched.
  * Copies past cap are dropped (slot_index -1) and set MOE_STATUS_OVERFLOW;
  * ids outside [-1, E) are dropped and set MOE_STATUS_EXPERT_ID; both are
@@ -166,6 +182,10 @@ int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
  * Sum over j = 0..k-1 in order in fp32 (weighted terms as fused
  * multiply-adds), skipping copies with slot_index -1; padding rows are never
  * read.  A token with no valid copy gets +0.
+ * Per-region layout: each row holds its region's message for the token (the
+ * gated sum of the token's experts there, [A2A] "Bring-up progress": the
+ * combine is an unweighted rank-sum), and each distinct row is added once,
+ * in the order of its first copy; weighted must be 0 (else MOE_ERR_ARG).
  * Returns MOE_OK, MOE_ERR_ARG, MOE_ERR_PHASE (not dispatched) or MOE_ERR_HIP.
  * On success the handle returns to idle.
  */

@@ -50,11 +50,12 @@ class GpuRun:
 
 
 def gpu_dispatch(x: np.ndarray, ids: np.ndarray, E: int, ep: int, cap: int, R: Optional[int] = None,
-                 max_tokens: Optional[int] = None, fill: Optional[int] = CANARY) -> GpuRun:
+                 max_tokens: Optional[int] = None, fill: Optional[int] = CANARY,
+                 layout: str = "copy") -> GpuRun:
     T, H = x.shape
     k = ids.shape[1]
     R = R if R is not None else max(T, 1)
-    h = moe.MoeA2A(max_tokens or R, H, k, E, ep, cap)
+    h = moe.MoeA2A(max_tokens or R, H, k, E, ep, cap, layout=layout)
     ws = h.new_workspace(fill)
     xd, idd = to_dev_bf16(x), to_dev(ids.astype(np.int32))
     moe.moe_dispatch(h, xd, idd, R, ws)
@@ -107,3 +108,18 @@ def assert_bf16_close(got: np.ndarray, want: np.ndarray, what: str, max_ulp: int
     worst = int(d.max())
     assert worst <= max_ulp, f"{what}: max {worst} ulp at {np.unravel_index(int(d.argmax()), d.shape)}"
     return int((d != 0).sum())
+
+
+def expert_stage_gpu_by_row(run: GpuRun, rows_by_copy: np.ndarray) -> None:
+    """Write into every valid row the row of the copy that holds it
+    (src_index): the per-copy output, or under the per-region layout the
+    region's message stored at the token's first copy."""
+    h = run.h
+    counts = h.counts.cpu().numpy()
+    src = h.src_index_view()
+    flat = run.ws.view(-1, h.hidden)
+    yd = to_dev_bf16(rows_by_copy)
+    for r in range(h.ep_size):
+        n = min(int(counts[r]), h.cap)
+        if n:
+            flat[r * h.cap: r * h.cap + n] = yd[src[r, :n].long()]

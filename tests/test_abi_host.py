@@ -53,7 +53,8 @@ def test_handle_layout_and_constants_match_header(tmp_path):
     prog += [f'printf("%zu\\n", offsetof(moe_handle, {f}));' for f in fields]
     consts = ["MOE_OK", "MOE_ERR_ARG", "MOE_ERR_PHASE", "MOE_ERR_OVERFLOW", "MOE_ERR_EXPERT_ID",
               "MOE_ERR_HIP", "MOE_STATUS_OVERFLOW", "MOE_STATUS_EXPERT_ID", "MOE_MAX_EP",
-              "MOE_MAX_TOP_K", "MOE_MAX_FUSED_HIDDEN"]
+              "MOE_MAX_TOP_K", "MOE_MAX_FUSED_HIDDEN", "MOE_LAYOUT_PER_COPY",
+              "MOE_LAYOUT_PER_REGION"]
     prog += [f'printf("%d\\n", (int){c});' for c in consts]
     prog += ["return 0;}"]
     src = tmp_path / "layout.c"
@@ -72,10 +73,10 @@ def test_handle_layout_and_constants_match_header(tmp_path):
 FAKE = 0x100000   # aligned, never dereferenced by the validation paths
 
 
-def make_handle(lib, max_tokens=64, H=128, k=2, E=8, ep=4, cap=128):
+def make_handle(lib, max_tokens=64, H=128, k=2, E=8, ep=4, cap=128, layout=0):
     h = moe.MoeHandle()
-    rc = lib.moe_init(ctypes.byref(h), max_tokens, H, k, E, ep, cap, FAKE, FAKE, FAKE, FAKE,
-                      FAKE, lib.moe_scratch_bytes(max_tokens, k, ep))
+    rc = lib.moe_init(ctypes.byref(h), max_tokens, H, k, E, ep, cap, layout, FAKE, FAKE, FAKE,
+                      FAKE, FAKE, lib.moe_scratch_bytes(max_tokens, k, ep))
     assert rc == moe.MOE_OK
     return h
 
@@ -94,23 +95,23 @@ def test_sizes(lib):
 @pytest.mark.parametrize("args", [
     dict(max_tokens=0), dict(H=0), dict(H=12), dict(H=4), dict(k=0), dict(k=65),
     dict(ep=0), dict(ep=257), dict(E=7), dict(E=2), dict(cap=0),
-    dict(ep=8, E=8, cap=1 << 29),
+    dict(ep=8, E=8, cap=1 << 29), dict(layout=2), dict(layout=-1),
 ])
 def test_init_rejects(lib, args):
-    p = dict(max_tokens=64, H=128, k=2, E=8, ep=4, cap=128)
+    p = dict(max_tokens=64, H=128, k=2, E=8, ep=4, cap=128, layout=0)
     p.update(args)
     h = moe.MoeHandle()
     sb = lib.moe_scratch_bytes(max(p["max_tokens"], 1), max(min(p["k"], 64), 1),
                                max(min(p["ep"], 256), 1))
     rc = lib.moe_init(ctypes.byref(h), p["max_tokens"], p["H"], p["k"], p["E"], p["ep"],
-                      p["cap"], FAKE, FAKE, FAKE, FAKE, FAKE, sb)
+                      p["cap"], p["layout"], FAKE, FAKE, FAKE, FAKE, FAKE, sb)
     assert rc == moe.MOE_ERR_ARG
 
 
 def test_init_rejects_pointers_and_scratch(lib):
     h = moe.MoeHandle()
     sb = lib.moe_scratch_bytes(64, 2, 4)
-    args = [64, 128, 2, 8, 4, 128]
+    args = [64, 128, 2, 8, 4, 128, 0]
     assert lib.moe_init(ctypes.byref(h), *args, None, FAKE, FAKE, FAKE, FAKE, sb) == moe.MOE_ERR_ARG
     assert lib.moe_init(ctypes.byref(h), *args, FAKE, FAKE, FAKE, FAKE + 2, FAKE, sb) == moe.MOE_ERR_ARG
     assert lib.moe_init(ctypes.byref(h), *args, FAKE, FAKE, FAKE, FAKE, FAKE, sb - 4) == moe.MOE_ERR_ARG
@@ -165,6 +166,16 @@ def test_combine_argument_and_phase_checks(lib):
     big.phase, big.num_tokens = 1, 8
     assert lib.moe_combine_residual_rmsnorm(ctypes.byref(big), FAKE, None, 0, FAKE, FAKE, FAKE,
                                             1e-6, FAKE, None) == moe.MOE_ERR_ARG
+
+
+def test_per_region_layout_rejects_a_weighted_combine(lib):
+    h = make_handle(lib, layout=moe.MOE_LAYOUT_PER_REGION)
+    assert h.layout == moe.MOE_LAYOUT_PER_REGION
+    h.phase, h.num_tokens = 1, 8
+    assert lib.moe_combine(ctypes.byref(h), FAKE, FAKE, 1, FAKE, None) == moe.MOE_ERR_ARG
+    assert lib.moe_combine_residual_rmsnorm(ctypes.byref(h), FAKE, FAKE, 1, FAKE, FAKE, FAKE,
+                                            1e-6, FAKE, None) == moe.MOE_ERR_ARG
+    assert h.phase == 1
 
 
 def test_strerror_and_reduced_flag(lib):
