@@ -54,8 +54,11 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_combine_residual_rmsnorm_region.argtypes = [
         _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_float, _P, _P, _P, _P]
     lib.oracle_combine_residual_rmsnorm_region.restype = ctypes.c_int
+    lib.oracle_quantize_e4m3_rows.argtypes = [_P, _I64, _I64, _P, _P]
+    lib.oracle_quantize_e4m3_rows.restype = None
     for name in ("oracle_bf16_to_f32_array", "oracle_f32_to_bf16_array",
-                 "oracle_f64_to_bf16_array"):
+                 "oracle_f64_to_bf16_array", "oracle_e4m3_to_f32_array",
+                 "oracle_f32_to_e4m3_array"):
         getattr(lib, name).argtypes = [_P, _P, _I64]
         getattr(lib, name).restype = None
     return lib
@@ -86,6 +89,43 @@ class Oracle:
         out = np.empty(a.shape, dtype=np.uint16)
         self.lib.oracle_f64_to_bf16_array(a.ctypes.data, out.ctypes.data, a.size)
         return out
+
+    def e4m3_to_f32(self, c: np.ndarray) -> np.ndarray:
+        c = np.ascontiguousarray(c, dtype=np.uint8)
+        out = np.empty(c.shape, dtype=np.float32)
+        self.lib.oracle_e4m3_to_f32_array(c.ctypes.data, out.ctypes.data, c.size)
+        return out
+
+    def f32_to_e4m3(self, a: np.ndarray) -> np.ndarray:
+        a = np.ascontiguousarray(a, dtype=np.float32)
+        out = np.empty(a.shape, dtype=np.uint8)
+        self.lib.oracle_f32_to_e4m3_array(a.ctypes.data, out.ctypes.data, a.size)
+        return out
+
+    def quantize_e4m3_rows(self, x: np.ndarray):
+        """(q uint8 [T, H], scale fp32 [T]) of the FP8 payload."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        T, H = x.shape
+        q = np.empty((T, H), dtype=np.uint8)
+        scale = np.empty(T, dtype=np.float32)
+        self.lib.oracle_quantize_e4m3_rows(x.ctypes.data, T, H, q.ctypes.data, scale.ctypes.data)
+        return q, scale
+
+    def dispatch_fp8(self, x: np.ndarray, ids: np.ndarray, ep: int, epr: int, cap: int,
+                     layout: str = "copy"):
+        """FP8 dispatch: quantised rows placed exactly as the bf16 rows are
+        (a byte copy of each quantised row), plus each row's scale.
+        Returns (DispatchResult with ws uint8 [ep, cap, H], scales fp32 [ep, cap])."""
+        q, scale = self.quantize_e4m3_rows(x)
+        T, H = q.shape
+        k = ids.shape[1]
+        d = self.dispatch(q.view(np.uint16), ids, ep, epr, cap, layout=layout)
+        d.ws = d.ws.view(np.uint8).reshape(ep, cap, H)
+        scales = np.full((ep, cap), np.nan, dtype=np.float32)
+        for r in range(ep):
+            n = min(int(d.counts[r]), cap)
+            scales[r, :n] = scale[d.src_index[r, :n] // k]
+        return d, scales
 
     # -- the method --------------------------------------------------------
     def dispatch(self, x: np.ndarray, ids: np.ndarray, ep: int, epr: int, cap: int,

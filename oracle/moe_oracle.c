@@ -323,7 +323,93 @@ int oracle_combine_residual_rmsnorm_region(const uint16_t *y, const int32_t *slo
     return 0;
 }
 
+/* ---- FP8 payload (InferenceX PR #2450, "The adapter" notes: an FP8 dispatch
+ * carries its scale as a second payload, checked against the oracle's cast
+ * round-trip) -------------------------------------------------------------------
+ * OCP FP8 E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits (bias 7), 3 stored
+ * fraction bits; normal numbers in [2^(e-1), 2^e) are spaced 2^(e-4), the
+ * smallest normal is 2^-6 and subnormals are spaced 2^-9; the largest finite
+ * value is 448 (exponent field 15, fraction 110); exponent 15 with fraction
+ * 111 is NaN and there is no infinity, so a magnitude that rounds past 448
+ * (at or beyond the tie point 464) becomes NaN.  Encoding rounds to nearest,
+ * ties to the even significand. */
+
+float oracle_e4m3_to_f32(uint8_t c)
+{
+    int sign = c >> 7, exp = (c >> 3) & 15, frac = c & 7;
+    double v;
+    if (exp == 15 && frac == 7)
+        v = NAN;
+    else if (exp == 0)
+        v = ldexp((double)frac, -9);
+    else
+        v = ldexp(1.0 + frac / 8.0, exp - 7);
+    return (float)(sign ? -v : v);
+}
+
+uint8_t oracle_f32_to_e4m3(float f)
+{
+    double v = (double)f;
+    uint8_t sign = signbit(v) ? 0x80u : 0u;
+    if (isnan(v))
+        return (uint8_t)(sign | 0x7Fu);
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    int e = 0;
+    if (!isinf(a))
+        frexp(a, &e);                  /* a in [2^(e-1), 2^e) */
+    int qexp = e - 4;                  /* spacing of 4-significant-bit values */
+    if (qexp < -9)
+        qexp = -9;                     /* subnormal spacing */
+    double r = isinf(a) ? INFINITY : ldexp(nearbyint(ldexp(a, -qexp)), qexp);
+    if (r > 448.0)
+        return (uint8_t)(sign | 0x7Fu);          /* no infinity: NaN */
+    if (r < ldexp(1.0, -6))                       /* subnormal: fraction = r / 2^-9 */
+        return (uint8_t)(sign | (uint8_t)ldexp(r, 9));
+    int re;
+    double m = frexp(r, &re);                     /* r = m * 2^re, m in [0.5, 1) */
+    int frac = (int)ldexp(m * 2.0 - 1.0, 3);      /* 1.fff */
+    return (uint8_t)(sign | ((re - 1 + 7) << 3) | frac);
+}
+
+/* Row quantisation for the FP8 payload: one fp32 scale per token row,
+ *   amax     = max_h |x[t, h]|
+ *   scale[t] = amax / 448          (fp32 division; 0 for an all-zero row)
+ *   inv      = 448 / amax          (fp32 division; 0 for an all-zero row)
+ *   q[t, h]  = e4m3( fp32(x[t, h]) * inv )   (fp32 product, then nearest-even)
+ * so the row's largest magnitude maps to 448 and x ~ e4m3_value(q) * scale.
+ * Inputs are finite. */
+void oracle_quantize_e4m3_rows(const uint16_t *x, int64_t T, int64_t H, uint8_t *q,
+                               float *scale)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        float amax = 0.0f;
+        for (int64_t h = 0; h < H; ++h) {
+            float a = fabsf(oracle_bf16_to_f32(x[t * H + h]));
+            if (a > amax)
+                amax = a;
+        }
+        float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+        scale[t] = amax / 448.0f;
+        for (int64_t h = 0; h < H; ++h)
+            q[t * H + h] = oracle_f32_to_e4m3(oracle_bf16_to_f32(x[t * H + h]) * inv);
+    }
+}
+
 /* ---- array forms of the codec, for the test suite ---------------------------- */
+void oracle_e4m3_to_f32_array(const uint8_t *in, float *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e4m3_to_f32(in[i]);
+}
+
+void oracle_f32_to_e4m3_array(const float *in, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f32_to_e4m3(in[i]);
+}
+
 void oracle_bf16_to_f32_array(const uint16_t *in, float *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i)

@@ -664,4 +664,80 @@ def pin_region_distinct_closed_form(o):
     assert abs(per_token - float(g["distinct_regions_closed_form"][0][0])) < 0.03, per_token
 
 
+# ---------------------------------------------------------------- FP8 pins
+# The FP8 payload: OCP E4M3 codes (torch.float8_e4m3fn is an independent
+# implementation of the same format) and one fp32 scale per row.
+
+def torch_e4m3_bits(a) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_decode_vs_torch(o):
+    codes = np.arange(256, dtype=np.uint8)
+    got = o.e4m3_to_f32(codes)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    assert ((got == want) | (np.isnan(got) & np.isnan(want))).all()
+    assert (np.signbit(got) == np.signbit(want)).all()
+
+
+def pin_e4m3_encode_vs_torch(o):
+    rng = np.random.default_rng(41)
+    v = np.concatenate([rng.standard_normal(1 << 16) * 100, rng.standard_normal(1 << 16) * 0.02,
+                        rng.uniform(-463.9, 463.9, 1 << 14)]).astype(np.float32)
+    assert np.array_equal(o.f32_to_e4m3(v), torch_e4m3_bits(v))
+
+
+def pin_e4m3_special(o):
+    cases = [(448.0, 0x7E), (464.0, 0x7E), (465.0, 0x7F), (1e6, 0x7F), (-448.0, 0xFE),
+             (2.0 ** -9, 0x01), (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (2.0 ** -6, 0x08),
+             (7 * 2.0 ** -9, 0x07), (15 * 2.0 ** -10, 0x08), (1.0, 0x38), (1.0625, 0x38),
+             (1.1875, 0x3A), (-0.0, 0x80), (0.0, 0x00), (2.0 ** -11, 0x00)]
+    for v, want in cases:
+        got = int(o.f32_to_e4m3(np.array([v], np.float32))[0])
+        assert got == want, (v, hex(got), hex(want))
+    assert int(o.f32_to_e4m3(np.array([np.nan], np.float32))[0]) & 0x7F == 0x7F
+
+
+def pin_fp8_row_quantisation(o):
+    rng = np.random.default_rng(43)
+    T, H = 24, 200
+    xf = (rng.standard_normal((T, H)) * np.exp(rng.uniform(-8, 8, (T, 1)))).astype(np.float32)
+    xf[5] = 0.0                                           # an all-zero row
+    xf[6, :] = 0.0
+    xf[6, 17] = -3.0                                      # one non-zero element
+    x = torch_bf16_bits(xf)
+    q, scale = o.quantize_e4m3_rows(x)
+    xv = torch_bf16_value(x)
+    amax = np.abs(xv).max(axis=1)
+    assert np.array_equal(scale, (amax / np.float32(448)).astype(np.float32))
+    inv = np.where(amax > 0, np.float32(448) / np.where(amax > 0, amax, 1), 0).astype(np.float32)
+    assert np.array_equal(q, torch_e4m3_bits((xv * inv[:, None]).astype(np.float32)))
+    assert (q[5] == 0).all() and scale[5] == 0
+    assert q[6, 17] == 0xFE and (np.delete(q[6], 17) == 0).all()
+    for t in range(T):                                    # the row maximum maps to +-448
+        if amax[t] > 0:
+            assert (np.abs(o.e4m3_to_f32(q[t])) == 448).any()
+    # round trip: within half a step of the 3-bit significand, or half the
+    # subnormal step (2^-10 in scaled units) near zero
+    back = o.e4m3_to_f32(q).astype(np.float64) * scale[:, None]
+    bound = np.maximum(np.abs(xv) * 2.0 ** -4, scale[:, None] * 2.0 ** -10) * (1 + 1e-6)
+    assert (np.abs(back - xv) <= bound).all()
+
+
+def pin_fp8_dispatch_places_rows_and_scales(o):
+    rng = np.random.default_rng(47)
+    T, H, k, E, ep = 60, 32, 4, 16, 4
+    ids = _random_routing(rng, T, k, E, p_missing=0.1)
+    x = random_bf16(rng, (T, H))
+    q, scale = o.quantize_e4m3_rows(x)
+    for layout in ("copy", "region"):
+        d, scales = o.dispatch_fp8(x, ids, ep, E // ep, T * k, layout=layout)
+        for r in range(ep):
+            n = int(d.counts[r])
+            toks = d.src_index[r, :n] // k
+            assert np.array_equal(d.ws[r, :n], q[toks])
+            assert np.array_equal(scales[r, :n], scale[toks])
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

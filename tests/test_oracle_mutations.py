@@ -103,6 +103,18 @@ MUTATIONS = [
      "slot_index[f] = slot_index[f];"),
     ("region_copies_wrong_token", "memcpy(ws + row * H, x + t * H,",
      "memcpy(ws + row * H, x + (t + 1 == T ? 0 : t + 1) * H,"),
+    # FP8 payload
+    ("e4m3_truncates", "double r = isinf(a) ? INFINITY : ldexp(nearbyint(ldexp(a, -qexp)), qexp);",
+     "double r = isinf(a) ? INFINITY : ldexp(floor(ldexp(a, -qexp)), qexp);"),
+    ("e4m3_subnormal_step", "if (qexp < -9)\n        qexp = -9;", "if (qexp < -10)\n        qexp = -10;"),
+    ("e4m3_bias", "return (uint8_t)(sign | ((re - 1 + 7) << 3) | frac);",
+     "return (uint8_t)(sign | ((re - 1 + 8) << 3) | frac);"),
+    ("e4m3_decode_bias", "v = ldexp(1.0 + frac / 8.0, exp - 7);", "v = ldexp(1.0 + frac / 8.0, exp - 8);"),
+    ("fp8_scale_to_480", "float inv = amax > 0.0f ? 448.0f / amax : 0.0f;",
+     "float inv = amax > 0.0f ? 480.0f / amax : 0.0f;"),
+    ("fp8_scale_inverted", "scale[t] = amax / 448.0f;", "scale[t] = 448.0f / amax;"),
+    ("fp8_amax_signed", "float a = fabsf(oracle_bf16_to_f32(x[t * H + h]));",
+     "float a = oracle_bf16_to_f32(x[t * H + h]);"),
     ("region_first_copy_scan_skips_copy_0", "for (int64_t i = 0; i < j; ++i) {\n        int32_t e = ids[t * k + i];",
      "for (int64_t i = 1; i < j; ++i) {\n        int32_t e = ids[t * k + i];"),
 ]
