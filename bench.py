@@ -29,7 +29,9 @@ line also carries:
   workloads     the same step on the skewed, decode and fused workloads, and
                 on prefill and skewed under the per-region layout (one row per
                 token and destination region, the form the FlashInfer pages
-                measure; unweighted combine of per-region messages)
+                measure; unweighted combine of per-region messages), and with
+                the fp8 dispatch payload (e4m3 codes + one scale per row; the
+                combine reads the experts' bf16 outputs)
 """
 from __future__ import annotations
 
@@ -123,7 +125,7 @@ def describe(wl, cap) -> str:
 
 
 def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0,
-            layout: str = "copy") -> dict:
+            layout: str = "copy", payload: str = "bf16") -> dict:
     import numpy as np
     import torch
 
@@ -144,6 +146,14 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0,
         del probe
     h = moe.MoeA2A(wl.R, wl.H, wl.k, wl.E, wl.ep, cap, device=dev, layout=layout)
     ws = h.new_workspace()
+    fp8 = payload == "fp8"
+    if fp8:
+        # the experts' bf16 outputs (here the dispatched rows themselves) sit in
+        # ws; each step dispatches the fp8 payload into ws8 / scales
+        moe.moe_dispatch(h, x, ids, wl.R, ws)
+        moe.moe_reset(h)
+        ws8 = h.new_workspace_fp8()
+        scales = h.new_scales()
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
     fused = wl.combine == "fused"
     if fused:
@@ -154,10 +164,16 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0,
     sh = stream.cuda_stream
     hev = HipEvents()
 
+    def dispatch():
+        if fp8:
+            moe.moe_dispatch_fp8(h, x, ids, wl.R, ws8, scales, stream=stream)
+        else:
+            moe.moe_dispatch(h, x, ids, wl.R, ws, stream=stream)
+
     def step(ev=None):
         if ev is not None:
             hev.record(ev[0], sh)
-        moe.moe_dispatch(h, x, ids, wl.R, ws, stream=stream)
+        dispatch()
         if ev is not None:
             hev.record(ev[1], sh)
         if fused:
@@ -208,7 +224,7 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0,
     for ev in cold:
         flush.max()
         hev.record(ev[0], sh)
-        moe.moe_dispatch(h, x, ids, wl.R, ws, stream=stream)
+        dispatch()
         hev.record(ev[1], sh)
         flush.max()
         hev.record(ev[2], sh)
@@ -230,11 +246,15 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0,
         b = wl.algorithmic_bytes()
     else:
         b = region_bytes(wl, int(h.counts.sum().item()))
+    if fp8:   # the dispatch writes H code bytes and a 4-byte scale per row instead of 2H
+        rows = int(h.counts.sum().item())
+        b["dispatch"] -= rows * (wl.H - 4)
     comb_bytes = b["fused"] if fused else b["combine"]
     ms = elapsed * 1e3 / steps
     res_d = {
         "workload": describe(wl, cap) + ("" if layout == "copy" else
-                                         ", per-region layout (one row per token and region)"),
+                                         ", per-region layout (one row per token and region)")
+                    + (", fp8 e4m3 dispatch payload with a per-row scale" if fp8 else ""),
         "ms_per_step": ms,
         "ms_per_step_instrumented": elapsed_ev * 1e3 / steps,
         "tokens_per_s": wl.T / (ms / 1e3),
@@ -327,9 +347,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill")
-    ap.add_argument("--extras", default="skewed,decode,fused,prefill_region,skewed_region",
+    ap.add_argument("--extras",
+                    default="skewed,decode,fused,prefill_region,skewed_region,prefill_fp8,"
+                            "prefill_region_fp8",
                     help="comma-separated workloads also measured (empty for none); a "
-                         "_region suffix runs the per-region layout")
+                         "_region suffix runs the per-region layout, _fp8 the fp8 payload")
     ap.add_argument("--cold-iters", type=int, default=100,
                     help="launches timed after an untimed 1 GiB cache-evicting read, per kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -352,10 +374,11 @@ def main() -> int:
     main_res = measure(wl, args.steps, args.warmup, args.cold_iters)
     extras = {}
     for name in [n for n in args.extras.split(",") if n and n != wl.name]:
-        base, _, layout = name.partition("_")
+        base, *mods = name.split("_")
         extras[name] = measure(synth.BY_NAME[base], max(args.steps // 2, 5),
                                max(args.warmup // 2, 2), args.cold_iters,
-                               layout=layout or "copy")
+                               layout="region" if "region" in mods else "copy",
+                               payload="fp8" if "fp8" in mods else "bf16")
 
     comb_ms = main_res["combine_ms_mean"]
     achieved = main_res["combine_bytes"] / (comb_ms / 1e3) / 1e9

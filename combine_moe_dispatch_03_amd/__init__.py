@@ -9,7 +9,7 @@ library is missing the import of the functions fails loudly.
 
 Functions carry the C names:
 
-  moe_dispatch, moe_combine, moe_combine_residual_rmsnorm, moe_route_counts,
+  moe_dispatch, moe_dispatch_fp8, moe_combine, moe_combine_residual_rmsnorm, moe_route_counts,
   moe_sync_status, moe_reset, moe_output_is_reduced, moe_strerror,
   moe_workspace_bytes, moe_scratch_bytes
 
@@ -42,7 +42,8 @@ MOE_MAX_TOP_K = 64
 MOE_MAX_FUSED_HIDDEN = 16384
 
 EXPORTED = (
-    "moe_workspace_bytes", "moe_scratch_bytes", "moe_init", "moe_dispatch", "moe_combine",
+    "moe_workspace_bytes", "moe_scratch_bytes", "moe_init", "moe_dispatch", "moe_dispatch_fp8",
+    "moe_combine",
     "moe_combine_residual_rmsnorm", "moe_route_counts", "moe_sync_status", "moe_reset",
     "moe_output_is_reduced", "moe_strerror",
 )
@@ -87,6 +88,7 @@ def library() -> ctypes.CDLL:
             "moe_scratch_bytes": (SZ, [I32, I32, I32]),
             "moe_init": (ctypes.c_int, [H, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, SZ]),
             "moe_dispatch": (ctypes.c_int, [H, P, P, I32, I32, P, P]),
+            "moe_dispatch_fp8": (ctypes.c_int, [H, P, P, I32, I32, P, P, P]),
             "moe_combine": (ctypes.c_int, [H, P, P, I32, P, P]),
             "moe_combine_residual_rmsnorm": (ctypes.c_int,
                                              [H, P, P, I32, P, P, P, ctypes.c_float, P, P]),
@@ -205,6 +207,18 @@ class MoeA2A:
         w.fill_(fill_bits - 65536 if fill_bits >= 32768 else fill_bits)
         return w.view(torch.bfloat16)
 
+    def new_workspace_fp8(self, fill_byte: Optional[int] = None) -> torch.Tensor:
+        """A [ep, cap, H] uint8 workspace for e4m3 codes (optionally filled)."""
+        w = torch.empty((self.ep_size, self.cap, self.hidden), dtype=torch.uint8, device=self.device)
+        if fill_byte is not None:
+            w.fill_(fill_byte)
+        return w
+
+    def new_scales(self) -> torch.Tensor:
+        """A [ep, cap] fp32 buffer for the fp8 row scales (filled with NaN)."""
+        return torch.full((self.ep_size, self.cap), float("nan"), dtype=torch.float32,
+                          device=self.device)
+
     def slot_index_view(self) -> torch.Tensor:
         T, k = self.handle.num_tokens, self.top_k
         return self.slot_index[: T * k].view(T, k)
@@ -224,6 +238,21 @@ def moe_dispatch(h: MoeA2A, x: torch.Tensor, topk_ids: torch.Tensor,
     _check(library().moe_dispatch(ctypes.byref(h.handle), _ptr(x), _ptr(topk_ids), T,
                                   runtime_max_tokens_per_rank, _ptr(workspace), _stream(stream)),
            "moe_dispatch")
+
+
+def moe_dispatch_fp8(h: MoeA2A, x: torch.Tensor, topk_ids: torch.Tensor,
+                     runtime_max_tokens_per_rank: int, workspace: torch.Tensor,
+                     scales: torch.Tensor, stream=None) -> None:
+    """Route every copy with an FP8 (e4m3) payload: codes into ``workspace``
+    ([ep, cap, H] uint8), one fp32 scale per row into ``scales`` ([ep, cap])."""
+    T = x.shape[0] if x.dim() == 2 else 0
+    _need(x, "x", torch.bfloat16, shape=(T, h.hidden))
+    _need(topk_ids, "topk_ids", torch.int32, shape=(T, h.top_k))
+    _need(workspace, "workspace", torch.uint8, numel=h.ep_size * h.cap * h.hidden)
+    _need(scales, "scales", torch.float32, numel=h.ep_size * h.cap)
+    _check(library().moe_dispatch_fp8(ctypes.byref(h.handle), _ptr(x), _ptr(topk_ids), T,
+                                      runtime_max_tokens_per_rank, _ptr(workspace), _ptr(scales),
+                                      _stream(stream)), "moe_dispatch_fp8")
 
 
 def moe_combine(h: MoeA2A, expert_out: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
@@ -295,7 +324,7 @@ def moe_reset(h: MoeA2A) -> None:
 
 
 __all__ = [
-    "MoeA2A", "MoeError", "MoeHandle", "library", "moe_dispatch", "moe_combine",
+    "MoeA2A", "MoeError", "MoeHandle", "library", "moe_dispatch", "moe_dispatch_fp8", "moe_combine",
     "moe_combine_residual_rmsnorm", "moe_route_counts", "moe_sync_status", "moe_reset",
     "moe_output_is_reduced", "moe_strerror", "moe_workspace_bytes", "moe_scratch_bytes",
 ]

@@ -123,33 +123,63 @@ static moe::DispatchArgs dispatch_args(moe_handle *h, const uint16_t *x, const i
     da.n_chunks = plan.n_chunks;
     da.count_only = count_only;
     da.per_region = h->layout == MOE_LAYOUT_PER_REGION;
+    da.fp8 = 0;
+    da.ws8 = nullptr;
+    da.scales = nullptr;
     return da;
 }
 
-int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
-                 int32_t num_tokens, int32_t runtime_max_tokens_per_rank,
-                 uint16_t *workspace, void *stream) {
+static int dispatch_checks(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
+                           int32_t num_tokens, int32_t R, const void *workspace) {
     if (h == nullptr || h->max_tokens < 1) return MOE_ERR_ARG;
     if (h->phase != 0) return MOE_ERR_PHASE;
-    const int32_t R = runtime_max_tokens_per_rank;
     if (R < 1 || R > h->max_tokens || num_tokens < 0 || num_tokens > R) return MOE_ERR_ARG;
     if (!dev_ok(workspace, 16)) return MOE_ERR_ARG;
     if (num_tokens > 0 && (!dev_ok(x, 16) || !dev_ok(topk_ids, 4))) return MOE_ERR_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    return MOE_OK;
+}
 
+static int dispatch_launch(moe_handle *h, moe::DispatchArgs da, const int32_t *topk_ids,
+                           int32_t num_tokens, int32_t R, hipStream_t s) {
     moe::RoutePlan plan = moe::plan_route(num_tokens);
     if (!moe::dispatch_is_small(num_tokens, h->top_k)) {   // small batches need no routing kernel
         int rc = route(h, topk_ids, num_tokens, s, &plan);
         if (rc != MOE_OK) return rc;
     }
-    const moe::DispatchArgs da = dispatch_args(h, x, topk_ids, num_tokens, workspace, plan, 0);
+    da.tokens_per_chunk = plan.tokens_per_chunk;
+    da.n_chunks = plan.n_chunks;
     hipError_t e = moe::launch_dispatch_copy(da, s);
     if (e != hipSuccess) return hip_fail(h, e);
-
     h->phase = 1;
     h->num_tokens = num_tokens;
     h->runtime_max_tokens_per_rank = R;
     return MOE_OK;
+}
+
+int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
+                 int32_t num_tokens, int32_t runtime_max_tokens_per_rank,
+                 uint16_t *workspace, void *stream) {
+    const int32_t R = runtime_max_tokens_per_rank;
+    int rc = dispatch_checks(h, x, topk_ids, num_tokens, R, workspace);
+    if (rc != MOE_OK) return rc;
+    const moe::DispatchArgs da = dispatch_args(h, x, topk_ids, num_tokens, workspace,
+                                               moe::plan_route(num_tokens), 0);
+    return dispatch_launch(h, da, topk_ids, num_tokens, R, static_cast<hipStream_t>(stream));
+}
+
+int moe_dispatch_fp8(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
+                     int32_t num_tokens, int32_t runtime_max_tokens_per_rank,
+                     uint8_t *workspace, float *scales, void *stream) {
+    const int32_t R = runtime_max_tokens_per_rank;
+    int rc = dispatch_checks(h, x, topk_ids, num_tokens, R, workspace);
+    if (rc != MOE_OK) return rc;
+    if (!dev_ok(scales, 4) || h->hidden > MOE_MAX_FUSED_HIDDEN) return MOE_ERR_ARG;
+    moe::DispatchArgs da = dispatch_args(h, x, topk_ids, num_tokens, nullptr,
+                                         moe::plan_route(num_tokens), 0);
+    da.fp8 = 1;
+    da.ws8 = workspace;
+    da.scales = scales;
+    return dispatch_launch(h, da, topk_ids, num_tokens, R, static_cast<hipStream_t>(stream));
 }
 
 int moe_route_counts(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens, void *stream) {

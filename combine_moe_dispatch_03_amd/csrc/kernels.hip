@@ -218,12 +218,94 @@ __device__ __forceinline__ void assign_rows(const DispatchArgs &a, int d, int ti
     __syncthreads();
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Payload writers: the token's row (VPT vectors of 8 bf16 per thread, lanes
+// with col >= vpr hold a duplicate vector and store nothing) goes to every
+// row in copy_rows.
 template <int VPT, bool NT>
+__device__ __forceinline__ void store_rows_bf16(const DispatchArgs &a, const u32x4 (&v)[VPT],
+                                                const int (&col)[VPT], const int64_t (&off)[VPT],
+                                                int vpr, const int32_t *copy_rows) {
+    for (int j = 0; j < a.k; ++j) {
+        const int row = uniform(copy_rows[j]);
+        if (row < 0) continue;
+        uint16_t *dst = a.ws + (int64_t)row * a.H;
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) {
+            if (col[q] >= vpr) continue;
+            u32x4 *p = reinterpret_cast<u32x4 *>(dst + off[q]);
+            if (NT)
+                __builtin_nontemporal_store(v[q], p);
+            else
+                *p = v[q];
+        }
+    }
+}
+
+// FP8 payload: one scale per row.  amax = max |x| over the row (block
+// reduction: wave shuffles, then the 4 wave maxima in LDS); scale = amax/448,
+// q = e4m3(x * (448/amax)) with gfx950's nearest-even conversion
+// (v_cvt_pk_fp8_f32), 8 codes per 8-byte store; an all-zero row gets scale 0
+// and zero codes.  The whole row must be in the block (one column block).
+template <int VPT, bool NT>
+__device__ __forceinline__ void store_rows_fp8(const DispatchArgs &a, const u32x4 (&v)[VPT],
+                                               const int (&col)[VPT], const int64_t (&off)[VPT],
+                                               int vpr, const int32_t *copy_rows, float *red,
+                                               int tid) {
+    float m = 0.0f;
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+        if (col[q] >= vpr) continue;
+        float f[8];
+        unpack8(v[q], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(f[e]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    float amax = red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, red[w]);
+    const float scale = amax / 448.0f;
+    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+    u32x2 qv[VPT];
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+        float f[8];
+        unpack8(v[q], f);
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] * inv, f[1] * inv, 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] * inv, f[3] * inv, lo, true);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4] * inv, f[5] * inv, 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6] * inv, f[7] * inv, hi, true);
+        qv[q] = u32x2{(uint32_t)lo, (uint32_t)hi};
+    }
+    for (int j = 0; j < a.k; ++j) {
+        const int row = uniform(copy_rows[j]);
+        if (row < 0) continue;
+        uint8_t *dst = a.ws8 + (int64_t)row * a.H;
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) {
+            if (col[q] >= vpr) continue;
+            u32x2 *p = reinterpret_cast<u32x2 *>(dst + off[q]);
+            if (NT)
+                __builtin_nontemporal_store(qv[q], p);
+            else
+                *p = qv[q];
+        }
+        if (tid == 0) a.scales[row] = scale;
+    }
+}
+
+template <int VPT, bool NT, bool FP8>
 __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a) {
     __shared__ int32_t base[MOE_MAX_EP];
     __shared__ int32_t dests[MOE_MAX_TOP_K];
     __shared__ int32_t rows[MOE_MAX_TOP_K];
     __shared__ int32_t copy_rows[MOE_MAX_TOP_K];
+    __shared__ float red[kWaves];
 
     const int tid = threadIdx.x;
     const int t = blockIdx.x;
@@ -271,21 +353,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
     add_region_sums(base, a.hist, chunk * ep, ep, tid);
     __syncthreads();
     assign_rows(a, d, tid, cb, f, base, rank, dests, rows, copy_rows);
-
-    for (int j = 0; j < a.k; ++j) {
-        const int row = uniform(copy_rows[j]);
-        if (row < 0) continue;
-        uint16_t *dst = a.ws + (int64_t)row * a.H;
-#pragma unroll
-        for (int q = 0; q < VPT; ++q) {
-            if (col[q] >= vpr) continue;
-            u32x4 *p = reinterpret_cast<u32x4 *>(dst + off[q]);
-            if (NT)
-                __builtin_nontemporal_store(v[q], p);
-            else
-                *p = v[q];
-        }
-    }
+    if constexpr (FP8)
+        store_rows_fp8<VPT, NT>(a, v, col, off, vpr, copy_rows, red, tid);
+    else
+        store_rows_bf16<VPT, NT>(a, v, col, off, vpr, copy_rows);
 }
 
 template <bool NT>
@@ -343,12 +414,13 @@ __device__ __forceinline__ void count_regions(int32_t *cnt, const DispatchArgs &
     }
 }
 
-template <int VPT, bool NT>
+template <int VPT, bool NT, bool FP8>
 __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a) {
     __shared__ int32_t cnt[MOE_MAX_EP];
     __shared__ int32_t dests[MOE_MAX_TOP_K];
     __shared__ int32_t rows[MOE_MAX_TOP_K];
     __shared__ int32_t copy_rows[MOE_MAX_TOP_K];
+    __shared__ float red[kWaves];
 
     const int tid = threadIdx.x;
     const int t = blockIdx.x;
@@ -397,21 +469,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
         for (int j = 0; j < tid; ++j) rank += (dests[j] == d);
     __syncthreads();
     assign_rows(a, d, tid, cb, f, cnt, rank, dests, rows, copy_rows);
-
-    for (int j = 0; j < a.k; ++j) {
-        const int row = uniform(copy_rows[j]);
-        if (row < 0) continue;
-        uint16_t *dst = a.ws + (int64_t)row * a.H;
-#pragma unroll
-        for (int q = 0; q < VPT; ++q) {
-            if (col[q] >= vpr) continue;
-            u32x4 *p = reinterpret_cast<u32x4 *>(dst + off[q]);
-            if (NT)
-                __builtin_nontemporal_store(v[q], p);
-            else
-                *p = v[q];
-        }
-    }
+    if constexpr (FP8)
+        store_rows_fp8<VPT, NT>(a, v, col, off, vpr, copy_rows, red, tid);
+    else
+        store_rows_bf16<VPT, NT>(a, v, col, off, vpr, copy_rows);
 }
 
 // G rows starting at compacted copy j0: all G x VPT loads, then the adds in
@@ -593,12 +654,22 @@ constexpr bool kCopyNT = true;
 constexpr bool kCombineNT = true;
 template <int VPT> constexpr int combine_group() { return VPT >= 8 ? 4 : 8; }
 
-template <int VPT>
+template <int VPT, bool FP8>
 void launch_copy_vpt(const DispatchArgs &a, dim3 grid, hipStream_t s, bool small) {
     if (small)
-        hipLaunchKernelGGL((dispatch_small_kernel<VPT, kCopyNT>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((dispatch_small_kernel<VPT, kCopyNT, FP8>), grid, dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT, FP8>), grid, dim3(kThreads), 0, s, a);
+}
+
+template <bool FP8>
+void launch_copy(const DispatchArgs &a, int vpt, dim3 grid, hipStream_t s, bool small) {
+    switch (vpt) {
+        case 1: launch_copy_vpt<1, FP8>(a, grid, s, small); break;
+        case 2: launch_copy_vpt<2, FP8>(a, grid, s, small); break;
+        case 4: launch_copy_vpt<4, FP8>(a, grid, s, small); break;
+        default: launch_copy_vpt<8, FP8>(a, grid, s, small); break;
+    }
 }
 
 template <int VPT, bool FUSED>
@@ -632,16 +703,15 @@ bool dispatch_is_small(int32_t num_tokens, int32_t top_k) {
 }
 
 hipError_t launch_dispatch_copy(const DispatchArgs &a, hipStream_t s) {
-    const int vpt = streaming_vpt(a.T, a.H);
+    // the fp8 payload needs the whole row in a block for its scale
+    const int vpt = a.fp8 ? full_row_vpt(a.H) : streaming_vpt(a.T, a.H);
     const dim3 grid(a.T > 0 && !a.count_only ? a.T : 1,
                     a.T > 0 && !a.count_only ? column_blocks(a.H, vpt) : 1);
     const bool small = !a.count_only && dispatch_is_small(a.T, a.k);
-    switch (vpt) {
-        case 1: launch_copy_vpt<1>(a, grid, s, small); break;
-        case 2: launch_copy_vpt<2>(a, grid, s, small); break;
-        case 4: launch_copy_vpt<4>(a, grid, s, small); break;
-        default: launch_copy_vpt<8>(a, grid, s, small); break;
-    }
+    if (a.fp8)
+        launch_copy<true>(a, vpt, grid, s, small);
+    else
+        launch_copy<false>(a, vpt, grid, s, small);
     return hipGetLastError();
 }
 

@@ -59,6 +59,9 @@ struct DispatchArgs {
     int32_t tokens_per_chunk, n_chunks;
     int32_t count_only;      // 1: only write counts
     int32_t per_region;      // 1: one row per (token, region), duplicates share it
+    int32_t fp8;             // 1: payload is e4m3 rows in ws8 plus one scale per row
+    uint8_t *ws8;            // [ep, cap, H] e4m3 (fp8 payload)
+    float *scales;           // [ep, cap]    row scales (fp8 payload)
 };
 
 struct CombineArgs {

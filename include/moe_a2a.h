@@ -171,6 +171,27 @@ int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
                  uint16_t *workspace, void *stream);
 
 /*
+ * moe_dispatch_fp8 -- moe_dispatch with an FP8 payload: each token row is
+ * quantised once to OCP FP8 E4M3 with one fp32 scale, and the codes and the
+ * scale travel to every destination row ([A2A] "The adapter" notes: an FP8
+ * dispatch carries its scale as a second payload, checked against the
+ * oracle's cast round-trip).  Per token row:
+ *   amax  = max_h |x[t, h]|,   scale = amax / 448,
+ *   q[h]  = e4m3_nearest_even( x[t, h] * (448 / amax) )      (fp32 ops)
+ * so x ~ e4m3_value(q) * scale; an all-zero row gets scale 0 and zero codes.
+ *   workspace  device [ep, cap, H] uint8 codes, 16-byte aligned
+ *   scales     device [ep, cap] fp32, 4-byte aligned; scales[r*cap + s] is
+ *              the scale of row (r, s), written for valid rows only
+ * Other arguments, outputs (counts, slot_index, src_index), errors and the
+ * phase as moe_dispatch; requires H <= MOE_MAX_FUSED_HIDDEN.  The combine
+ * that follows reads bf16 expert outputs from a buffer of the same
+ * [ep, cap, H] layout (the experts dequantise and write it).
+ */
+int moe_dispatch_fp8(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
+                     int32_t num_tokens, int32_t runtime_max_tokens_per_rank,
+                     uint8_t *workspace, float *scales, void *stream);
+
+/*
  * moe_combine -- reduce each token's k expert outputs exactly once.
  * [A2A] "Update -- the correctness failures are resolved": fp32
  * accumulation, one nearest-even narrowing store; [DR]: the result is final.

@@ -32,7 +32,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_exports_every_declared_function(lib):
@@ -140,6 +140,21 @@ def test_dispatch_argument_checks(lib):
     assert lib.moe_reset(ctypes.byref(h)) == moe.MOE_OK and h.phase == 0
     assert lib.moe_route_counts(ctypes.byref(h), FAKE, 65, None) == moe.MOE_ERR_ARG
     assert lib.moe_route_counts(ctypes.byref(h), FAKE + 1, 8, None) == moe.MOE_ERR_ARG
+
+
+def test_fp8_dispatch_argument_checks(lib):
+    h = make_handle(lib)
+    d = lambda x, ids, T, R, ws, sc: lib.moe_dispatch_fp8(ctypes.byref(h), x, ids, T, R, ws, sc, None)
+    assert d(FAKE, FAKE, 8, 8, FAKE, None) == moe.MOE_ERR_ARG      # no scales
+    assert d(FAKE, FAKE, 8, 8, FAKE, FAKE + 2) == moe.MOE_ERR_ARG  # scales misaligned
+    assert d(FAKE, FAKE, 8, 8, FAKE + 8, FAKE) == moe.MOE_ERR_ARG  # workspace misaligned
+    assert d(FAKE, FAKE, 65, 65, FAKE, FAKE) == moe.MOE_ERR_ARG
+    wide = make_handle(lib, H=16392)
+    assert lib.moe_dispatch_fp8(ctypes.byref(wide), FAKE, FAKE, 8, 8, FAKE, FAKE,
+                                None) == moe.MOE_ERR_ARG         # row too wide for one block
+    h.phase = 1
+    assert d(FAKE, FAKE, 8, 8, FAKE, FAKE) == moe.MOE_ERR_PHASE
+    assert h.phase == 1 and wide.phase == 0
 
 
 def test_combine_argument_and_phase_checks(lib):

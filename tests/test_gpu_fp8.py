@@ -1,0 +1,102 @@
+"""Parity of the FP8 (OCP E4M3) dispatch payload with the oracle on the GPU.
+
+Codes, per-row scales, counts, slot_index and src_index must match the
+oracle bit for bit (the quantisation is fp32 arithmetic plus a
+nearest-even conversion on both sides); padding bytes and scales keep their
+NaN fill.  Full prefill / decode / skewed shapes, both layouts and both
+dispatch paths, plus rows that exercise zero, subnormal and saturating codes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_dispatch_03_amd as moe
+import oracle
+import pins
+import synth
+from gpu_harness import say, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+FILL = 0x7F            # e4m3 NaN: marks workspace bytes that must stay untouched
+
+
+def fp8_check(x, ids, E, ep, cap, R=None, layout="copy"):
+    orc = oracle.load()
+    T, H = x.shape
+    k = ids.shape[1]
+    ref, ref_scales = orc.dispatch_fp8(x, ids, ep, E // ep, cap, layout=layout)
+    h = moe.MoeA2A(R or max(T, 1), H, k, E, ep, cap, layout=layout)
+    ws = h.new_workspace_fp8(FILL)
+    scales = h.new_scales()
+    moe.moe_dispatch_fp8(h, to_dev_bf16(x), to_dev(ids), R or max(T, 1), ws, scales)
+    code, bits = moe.moe_sync_status(h)
+    assert bits == ref.status, (bits, ref.status)
+    assert np.array_equal(h.counts.cpu().numpy(), ref.counts)
+    assert np.array_equal(h.slot_index_view().cpu().numpy(), ref.slot_index)
+    src = h.src_index_view().cpu().numpy()
+    sc = scales.cpu().numpy()
+    for r in range(ep):
+        n = min(int(ref.counts[r]), cap)
+        assert np.array_equal(src[r, :n], ref.src_index[r, :n])
+        got = ws[r, :n].cpu().numpy()
+        bad = np.argwhere(got != ref.ws[r, :n])
+        assert bad.size == 0, (r, bad[:3], got[tuple(bad[0])], ref.ws[r, :n][tuple(bad[0])])
+        assert np.array_equal(sc[r, :n].view(np.uint32), ref_scales[r, :n].view(np.uint32))
+        if n < cap:
+            assert bool((ws[r, n:] == FILL).all()) and np.isnan(sc[r, n:]).all()
+    assert h.handle.phase == 1
+    return ref
+
+
+@pytest.mark.parametrize("name,layout", [("prefill", "copy"), ("decode", "copy"),
+                                         ("skewed", "copy"), ("prefill", "region"),
+                                         ("decode", "region")])
+def test_fp8_dispatch_full_size(name, layout):
+    wl = synth.BY_NAME[name]
+    say("fp8 dispatch", name, layout)
+    inp = synth.make_inputs(wl, 0)
+    cap = wl.T if layout == "region" else wl.cap
+    if cap is None:
+        cap = int(oracle.load().dispatch(np.zeros((wl.T, 1), np.uint16), inp.ids, wl.ep, wl.epr,
+                                         wl.T * wl.k).counts.max())
+    fp8_check(inp.x, inp.ids, wl.E, wl.ep, cap, R=wl.R, layout=layout)
+
+
+def test_fp8_rows_with_zero_subnormal_and_extreme_values():
+    say("fp8 special rows")
+    rng = np.random.default_rng(3)
+    T, H, k, E, ep = 12, 256, 2, 8, 4
+    xf = rng.standard_normal((T, H)).astype(np.float32)
+    xf[0] = 0.0                                        # all zero: scale 0, codes 0
+    xf[1] = 0.0
+    xf[1, 7] = -5.0                                    # one element: -448, rest zero
+    xf[2] *= np.float32(2.0 ** -100)                   # tiny magnitudes
+    xf[3] *= np.float32(2.0 ** 100)                    # huge magnitudes
+    xf[4, :] = rng.standard_normal(H).astype(np.float32) * 1e-4
+    xf[4, 0] = 300.0                                   # most codes subnormal or zero
+    xf[5, :] = 1.0                                     # constant row
+    x = pins.torch_bf16_bits(xf)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    fp8_check(x, ids, E, ep, T * k)
+
+
+@pytest.mark.parametrize("T,H", [(37, 136), (5, 16384), (2500, 64)])
+def test_fp8_ragged_and_two_kernel_shapes(T, H):
+    say("fp8 shapes", T, H)
+    rng = np.random.default_rng(T + H)
+    x = pins.random_bf16(rng, (T, H))
+    ids = rng.integers(-1, 24, size=(T, 3)).astype(np.int32)
+    fp8_check(x, ids, 24, 4, T * 3)
+    fp8_check(x, ids, 24, 4, T, layout="region")
+
+
+def test_fp8_bad_ids_and_overflow():
+    say("fp8 bad ids / overflow")
+    rng = np.random.default_rng(9)
+    T, H, k, E, ep = 50, 64, 4, 8, 2
+    x = pins.random_bf16(rng, (T, H))
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids[4, 1] = 99
+    ref = fp8_check(x, ids, E, ep, 60)
+    assert ref.status == oracle.STATUS_BAD_ID | oracle.STATUS_OVERFLOW
