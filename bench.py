@@ -26,7 +26,8 @@ line also carries:
                 same workload, repeated for about 10 s
   cold          per-kernel p50 / mean over --cold-iters launches, each after
                 an untimed 1 GiB read that evicts the 256 MB Infinity Cache
-  workloads     the same step on the skewed, decode and fused workloads, and
+  workloads     the same step on the skewed, decode and fused workloads (decode
+                also replayed from a captured HIP graph, ``graph_*``), and
                 on prefill and skewed under the per-region layout (one row per
                 token and destination region, the form the FlashInfer pages
                 measure; unweighted combine of per-region messages), and with
@@ -125,7 +126,7 @@ def describe(wl, cap) -> str:
 
 
 def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0,
-            layout: str = "copy", payload: str = "bf16") -> dict:
+            layout: str = "copy", payload: str = "bf16", graph: bool = False) -> dict:
     import numpy as np
     import torch
 
@@ -164,23 +165,26 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0,
     sh = stream.cuda_stream
     hev = HipEvents()
 
-    def dispatch():
+    def dispatch(st=stream):
         if fp8:
-            moe.moe_dispatch_fp8(h, x, ids, wl.R, ws8, scales, stream=stream)
+            moe.moe_dispatch_fp8(h, x, ids, wl.R, ws8, scales, stream=st)
         else:
-            moe.moe_dispatch(h, x, ids, wl.R, ws, stream=stream)
+            moe.moe_dispatch(h, x, ids, wl.R, ws, stream=st)
 
-    def step(ev=None):
-        if ev is not None:
-            hev.record(ev[0], sh)
-        dispatch()
-        if ev is not None:
-            hev.record(ev[1], sh)
+    def combine(st=stream):
         if fused:
             moe.moe_combine_residual_rmsnorm(h, ws, w, weighted, res, gamma, wl.eps,
-                                             residual_out=res_out, normed=out, stream=stream)
+                                             residual_out=res_out, normed=out, stream=st)
         else:
-            moe.moe_combine(h, ws, w, weighted, out=out, stream=stream)
+            moe.moe_combine(h, ws, w, weighted, out=out, stream=st)
+
+    def step(ev=None, st=stream):
+        if ev is not None:
+            hev.record(ev[0], sh)
+        dispatch(st)
+        if ev is not None:
+            hev.record(ev[1], sh)
+        combine(st)
         if ev is not None:
             hev.record(ev[2], sh)
 
@@ -192,6 +196,34 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0,
     for _ in range(warmup):
         step()
     check_status("after warmup")
+    graph_ms = None
+    if graph:
+        # the same step captured once in a HIP graph and replayed: no host
+        # launch overhead between steps (the decode step is launch-bound)
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(st=side)
+        stream.wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(st=torch.cuda.current_stream(dev))     # the capturing stream
+        if h.handle.phase != 0:
+            raise RuntimeError("capture left the handle dispatched")
+        eager = out.clone()
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize(dev)
+        if not torch.equal(out.view(torch.int16), eager.view(torch.int16)):
+            raise RuntimeError("graph replay does not reproduce the eager step")
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize(dev)
+        graph_ms = (time.perf_counter() - t0) * 1e3 / steps
+        check_status("after the graph replays")
+        del g
     # timed steps (the headline figure): nothing but the path itself is enqueued
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
@@ -228,11 +260,7 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0,
         hev.record(ev[1], sh)
         flush.max()
         hev.record(ev[2], sh)
-        if fused:
-            moe.moe_combine_residual_rmsnorm(h, ws, w, weighted, res, gamma, wl.eps,
-                                             residual_out=res_out, normed=out, stream=stream)
-        else:
-            moe.moe_combine(h, ws, w, weighted, out=out, stream=stream)
+        combine()
         hev.record(ev[3], sh)
     torch.cuda.synchronize(dev)
     check_status("after the cold launches")
@@ -266,6 +294,10 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0,
     res_d["dispatch_gbs"] = b["dispatch"] / (res_d["dispatch_ms_mean"] / 1e3) / 1e9
     res_d["combine_gbs"] = comb_bytes / (res_d["combine_ms_mean"] / 1e3) / 1e9
     res_d["step_hbm_frac"] = res_d["step_gbs"] / HBM_PEAK_GBS
+    if graph_ms is not None:
+        res_d["graph_ms_per_step"] = graph_ms
+        res_d["graph_tokens_per_s"] = wl.T / (graph_ms / 1e3)
+        res_d["graph_step_gbs"] = (b["dispatch"] + comb_bytes) / (graph_ms / 1e3) / 1e9
     res_d["cold"] = None
     if cold_iters > 0:
         res_d["cold"] = cold_stats(cd_ms, cc_ms, cold_iters, wl.T, b["dispatch"], comb_bytes)
@@ -346,7 +378,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--workload", default="prefill",
+                    help="headline workload (a _region / _fp8 suffix selects a variant)")
     ap.add_argument("--extras",
                     default="skewed,decode,fused,prefill_region,skewed_region,prefill_fp8,"
                             "prefill_region_fp8",
@@ -370,15 +403,20 @@ def main() -> int:
         return 0
 
     import synth
-    wl = synth.BY_NAME[args.workload]
-    main_res = measure(wl, args.steps, args.warmup, args.cold_iters)
-    extras = {}
-    for name in [n for n in args.extras.split(",") if n and n != wl.name]:
+
+    def variant(name):
+        """workload name with optional _region / _fp8 suffixes"""
         base, *mods = name.split("_")
-        extras[name] = measure(synth.BY_NAME[base], max(args.steps // 2, 5),
-                               max(args.warmup // 2, 2), args.cold_iters,
-                               layout="region" if "region" in mods else "copy",
-                               payload="fp8" if "fp8" in mods else "bf16")
+        return synth.BY_NAME[base], dict(layout="region" if "region" in mods else "copy",
+                                         payload="fp8" if "fp8" in mods else "bf16")
+
+    wl, opts = variant(args.workload)
+    main_res = measure(wl, args.steps, args.warmup, args.cold_iters, **opts)
+    extras = {}
+    for name in [n for n in args.extras.split(",") if n and n != args.workload]:
+        ewl, eopts = variant(name)
+        extras[name] = measure(ewl, max(args.steps // 2, 5), max(args.warmup // 2, 2),
+                               args.cold_iters, graph=ewl.name == "decode", **eopts)
 
     comb_ms = main_res["combine_ms_mean"]
     achieved = main_res["combine_bytes"] / (comb_ms / 1e3) / 1e9

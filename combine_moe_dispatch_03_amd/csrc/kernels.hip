@@ -92,6 +92,21 @@ __device__ __forceinline__ void add_region_sums(int32_t *base, const int32_t *hi
     }
 }
 
+// Per-region layout, wave form: d is this lane's region (or -1) and j the
+// position of its copy within the token.  When k divides 64 and the items of
+// a wave are consecutive flat indices starting at a multiple of k, a token's
+// copies sit in consecutive lanes of one wave, so the earlier copies are the
+// j lanes below; every lane must call this (shuffles), k is uniform.
+__device__ __forceinline__ bool first_in_wave(int d, int j, int k) {
+    const int lane = threadIdx.x & 63;
+    bool first = true;
+    for (int jj = 1; jj < k; ++jj) {
+        const int other = __shfl(d, (lane - jj) & 63);
+        if (jj <= j && other == d) first = false;
+    }
+    return first;
+}
+
 // Per-region layout: true if no earlier copy of the same token (flat indices
 // token_base .. i-1) is bound for region d.  Reads the token's ids from L1/L2.
 __device__ __forceinline__ bool first_to_region(const int32_t *ids, int64_t token_base, int64_t i,
@@ -101,6 +116,21 @@ __device__ __forceinline__ bool first_to_region(const int32_t *ids, int64_t toke
         if (e >= 0 && e < n_experts && e / epr == d) return false;
     }
     return true;
+}
+
+// Per-region layout: d if flat copy i is its token's first copy to region d,
+// else -1.  Called by every lane with uniform k; `active` lanes hold a copy.
+// Items are consecutive flat indices from a multiple of k (tiles of 256 from
+// a chunk start), so when k divides 64 the wave form applies.
+template <typename Args>
+__device__ __forceinline__ int first_copy_region(const Args &a, int d, int64_t i, bool active) {
+    if (64 % a.k == 0) {
+        const bool first = first_in_wave(d, active ? (int)(i % a.k) : 0, a.k);
+        return first ? d : -1;
+    }
+    if (active && d >= 0 && !first_to_region(a.ids, i - i % a.k, i, d, a.epr, a.n_experts))
+        return -1;
+    return d;
 }
 
 // ---------------------------------------------------------------------------
@@ -142,9 +172,9 @@ __global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
                 d = e / a.epr;
             else if (e != -1)
                 bad = true;
-            if (d >= 0 && a.per_region && !first_to_region(a.ids, i - i % a.k, i, d, a.epr, a.n_experts))
-                d = -1;                          // shares the row of the token's first copy
         }
+        if (a.per_region)                        // later copies share the first copy's row
+            d = first_copy_region(a, d, i, i < end);
         uint64_t same = __ballot(d >= 0);
         for (int b = 0; b < region_bits; ++b) {
             const bool bit = d >= 0 && ((d >> b) & 1);
@@ -389,21 +419,31 @@ __device__ __forceinline__ void accumulate(float (&acc)[VPT][8], const u32x4 (&r
 // Within a wave, lanes bound for the same region are grouped with one ballot
 // per bit of the region number (as in route_rank_kernel) so each group adds
 // its size to the LDS counter with one atomic.
+static_assert(kSmallItems % kThreads == 0, "small-batch ids are split evenly over a block");
 __device__ __forceinline__ void count_regions(int32_t *cnt, const DispatchArgs &a, int64_t n,
                                               int region_bits, int tid, bool *bad) {
+    // n <= kSmallItems: every id this thread needs is loaded up front
+    constexpr int kPer = kSmallItems / kThreads;
     const int lane = tid & 63;
-    for (int64_t base = 0; base < n; base += kThreads) {
-        const int64_t i = base + tid;
+    int ids[kPer];
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+        const int64_t i = (int64_t)p * kThreads + tid;
+        ids[p] = i < n ? a.ids[i] : -1;
+    }
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+        if ((int64_t)p * kThreads >= n) break;         // uniform
+        const int64_t i = (int64_t)p * kThreads + tid;
+        const int e = ids[p];
         int d = -1;
         if (i < n) {
-            const int e = a.ids[i];
             if (e >= 0 && e < a.n_experts)
                 d = e / a.epr;
             else if (e != -1)
                 *bad = true;
-            if (d >= 0 && a.per_region && !first_to_region(a.ids, i - i % a.k, i, d, a.epr, a.n_experts))
-                d = -1;
         }
+        if (a.per_region) d = first_copy_region(a, d, i, i < n);
         uint64_t same = __ballot(d >= 0);
         for (int b = 0; b < region_bits; ++b) {
             const bool bit = d >= 0 && ((d >> b) & 1);

@@ -1,0 +1,76 @@
+"""dispatch + combine captured in a HIP graph (torch.cuda.CUDAGraph).
+
+The hot-path calls only enqueue kernels (no host synchronisation, no memset),
+so a caller can capture them.  Each graph is replayed several times with the
+program's own eager work and synchronisations in between, and every replay is
+checked bit for bit against the eager result.  (moe_sync_status synchronises
+and is not captured.)
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_dispatch_03_amd as moe
+import synth
+from gpu_harness import say, to_dev, to_dev_bf16, to_u16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,layout,fused", [("decode", "copy", False),
+                                               ("decode", "region", False),
+                                               ("fused", "copy", True)])
+def test_graph_replays_match_eager(name, layout, fused):
+    wl = synth.BY_NAME[name]
+    say("graph", name, layout, "fused" if fused else "")
+    inp = synth.make_inputs(wl, 0)
+    x, ids = to_dev_bf16(inp.x), to_dev(inp.ids)
+    weighted = layout == "copy"
+    w = to_dev(inp.weights) if weighted else None
+    cap = wl.cap if layout == "copy" else wl.T
+    h = moe.MoeA2A(wl.R, wl.H, wl.k, wl.E, wl.ep, cap, layout=layout)
+    ws = h.new_workspace(0)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    if fused:
+        res, gamma = to_dev_bf16(inp.residual), to_dev_bf16(inp.gamma)
+        res_out = torch.empty_like(res)
+
+    def step():
+        moe.moe_dispatch(h, x, ids, wl.R, ws)
+        if fused:
+            moe.moe_combine_residual_rmsnorm(h, ws, w, weighted, res, gamma, wl.eps,
+                                             residual_out=res_out, normed=out)
+        else:
+            moe.moe_combine(h, ws, w, weighted, out=out)
+
+    step()                                            # eager reference
+    torch.cuda.synchronize()
+    assert moe.moe_sync_status(h) == (moe.MOE_OK, 0)
+    want = [to_u16(out), h.slot_index_view().cpu().numpy().copy()]
+    if fused:
+        want.append(to_u16(res_out))
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                        # warm the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    assert h.handle.phase == 0
+
+    for rep in range(4):
+        out.zero_()                                   # eager work between replays
+        h.slot_index.fill_(-7)
+        if fused:
+            res_out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [to_u16(out), h.slot_index_view().cpu().numpy()]
+        if fused:
+            got.append(to_u16(res_out))
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b), f"replay {rep} differs"
+    assert moe.moe_sync_status(h) == (moe.MOE_OK, 0)
