@@ -1,0 +1,115 @@
+// Drives the host side of the C ABI (argument checks, phase machine, scratch
+// carving, HIP error path) built with host-only AddressSanitizer and
+// UndefinedBehaviorSanitizer by test_sanitizers.py.  The kernel launchers are
+// replaced by stubs that check the argument blocks against the caller's
+// buffers and count launches, so no GPU is needed; moe_sync_status runs into
+// the HIP runtime and must either succeed or report MOE_ERR_HIP.
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "launch.h"
+#include "moe_a2a.h"
+
+static const int32_t *g_scratch = nullptr;   // the scratch buffer handed to moe_init
+static int64_t g_scratch_ints = 0;
+
+static bool in_scratch(const int32_t *p, int64_t n) {
+    return p >= g_scratch && n >= 0 && (p - g_scratch) + n <= g_scratch_ints;
+}
+
+namespace moe {
+static int launches = 0;
+RoutePlan plan_route(int32_t num_tokens) {
+    RoutePlan p;
+    p.tokens_per_chunk = num_tokens > 0 ? (num_tokens + kMaxChunks - 1) / kMaxChunks : 1;
+    p.n_chunks = num_tokens > 0 ? (num_tokens + p.tokens_per_chunk - 1) / p.tokens_per_chunk : 0;
+    return p;
+}
+bool dispatch_is_small(int32_t num_tokens, int32_t top_k) {
+    return (int64_t)num_tokens * top_k <= kSmallItems;
+}
+hipError_t launch_route(const RouteArgs &a, int32_t n_chunks, hipStream_t) {
+    if (n_chunks < 1 || n_chunks > kMaxChunks || a.n_items < 1) std::abort();
+    if (!in_scratch(a.rank, a.n_items) || !in_scratch(a.hist, (int64_t)n_chunks * a.ep)) std::abort();
+    if ((int64_t)a.items_per_chunk * n_chunks < a.n_items) std::abort();
+    ++launches;
+    return hipSuccess;
+}
+hipError_t launch_dispatch_copy(const DispatchArgs &a, hipStream_t) {
+    if (a.T < 0 || a.n_chunks > kMaxChunks || (a.fp8 && (!a.ws8 || !a.scales))) std::abort();
+    if (!dispatch_is_small(a.T, a.k) &&
+        (!in_scratch(a.rank, (int64_t)a.T * a.k) || !in_scratch(a.hist, (int64_t)a.n_chunks * a.ep)))
+        std::abort();
+    ++launches;
+    return hipSuccess;
+}
+hipError_t launch_combine(const CombineArgs &a, bool fused, hipStream_t) {
+    if (a.T < 0 || a.k < 1 || (fused && (!a.residual || !a.gamma || !a.normed))) std::abort();
+    ++launches;
+    return hipSuccess;
+}
+}  // namespace moe
+
+#define CHECK(cond) do { if (!(cond)) { std::printf("FAILED: %s (line %d)\n", #cond, __LINE__); return 1; } } while (0)
+// launches made by one call
+#define LAUNCHES(call, n) do { int before_ = moe::launches; CHECK((call) == MOE_OK); CHECK(moe::launches - before_ == (n)); } while (0)
+
+int main() {
+    const int32_t T = 512, H = 128, k = 8, E = 64, ep = 8;
+    // aligned host buffers stand in for device memory: the stubs never dereference them
+    std::vector<int32_t> counts(ep), src(ep * T), slot(T * k), status(4);
+    alignas(16) static uint16_t x[T * H], ws[1 << 12], out[1 << 12];
+    alignas(16) static uint8_t ws8[1 << 12];
+    static float w[T * k], scales[ep * T];
+    static int32_t ids[T * k];
+    const size_t sb = moe_scratch_bytes(T, k, ep);
+    CHECK(sb >= (size_t)T * k * 4);
+    std::vector<int32_t> scratch(sb / 4);
+    g_scratch = scratch.data();
+    g_scratch_ints = (int64_t)scratch.size();
+    CHECK(moe_scratch_bytes(T, k, ep) == sb);
+
+    moe_handle h;
+    CHECK(moe_init(&h, T, H, k, E, ep, T, MOE_LAYOUT_PER_COPY, counts.data(), src.data(),
+                   slot.data(), status.data(), scratch.data(), sb - 4) == MOE_ERR_ARG);
+    CHECK(moe_init(&h, T, H, k, E, ep, T, MOE_LAYOUT_PER_COPY, counts.data(), src.data(),
+                   slot.data(), status.data(), scratch.data(), sb) == MOE_OK);
+    CHECK(moe_combine(&h, ws, w, 1, out, nullptr) == MOE_ERR_PHASE);
+    LAUNCHES(moe_dispatch(&h, x, ids, T, T, ws, nullptr), 2);           // routed: route + copy
+    CHECK(h.phase == 1 && h.num_tokens == T);
+    CHECK(moe_dispatch(&h, x, ids, T, T, ws, nullptr) == MOE_ERR_PHASE);
+    CHECK(moe_combine(&h, ws, nullptr, 1, out, nullptr) == MOE_ERR_ARG && h.phase == 1);
+    LAUNCHES(moe_combine(&h, ws, w, 1, out, nullptr), 1);
+    CHECK(h.phase == 0);
+    LAUNCHES(moe_dispatch(&h, x, ids, 256, 256, ws, nullptr), 1);      // 2048 copies: single launch
+    LAUNCHES(moe_combine_residual_rmsnorm(&h, ws, w, 1, out, out, out, 1e-6f, out, nullptr), 1);
+    LAUNCHES(moe_dispatch(&h, x, ids, 257, 300, ws, nullptr), 2);      // first routed size
+    CHECK(moe_reset(&h) == MOE_OK && h.phase == 0);
+    LAUNCHES(moe_dispatch_fp8(&h, x, ids, T, T, ws8, scales, nullptr), 2);
+    CHECK(moe_reset(&h) == MOE_OK);
+    LAUNCHES(moe_route_counts(&h, ids, T, nullptr), 2);
+    CHECK(h.phase == 0);
+    CHECK(moe_dispatch(&h, x, ids, T + 1, T, ws, nullptr) == MOE_ERR_ARG);
+    CHECK(moe_dispatch(&h, x, ids, 10, T + 1, ws, nullptr) == MOE_ERR_ARG);
+    CHECK(moe_dispatch(&h, x + 1, ids, 10, 10, ws, nullptr) == MOE_ERR_ARG);   // misaligned rows
+    LAUNCHES(moe_dispatch(&h, x, ids, 0, 1, ws, nullptr), 1);          // empty batch
+    LAUNCHES(moe_combine(&h, ws, nullptr, 0, nullptr, nullptr), 1);
+
+    // the status read needs the HIP runtime; with no GPU it must fail cleanly
+    int32_t bits = -1;
+    const int rc = moe_sync_status(&h, nullptr, &bits);
+    CHECK(rc == MOE_ERR_HIP || rc == MOE_OK);
+    CHECK(rc != MOE_ERR_HIP || h.hip_error != 0);
+
+    // per-region layout rejects a weighted combine
+    moe_handle g;
+    CHECK(moe_init(&g, T, H, k, E, ep, T, MOE_LAYOUT_PER_REGION, counts.data(), src.data(),
+                   slot.data(), status.data(), scratch.data(), sb) == MOE_OK);
+    LAUNCHES(moe_dispatch(&g, x, ids, T, T, ws, nullptr), 2);
+    CHECK(moe_combine(&g, ws, w, 1, out, nullptr) == MOE_ERR_ARG);
+    LAUNCHES(moe_combine(&g, ws, nullptr, 0, out, nullptr), 1);
+    for (int code = -6; code <= 1; ++code) CHECK(moe_strerror(code) != nullptr);
+    std::printf("sanitized ABI driver: ok (%d launches, sync_status rc %d)\n", moe::launches, rc);
+    return 0;
+}
