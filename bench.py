@@ -359,7 +359,19 @@ def cpu_baseline(wl, seconds: float = 10.0, seed: int = 0) -> dict:
         del d
     return {"value": wl.T * reps / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"the full {wl.name} workload ({wl.T} tokens, dispatch + combine), "
-                      f"{reps} repetition(s), {t_total:.1f} s, single-threaded scalar C"}
+                      f"{reps} repetition(s), {t_total:.1f} s, single-threaded scalar C",
+            "cpu_model": _cpu_model(), "host_cpus_visible": os.cpu_count()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def calibrate_copy(nbytes: int, reps: int) -> None:

@@ -107,9 +107,12 @@ def library() -> ctypes.CDLL:
 
 # ---------------------------------------------------------------- helpers
 
-def _stream(stream) -> Optional[int]:
+def _stream(stream, device_index: int) -> int:
+    """Raw HIP stream handle: the given stream, else the current stream of the
+    handle's device (read without building a torch Stream object, which costs
+    a few microseconds per call and would dominate a decode step)."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        return torch._C._cuda_getCurrentRawStream(device_index)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -118,6 +121,14 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None, numel=None):
+    # one combined test on the common path; the messages are built only on failure
+    if (isinstance(t, torch.Tensor) and t.dtype is dtype and t.is_cuda and t.is_contiguous()
+            and (shape is None or t.shape == shape) and (numel is None or t.numel() == numel)):
+        return
+    _need_failed(t, name, dtype, shape, numel)
+
+
+def _need_failed(t, name, dtype, shape, numel):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if t.dtype != dtype:
@@ -182,6 +193,8 @@ class MoeA2A:
                             _ptr(self.slot_index), _ptr(self.status), _ptr(self.scratch),
                             self.scratch.numel() * 4), "moe_init")
         self.device = dev
+        self.device_index = dev.index if dev.index is not None else torch.cuda.current_device()
+        self.ref = ctypes.byref(self.handle)     # built once, passed on every call
 
     # shapes
     @property
@@ -192,6 +205,9 @@ class MoeA2A:
     def ep_size(self) -> int: return self.handle.ep_size
     @property
     def cap(self) -> int: return self.handle.max_tokens_per_rank
+    @property
+    def workspace_numel(self) -> int:
+        return self.handle.ep_size * self.handle.max_tokens_per_rank * self.handle.hidden
     @property
     def num_tokens(self) -> int: return self.handle.num_tokens
     @property
@@ -234,9 +250,9 @@ def moe_dispatch(h: MoeA2A, x: torch.Tensor, topk_ids: torch.Tensor,
     T = x.shape[0] if x.dim() == 2 else 0
     _need(x, "x", torch.bfloat16, shape=(T, h.hidden))
     _need(topk_ids, "topk_ids", torch.int32, shape=(T, h.top_k))
-    _need(workspace, "workspace", torch.bfloat16, numel=h.ep_size * h.cap * h.hidden)
-    _check(library().moe_dispatch(ctypes.byref(h.handle), _ptr(x), _ptr(topk_ids), T,
-                                  runtime_max_tokens_per_rank, _ptr(workspace), _stream(stream)),
+    _need(workspace, "workspace", torch.bfloat16, numel=h.workspace_numel)
+    _check(library().moe_dispatch(h.ref, _ptr(x), _ptr(topk_ids), T, runtime_max_tokens_per_rank,
+                                  _ptr(workspace), _stream(stream, h.device_index)),
            "moe_dispatch")
 
 
@@ -248,11 +264,11 @@ def moe_dispatch_fp8(h: MoeA2A, x: torch.Tensor, topk_ids: torch.Tensor,
     T = x.shape[0] if x.dim() == 2 else 0
     _need(x, "x", torch.bfloat16, shape=(T, h.hidden))
     _need(topk_ids, "topk_ids", torch.int32, shape=(T, h.top_k))
-    _need(workspace, "workspace", torch.uint8, numel=h.ep_size * h.cap * h.hidden)
+    _need(workspace, "workspace", torch.uint8, numel=h.workspace_numel)
     _need(scales, "scales", torch.float32, numel=h.ep_size * h.cap)
-    _check(library().moe_dispatch_fp8(ctypes.byref(h.handle), _ptr(x), _ptr(topk_ids), T,
+    _check(library().moe_dispatch_fp8(h.ref, _ptr(x), _ptr(topk_ids), T,
                                       runtime_max_tokens_per_rank, _ptr(workspace), _ptr(scales),
-                                      _stream(stream)), "moe_dispatch_fp8")
+                                      _stream(stream, h.device_index)), "moe_dispatch_fp8")
 
 
 def moe_combine(h: MoeA2A, expert_out: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
@@ -261,15 +277,15 @@ def moe_combine(h: MoeA2A, expert_out: torch.Tensor, topk_weights: Optional[torc
     """out[t] = bf16(sum_j c_j * expert_out[slot(t, j)]), reduced once in fp32."""
     T = h.handle.num_tokens
     weighted = (topk_weights is not None) if weighted is None else bool(weighted)
-    _need(expert_out, "expert_out", torch.bfloat16, numel=h.ep_size * h.cap * h.hidden)
+    _need(expert_out, "expert_out", torch.bfloat16, numel=h.workspace_numel)
     if weighted:
         _need(topk_weights, "topk_weights", torch.float32, shape=(T, h.top_k))
     if out is None:
         out = torch.empty((T, h.hidden), dtype=torch.bfloat16, device=expert_out.device)
     _need(out, "out", torch.bfloat16, shape=(T, h.hidden))
-    _check(library().moe_combine(ctypes.byref(h.handle), _ptr(expert_out),
+    _check(library().moe_combine(h.ref, _ptr(expert_out),
                                  _ptr(topk_weights) if weighted else None, int(weighted),
-                                 _ptr(out), _stream(stream)), "moe_combine")
+                                 _ptr(out), _stream(stream, h.device_index)), "moe_combine")
     return out
 
 
@@ -283,7 +299,7 @@ def moe_combine_residual_rmsnorm(h: MoeA2A, expert_out: torch.Tensor,
 
     Returns (residual_out, normed); ``residual_out`` may be ``residual``."""
     T, H = h.handle.num_tokens, h.hidden
-    _need(expert_out, "expert_out", torch.bfloat16, numel=h.ep_size * h.cap * H)
+    _need(expert_out, "expert_out", torch.bfloat16, numel=h.workspace_numel)
     if weighted:
         _need(topk_weights, "topk_weights", torch.float32, shape=(T, h.top_k))
     _need(residual, "residual", torch.bfloat16, shape=(T, H))
@@ -295,9 +311,9 @@ def moe_combine_residual_rmsnorm(h: MoeA2A, expert_out: torch.Tensor,
     _need(residual_out, "residual_out", torch.bfloat16, shape=(T, H))
     _need(normed, "normed", torch.bfloat16, shape=(T, H))
     _check(library().moe_combine_residual_rmsnorm(
-        ctypes.byref(h.handle), _ptr(expert_out), _ptr(topk_weights) if weighted else None,
+        h.ref, _ptr(expert_out), _ptr(topk_weights) if weighted else None,
         int(bool(weighted)), _ptr(residual), _ptr(residual_out), _ptr(gamma), float(eps),
-        _ptr(normed), _stream(stream)), "moe_combine_residual_rmsnorm")
+        _ptr(normed), _stream(stream, h.device_index)), "moe_combine_residual_rmsnorm")
     return residual_out, normed
 
 
@@ -305,22 +321,22 @@ def moe_route_counts(h: MoeA2A, topk_ids: torch.Tensor, stream=None) -> torch.Te
     """Per-region copy counts of a routing (for sizing max_tokens_per_rank)."""
     T = topk_ids.shape[0]
     _need(topk_ids, "topk_ids", torch.int32, shape=(T, h.top_k))
-    _check(library().moe_route_counts(ctypes.byref(h.handle), _ptr(topk_ids), T,
-                                      _stream(stream)), "moe_route_counts")
+    _check(library().moe_route_counts(h.ref, _ptr(topk_ids), T,
+                                      _stream(stream, h.device_index)), "moe_route_counts")
     return h.counts
 
 
 def moe_sync_status(h: MoeA2A, stream=None) -> Tuple[int, int]:
     """Wait for the stream; returns (code, status bits) and clears the bits."""
     bits = ctypes.c_int32(0)
-    code = library().moe_sync_status(ctypes.byref(h.handle), _stream(stream), ctypes.byref(bits))
+    code = library().moe_sync_status(h.ref, _stream(stream, h.device_index), ctypes.byref(bits))
     if code == MOE_ERR_HIP or code == MOE_ERR_ARG:
         raise MoeError(code, "moe_sync_status")
     return code, bits.value
 
 
 def moe_reset(h: MoeA2A) -> None:
-    _check(library().moe_reset(ctypes.byref(h.handle)), "moe_reset")
+    _check(library().moe_reset(h.ref), "moe_reset")
 
 
 __all__ = [
