@@ -105,20 +105,21 @@ __device__ __forceinline__ void add_region_sums(int32_t *base, const int32_t *hi
     }
 }
 
-// Per-region layout, wave form: d is this lane's region (or -1) and j the
-// position of its copy within the token.  When k divides 64 and the items of
-// a wave are consecutive flat indices starting at a multiple of k, a token's
-// copies sit in consecutive lanes of one wave, so the earlier copies are the
-// j lanes below; every lane must call this (shuffles), k is uniform.
-__device__ __forceinline__ bool first_in_wave(int d, int j, int k) {
-    const int lane = threadIdx.x & 63;
-    bool first = true;
-    for (int jj = 1; jj < k; ++jj) {
-        const int other = __shfl(d, (lane - jj) & 63);
-        if (jj <= j && other == d) first = false;
+// Lanes of this wave bound for the same region as this lane (d >= 0), found
+// by intersecting one ballot per bit of the region number.  Every lane must
+// call this (ballots).
+__device__ __forceinline__ uint64_t region_group(int d, int region_bits) {
+    uint64_t same = __ballot(d >= 0);
+    for (int b = 0; b < region_bits; ++b) {
+        const bool bit = d >= 0 && ((d >> b) & 1);
+        const uint64_t m = __ballot(bit);
+        same &= bit ? m : ~m;
     }
-    return first;
+    return same;
 }
+
+// Lanes 0 .. n-1 of a wave.
+__device__ __forceinline__ uint64_t low_lanes(int n) { return n == 0 ? 0ull : ~0ull >> (64 - n); }
 
 // Per-region layout: true if no earlier copy of the same token (flat indices
 // token_base .. i-1) is bound for region d.  Reads the token's ids from L1/L2.
@@ -131,19 +132,31 @@ __device__ __forceinline__ bool first_to_region(const int32_t *ids, int64_t toke
     return true;
 }
 
-// Per-region layout: d if flat copy i is its token's first copy to region d,
-// else -1.  Called by every lane with uniform k; `active` lanes hold a copy.
-// Items are consecutive flat indices from a multiple of k (tiles of 256 from
-// a chunk start), so when k divides 64 the wave form applies.
+// The lanes a copy is ranked with: region_group of its region d.  Under the
+// per-region layout only a token's first copy to each region is ranked, so
+// later copies get d = -1 and leave every group.  A wave's items are
+// consecutive flat indices starting at a multiple of k (tiles of 256 from a
+// chunk start); when k divides 64 a token's copies are therefore the lanes
+// lane - lane % k .. lane, and a copy is first iff none of the earlier ones is
+// in its group (one more ballot then drops the later copies).  Otherwise the
+// token's earlier ids are re-read before grouping.  Called by every lane with
+// uniform k; `active` lanes hold a copy.
 template <typename Args>
-__device__ __forceinline__ int first_copy_region(const Args &a, int d, int64_t i, bool active) {
-    if (64 % a.k == 0) {
-        const bool first = first_in_wave(d, active ? (int)(i % a.k) : 0, a.k);
-        return first ? d : -1;
+__device__ __forceinline__ uint64_t rank_group(const Args &a, int &d, int64_t i, bool active,
+                                               int region_bits) {
+    const bool wave_form = a.per_region && 64 % a.k == 0;
+    if (a.per_region && !wave_form && active && d >= 0 &&
+        !first_to_region(a.ids, i - i % a.k, i, d, a.epr, a.n_experts))
+        d = -1;
+    uint64_t same = region_group(d, region_bits);
+    if (wave_form) {
+        const int lane = threadIdx.x & 63;
+        const uint64_t earlier = low_lanes(lane) & ~low_lanes(lane - lane % a.k);
+        const bool first = d >= 0 && (same & earlier) == 0;
+        same &= __ballot(first);
+        if (!first) d = -1;
     }
-    if (active && d >= 0 && !first_to_region(a.ids, i - i % a.k, i, d, a.epr, a.n_experts))
-        return -1;
-    return d;
+    return same;
 }
 
 // ---------------------------------------------------------------------------
@@ -151,10 +164,14 @@ __device__ __forceinline__ int first_copy_region(const Args &a, int d, int64_t i
 // Items of the chunk are taken 256 at a time (one per thread, flat order).
 // Under the per-region layout only a token's first copy to each region is
 // ranked (later copies share its row).
-// Within a wave, lanes with the same region are found by intersecting one
-// ballot per bit of the region number; a lane's rank is the number of such
-// lanes below it.  Per-wave counts go through LDS to give wave offsets, and a
-// per-region carry runs across tiles, so ranks follow the flat order f.
+// Within a wave, lanes with the same region are found with ballots
+// (rank_group); a lane's rank is the number of such lanes below it.  Per-wave
+// counts go through LDS to give wave offsets, and a per-region carry runs
+// across tiles, so ranks follow the flat order f.
+// The ids of kTileGroup tiles are loaded before the first of them is ranked
+// (clamped to the chunk, so the loads are unconditional and all in flight),
+// instead of one dependent load per tile after the previous tile's barriers.
+constexpr int kTileGroup = 4;
 __global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
     __shared__ int32_t wave_cnt[kWaves * MOE_MAX_EP];
     __shared__ int32_t carry[MOE_MAX_EP];
@@ -173,44 +190,47 @@ __global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
     for (int r = tid; r < ep; r += kThreads) carry[r] = 0;
     bool bad = false;
 
-    for (int64_t tile = begin; tile < end; tile += kThreads) {
-        for (int r = tid; r < kWaves * ep; r += kThreads) wave_cnt[r] = 0;
-        __syncthreads();
+    for (int64_t group = begin; group < end; group += kTileGroup * kThreads) {
+        int ids[kTileGroup];
+#pragma unroll
+        for (int g = 0; g < kTileGroup; ++g)       // end > begin: the chunk is never empty
+            ids[g] = a.ids[min(group + g * kThreads + tid, end - 1)];
+#pragma unroll
+        for (int g = 0; g < kTileGroup; ++g) {
+            const int64_t tile = group + g * kThreads;
+            if (tile >= end) break;                  // uniform
+            for (int r = tid; r < kWaves * ep; r += kThreads) wave_cnt[r] = 0;
+            __syncthreads();
 
-        const int64_t i = tile + tid;
-        int d = -1;
-        if (i < end) {
-            const int e = a.ids[i];
-            if (e >= 0 && e < a.n_experts)
-                d = e / a.epr;
-            else if (e != -1)
-                bad = true;
-        }
-        if (a.per_region)                        // later copies share the first copy's row
-            d = first_copy_region(a, d, i, i < end);
-        uint64_t same = __ballot(d >= 0);
-        for (int b = 0; b < region_bits; ++b) {
-            const bool bit = d >= 0 && ((d >> b) & 1);
-            const uint64_t m = __ballot(bit);
-            same &= bit ? m : ~m;
-        }
-        const int lane_rank = __popcll(same & below);
-        if (d >= 0 && (same >> lane) == 1ull)          // highest lane of its group
-            wave_cnt[wave * ep + d] = __popcll(same);
-        __syncthreads();
+            const int64_t i = tile + tid;
+            int d = -1;
+            if (i < end) {
+                const int e = ids[g];
+                if (e >= 0 && e < a.n_experts)
+                    d = e / a.epr;
+                else if (e != -1)
+                    bad = true;
+            }
+            const uint64_t same = a.per_region ? rank_group(a, d, i, i < end, region_bits)
+                                               : region_group(d, region_bits);
+            const int lane_rank = __popcll(same & below);
+            if (d >= 0 && (same >> lane) == 1ull)          // highest lane of its group
+                wave_cnt[wave * ep + d] = __popcll(same);
+            __syncthreads();
 
-        if (d >= 0) {
-            int off = carry[d];
-            for (int w = 0; w < wave; ++w) off += wave_cnt[w * ep + d];
-            a.rank[i] = off + lane_rank;
+            if (d >= 0) {
+                int off = carry[d];
+                for (int w = 0; w < wave; ++w) off += wave_cnt[w * ep + d];
+                a.rank[i] = off + lane_rank;
+            }
+            __syncthreads();
+            for (int r = tid; r < ep; r += kThreads) {
+                int add = 0;
+                for (int w = 0; w < kWaves; ++w) add += wave_cnt[w * ep + r];
+                carry[r] += add;
+            }
+            __syncthreads();
         }
-        __syncthreads();
-        for (int r = tid; r < ep; r += kThreads) {
-            int add = 0;
-            for (int w = 0; w < kWaves; ++w) add += wave_cnt[w * ep + r];
-            carry[r] += add;
-        }
-        __syncthreads();
     }
 
     if (bad) atomicOr(a.status, MOE_STATUS_EXPERT_ID);
@@ -456,13 +476,8 @@ __device__ __forceinline__ void count_regions(int32_t *cnt, const DispatchArgs &
             else if (e != -1)
                 *bad = true;
         }
-        if (a.per_region) d = first_copy_region(a, d, i, i < n);
-        uint64_t same = __ballot(d >= 0);
-        for (int b = 0; b < region_bits; ++b) {
-            const bool bit = d >= 0 && ((d >> b) & 1);
-            const uint64_t m = __ballot(bit);
-            same &= bit ? m : ~m;
-        }
+        const uint64_t same = a.per_region ? rank_group(a, d, i, i < n, region_bits)
+                                           : region_group(d, region_bits);
         if (d >= 0 && (same >> lane) == 1ull) atomicAdd(&cnt[d], __popcll(same));
     }
 }
