@@ -7,6 +7,10 @@ pointers and the current HIP stream, and turns return codes into exceptions.
 PyTorch provides device memory and streams.  There is no fallback: if the
 library is missing the import of the functions fails loudly.
 
+The per-call functions go through ``_moe_fast``, a small CPython extension
+linked to the same library that converts the arguments in C (ctypes costs
+more per call than a decode-sized launch); the rest use ctypes.
+
 Functions carry the C names:
 
   moe_dispatch, moe_dispatch_fp8, moe_combine, moe_combine_residual_rmsnorm, moe_route_counts,
@@ -18,13 +22,16 @@ and ``MoeA2A`` owns one ``moe_handle`` plus the device buffers it binds.
 from __future__ import annotations
 
 import ctypes
+import importlib
 import os
+import sysconfig
 from typing import Optional, Tuple
 
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(PKG, "libmoe_a2a.so")
+FAST_MODULE = os.path.join(PKG, "_moe_fast" + sysconfig.get_config_var("EXT_SUFFIX"))
 
 MOE_OK = 0
 MOE_ERR_ARG = -1
@@ -103,6 +110,24 @@ def library() -> ctypes.CDLL:
             fn.restype, fn.argtypes = res, args
         _lib = lib
     return _lib
+
+
+_fast_mod = None
+
+
+def _fast():
+    """The ``_moe_fast`` extension: the per-call entry points (dispatch,
+    dispatch_fp8, combine, combine_residual_rmsnorm, route_counts) with their
+    argument conversion in C, a few microseconds cheaper per call than ctypes.
+    It calls the same functions of the same loaded library."""
+    global _fast_mod
+    if _fast_mod is None:
+        library()                       # the library first: one copy, loaded by path
+        if not os.path.exists(FAST_MODULE):
+            raise RuntimeError(f"{FAST_MODULE} is missing: build it with "
+                               "`python -m combine_moe_dispatch_03_amd.build`")
+        _fast_mod = importlib.import_module(__name__ + "._moe_fast")
+    return _fast_mod
 
 
 # ---------------------------------------------------------------- helpers
@@ -194,7 +219,8 @@ class MoeA2A:
                             self.scratch.numel() * 4), "moe_init")
         self.device = dev
         self.device_index = dev.index if dev.index is not None else torch.cuda.current_device()
-        self.ref = ctypes.byref(self.handle)     # built once, passed on every call
+        self.ref = ctypes.byref(self.handle)     # built once, passed on ctypes calls
+        self.addr = ctypes.addressof(self.handle)  # passed to the _moe_fast calls
 
     # shapes
     @property
@@ -251,9 +277,8 @@ def moe_dispatch(h: MoeA2A, x: torch.Tensor, topk_ids: torch.Tensor,
     _need(x, "x", torch.bfloat16, shape=(T, h.hidden))
     _need(topk_ids, "topk_ids", torch.int32, shape=(T, h.top_k))
     _need(workspace, "workspace", torch.bfloat16, numel=h.workspace_numel)
-    _check(library().moe_dispatch(h.ref, _ptr(x), _ptr(topk_ids), T, runtime_max_tokens_per_rank,
-                                  _ptr(workspace), _stream(stream, h.device_index)),
-           "moe_dispatch")
+    _check(_fast().dispatch(h.addr, _ptr(x), _ptr(topk_ids), T, runtime_max_tokens_per_rank,
+                            _ptr(workspace), _stream(stream, h.device_index)), "moe_dispatch")
 
 
 def moe_dispatch_fp8(h: MoeA2A, x: torch.Tensor, topk_ids: torch.Tensor,
@@ -266,9 +291,9 @@ def moe_dispatch_fp8(h: MoeA2A, x: torch.Tensor, topk_ids: torch.Tensor,
     _need(topk_ids, "topk_ids", torch.int32, shape=(T, h.top_k))
     _need(workspace, "workspace", torch.uint8, numel=h.workspace_numel)
     _need(scales, "scales", torch.float32, numel=h.ep_size * h.cap)
-    _check(library().moe_dispatch_fp8(h.ref, _ptr(x), _ptr(topk_ids), T,
-                                      runtime_max_tokens_per_rank, _ptr(workspace), _ptr(scales),
-                                      _stream(stream, h.device_index)), "moe_dispatch_fp8")
+    _check(_fast().dispatch_fp8(h.addr, _ptr(x), _ptr(topk_ids), T, runtime_max_tokens_per_rank,
+                                _ptr(workspace), _ptr(scales), _stream(stream, h.device_index)),
+           "moe_dispatch_fp8")
 
 
 def moe_combine(h: MoeA2A, expert_out: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
@@ -283,9 +308,9 @@ def moe_combine(h: MoeA2A, expert_out: torch.Tensor, topk_weights: Optional[torc
     if out is None:
         out = torch.empty((T, h.hidden), dtype=torch.bfloat16, device=expert_out.device)
     _need(out, "out", torch.bfloat16, shape=(T, h.hidden))
-    _check(library().moe_combine(h.ref, _ptr(expert_out),
-                                 _ptr(topk_weights) if weighted else None, int(weighted),
-                                 _ptr(out), _stream(stream, h.device_index)), "moe_combine")
+    _check(_fast().combine(h.addr, _ptr(expert_out), _ptr(topk_weights) if weighted else None,
+                           int(weighted), _ptr(out), _stream(stream, h.device_index)),
+           "moe_combine")
     return out
 
 
@@ -310,8 +335,8 @@ def moe_combine_residual_rmsnorm(h: MoeA2A, expert_out: torch.Tensor,
         normed = torch.empty_like(residual)
     _need(residual_out, "residual_out", torch.bfloat16, shape=(T, H))
     _need(normed, "normed", torch.bfloat16, shape=(T, H))
-    _check(library().moe_combine_residual_rmsnorm(
-        h.ref, _ptr(expert_out), _ptr(topk_weights) if weighted else None,
+    _check(_fast().combine_residual_rmsnorm(
+        h.addr, _ptr(expert_out), _ptr(topk_weights) if weighted else None,
         int(bool(weighted)), _ptr(residual), _ptr(residual_out), _ptr(gamma), float(eps),
         _ptr(normed), _stream(stream, h.device_index)), "moe_combine_residual_rmsnorm")
     return residual_out, normed
@@ -321,8 +346,8 @@ def moe_route_counts(h: MoeA2A, topk_ids: torch.Tensor, stream=None) -> torch.Te
     """Per-region copy counts of a routing (for sizing max_tokens_per_rank)."""
     T = topk_ids.shape[0]
     _need(topk_ids, "topk_ids", torch.int32, shape=(T, h.top_k))
-    _check(library().moe_route_counts(h.ref, _ptr(topk_ids), T,
-                                      _stream(stream, h.device_index)), "moe_route_counts")
+    _check(_fast().route_counts(h.addr, _ptr(topk_ids), T, _stream(stream, h.device_index)),
+           "moe_route_counts")
     return h.counts
 
 

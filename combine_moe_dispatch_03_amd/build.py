@@ -1,4 +1,6 @@
-"""Build the gfx950 shared library ``libmoe_a2a.so`` in-tree with hipcc.
+"""Build the gfx950 shared library ``libmoe_a2a.so`` in-tree with hipcc, and
+the small CPython extension ``_moe_fast`` (per-call entry points with the
+argument conversion in C) against it with the host C compiler.
 
 Run ``python -m combine_moe_dispatch_03_amd.build`` (or call ``build()``).
 Compiles for gfx950 only.  Flags:
@@ -12,6 +14,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import sysconfig
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -20,6 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libmoe_a2a.so")
 SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.hip")]
 ARCH = "gfx950"
+FAST_SOURCE = os.path.join(CSRC, "pyfast.c")
+FAST_MODULE = os.path.join(PKG, "_moe_fast" + sysconfig.get_config_var("EXT_SUFFIX"))
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
@@ -48,7 +53,25 @@ def build(output: str = LIBRARY, verbose: bool = False) -> str:
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(tmp, output)
+    if output == LIBRARY:
+        build_fast(verbose)
     return output
+
+
+def build_fast(verbose: bool = False) -> str:
+    """The CPython extension, linked to the in-tree library (found at run time
+    next to the extension through its $ORIGIN run path)."""
+    tmp = FAST_MODULE + ".tmp"
+    cmd = [os.environ.get("CC", "gcc"), "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-Werror", "-I", sysconfig.get_paths()["include"], "-I", INCLUDE, "-o", tmp, FAST_SOURCE,
+           "-L", PKG, "-lmoe_a2a", "-Wl,-rpath,$ORIGIN"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("building _moe_fast failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, FAST_MODULE)
+    return FAST_MODULE
 
 
 if __name__ == "__main__":

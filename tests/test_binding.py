@@ -2,6 +2,9 @@
 on.  The checks run on every call, so they are one combined test on the
 common path with the messages built only on failure; these tests pin the
 messages and that nothing malformed slips through."""
+import ctypes
+import os
+
 import pytest
 import torch
 
@@ -55,3 +58,58 @@ def test_default_stream_is_torchs_current_stream():
     side.synchronize()
     want = (x.float() * 2).to(torch.bfloat16)             # both copies of a row, summed once
     assert torch.equal(out, want)
+
+
+FAKE = 0x100000   # aligned, never dereferenced by the host-side checks
+
+
+def fake_handle(k=2):
+    lib = moe.library()
+    h = moe.MoeHandle()
+    rc = lib.moe_init(ctypes.byref(h), 64, 128, k, 8, 4, 128, 0, FAKE, FAKE, FAKE, FAKE, FAKE,
+                      lib.moe_scratch_bytes(64, k, 4))
+    assert rc == moe.MOE_OK
+    return h
+
+
+def test_fast_module_is_the_in_tree_build():
+    fast = moe._fast()
+    assert os.path.samefile(fast.__file__, moe.FAST_MODULE)
+
+
+def test_fast_calls_reject_malformed_arguments():
+    fast = moe._fast()
+    with pytest.raises(TypeError, match="takes 7 arguments"):
+        fast.dispatch(0, 0, 0)
+    with pytest.raises(OverflowError):
+        fast.dispatch(ctypes.addressof(fake_handle()), FAKE, FAKE, 1 << 40, 1, FAKE, None)
+    with pytest.raises(TypeError):
+        fast.combine(ctypes.addressof(fake_handle()), "not a pointer", None, 0, FAKE, None)
+
+
+def test_fast_calls_return_the_library_codes():
+    # host-side rejections (no HIP call): the extension and ctypes give the same code
+    lib, fast = moe.library(), moe._fast()
+    cases = [
+        ("combine before dispatch", lambda h, a: fast.combine(a, FAKE, None, 0, FAKE, None),
+         lambda h: lib.moe_combine(ctypes.byref(h), FAKE, None, 0, FAKE, None)),
+        ("null workspace", lambda h, a: fast.dispatch(a, FAKE, FAKE, 8, 8, None, None),
+         lambda h: lib.moe_dispatch(ctypes.byref(h), FAKE, FAKE, 8, 8, None, None)),
+        ("rung above max_tokens", lambda h, a: fast.dispatch(a, FAKE, FAKE, 8, 65, FAKE, None),
+         lambda h: lib.moe_dispatch(ctypes.byref(h), FAKE, FAKE, 8, 65, FAKE, None)),
+        ("misaligned rows", lambda h, a: fast.dispatch(a, FAKE + 2, FAKE, 8, 8, FAKE, None),
+         lambda h: lib.moe_dispatch(ctypes.byref(h), FAKE + 2, FAKE, 8, 8, FAKE, None)),
+        ("fp8 null scales", lambda h, a: fast.dispatch_fp8(a, FAKE, FAKE, 8, 8, FAKE, None, None),
+         lambda h: lib.moe_dispatch_fp8(ctypes.byref(h), FAKE, FAKE, 8, 8, FAKE, None, None)),
+        ("fused before dispatch",
+         lambda h, a: fast.combine_residual_rmsnorm(a, FAKE, None, 0, FAKE, FAKE, FAKE, 1e-6, FAKE, None),
+         lambda h: lib.moe_combine_residual_rmsnorm(ctypes.byref(h), FAKE, None, 0, FAKE, FAKE, FAKE,
+                                                    1e-6, FAKE, None)),
+        ("route counts above max_tokens", lambda h, a: fast.route_counts(a, FAKE, 65, None),
+         lambda h: lib.moe_route_counts(ctypes.byref(h), FAKE, 65, None)),
+    ]
+    for name, via_fast, via_ctypes in cases:
+        h1, h2 = fake_handle(), fake_handle()
+        got = via_fast(h1, ctypes.addressof(h1))
+        want = via_ctypes(h2)
+        assert got == want != moe.MOE_OK, name
