@@ -14,6 +14,8 @@ oracle, and a seed sweep against it.
   twice or missed changes the sum.
 * Seeds 1-4 on the small workloads: dispatch bit-exact and combine (and the
   fused epilogue) within 1 ulp of the oracle.
+* The combine reads expert outputs from a buffer other than the dispatch
+  workspace and leaves the workspace as dispatched.
 """
 import numpy as np
 import pytest
@@ -133,3 +135,38 @@ def test_seed_sweep_against_oracle(name, seed):
         got = to_u16(moe.moe_combine(run.h, run.ws, w if weighted else None, weighted))
         want = orc.combine(ref.ws, ref.slot_index, inp.weights, weighted, wl.H)
         assert_bf16_close(got, want, f"{name} seed {seed} combine")
+
+
+@pytest.mark.parametrize("name", ["decode", "fused"])
+def test_combine_reads_a_separate_expert_output_buffer(name):
+    # expert_out need not be the dispatch workspace: the experts may write
+    # their outputs into a buffer of their own with the same [ep, cap, H]
+    # layout.  Its padding holds NaN, so a read outside the valid rows would
+    # poison the output; the dispatch workspace must be left as dispatched.
+    wl = synth.BY_NAME[name]
+    orc = oracle.load()
+    inp = synth.make_inputs(wl, 0)
+    cap = wl.cap
+    say("separate expert-output buffer", name)
+    ref = orc.dispatch(inp.x, inp.ids, wl.ep, wl.epr, cap)
+    y = synth.expert_outputs(wl, inp)
+    expert_stage_oracle(ref, y)
+    run = gpu_dispatch(inp.x, inp.ids, wl.E, wl.ep, cap, R=wl.R)
+    dispatched = run.ws.clone()
+    ybuf = run.h.new_workspace(CANARY)
+    slot = run.h.slot_index_view().reshape(-1).long()
+    valid = slot >= 0
+    ybuf.view(-1, wl.H)[slot[valid]] = to_dev_bf16(y)[valid]
+    w = to_dev(inp.weights)
+    if wl.combine == "fused":
+        want_r, want_n = orc.combine_residual_rmsnorm(ref.ws, ref.slot_index, inp.weights, True,
+                                                      inp.residual, inp.gamma, wl.eps)
+        r_out, normed = moe.moe_combine_residual_rmsnorm(
+            run.h, ybuf, w, True, to_dev_bf16(inp.residual), to_dev_bf16(inp.gamma), wl.eps)
+        assert_bf16_close(to_u16(r_out), want_r, "residual_out")
+        assert_bf16_close(to_u16(normed), want_n, "normed")
+    else:
+        got = to_u16(moe.moe_combine(run.h, ybuf, w, True))
+        assert_bf16_close(got, orc.combine(ref.ws, ref.slot_index, inp.weights, True, wl.H),
+                          f"{name} combine")
+    assert torch.equal(run.ws.view(torch.int16), dispatched.view(torch.int16))
