@@ -41,6 +41,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -52,9 +53,15 @@ PROFILE = os.path.join(ROOT, "profiles", "combine_prefill_counters.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "combine_moe_dispatch_03_amd", "csrc", "kernels.hip")
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()
+def kernel_source_hash(path: str = KERNEL_SOURCE) -> str:
+    """SHA-256 of the kernel source with comments removed and whitespace
+    collapsed: a counter summary stays valid across comment edits, and no
+    longer matches after any change to the code itself."""
+    with open(path) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
 def measured_traffic():
@@ -68,7 +75,7 @@ def measured_traffic():
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != kernel_source_hash():
+    if fields.get("kernel_code_sha256") != kernel_source_hash():
         return None
     try:
         return int(float(fields["hbm_bytes_per_launch"]))

@@ -1,7 +1,7 @@
 // gfx950 kernels of the MoE dispatch / combine path.
 //
 // Nothing here is a dense contraction, so nothing uses MFMA: the path is
-// bound by HBM bandwidth.  Three kernels:
+// bound by HBM bandwidth.  Four kernels:
 //
 //  route_rank_kernel     per chunk of tokens: each routed copy's rank among
 //                        the chunk's copies to the same region (a stable
@@ -10,6 +10,9 @@
 //                        (chunk prefix + rank), the index maps, and the
 //                        16-byte row copies x[t] -> workspace rows.  The
 //                        source row is read once and written k times.
+//  dispatch_small_kernel the whole dispatch in one launch for small batches
+//                        (decode): each block counts the earlier copies
+//                        itself instead of reading route_rank_kernel's output.
 //  combine_kernel        per token (x column block): gathers the k rows,
 //                        accumulates in fp32 in j order, narrows once to
 //                        bf16 (nearest-even); optionally adds the residual
@@ -239,13 +242,7 @@ __global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dispatch_copy_kernel<VPT, NT>: grid = (T, column blocks); each thread moves
-// VPT 16-byte vectors of the token's row, vector v of block cb at
-// (cb*VPT + v)*256 + tid, so every vector step is one coalesced 4 KB stripe.
-// The source loads are issued first (they do not depend on the slots) and
-// unconditionally (lanes past the row end re-read the row's last vector and
-// store nothing), so they are all in flight while the slots are computed.
-// NT marks the workspace stores non-temporal.
+// Dispatch helpers.
 // Rows of token t's copies from the region prefix `base` (copies of earlier
 // tokens) and each copy's rank after them; writes slot_index / src_index
 // (column block 0 only) and, in copy_rows, the rows this block must fill.
@@ -362,6 +359,14 @@ __device__ __forceinline__ void store_rows_fp8(const DispatchArgs &a, const u32x
     }
 }
 
+// dispatch_copy_kernel<VPT, NT, FP8>: grid = (T, column blocks); each thread
+// moves VPT 16-byte vectors of the token's row, vector v of block cb at
+// (cb*VPT + v)*256 + tid, so every vector step is one coalesced 4 KB stripe.
+// The source loads are issued first (they do not depend on the slots) and
+// unconditionally (lanes past the row end re-read the row's last vector and
+// store nothing), so they are all in flight while the slots are computed.
+// NT marks the workspace stores non-temporal; FP8 writes e4m3 codes and a
+// row scale instead of the bf16 row.
 template <int VPT, bool NT, bool FP8>
 __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a) {
     __shared__ int32_t base[MOE_MAX_EP];
@@ -442,16 +447,16 @@ __device__ __forceinline__ void accumulate(float (&acc)[VPT][8], const u32x4 (&r
 }
 
 // ---------------------------------------------------------------------------
-// dispatch_small_kernel<VPT, NT>: the whole dispatch in one launch, for
+// dispatch_small_kernel<VPT, NT, FP8>: the whole dispatch in one launch, for
 // batches of at most kSmallItems routed copies (decode).  Each block counts,
 // per region, the copies of all earlier tokens itself (at most kSmallItems
 // ids, read from L2), adds the rank among its own token's earlier copies,
 // and copies its row like dispatch_copy_kernel.  Block (0, 0) also counts
 // every copy for `counts` and flags bad ids.  Same stable slot order as the
 // two-kernel path: copies fill a region in increasing flat index.
-// Within a wave, lanes bound for the same region are grouped with one ballot
-// per bit of the region number (as in route_rank_kernel) so each group adds
-// its size to the LDS counter with one atomic.
+// Within a wave, lanes bound for the same region are grouped with ballots
+// (rank_group, as in route_rank_kernel) so each group adds its size to the
+// LDS counter with one atomic.
 static_assert(kSmallItems % kThreads == 0, "small-batch ids are split evenly over a block");
 __device__ __forceinline__ void count_regions(int32_t *cnt, const DispatchArgs &a, int64_t n,
                                               int region_bits, int tid, bool *bad) {
@@ -568,9 +573,10 @@ __device__ __forceinline__ void gather_group(float (&acc)[VPT][8], const uint16_
 // Wave 0 first compacts the token's valid copies (slot_index >= 0) into LDS,
 // keeping j order, so only rows holding valid copies are ever read (padding
 // rows never are).  Under the per-region layout a row named by an earlier
-// copy of the token is dropped: each region's message is added once.  Rows are then fetched JU at a time with every load of a
-// group issued before the first add, and no load under a branch (a branch
-// around a load makes the compiler wait for all outstanding loads).  Lanes
+// copy of the token is dropped: each region's message is added once.  Rows
+// are then fetched JU at a time with every load of a group issued before the
+// first add, and no load under a branch (a branch around a load makes the
+// compiler wait for all outstanding loads).  Lanes
 // past the end of the row load the row's last vector instead and store
 // nothing.  Adds run in j order, so the fp32 sum is the same sequence of
 // roundings for every layout.  NT marks the gathered rows non-temporal (each
@@ -627,7 +633,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     // every load of a group is issued before its first add (the scheduling
     // barrier keeps the compiler from sinking loads to their uses).
     int j0 = 0;
-    for (; j0 + JU <= nv; j0 += JU) gather_group<JU, VPT, WEIGHTED, NT>(acc, a.y, a.H, rows, gates, j0, off);
+    for (; j0 + JU <= nv; j0 += JU)
+        gather_group<JU, VPT, WEIGHTED, NT>(acc, a.y, a.H, rows, gates, j0, off);
     if (JU > 4 && j0 + 4 <= nv) {
         gather_group<4, VPT, WEIGHTED, NT>(acc, a.y, a.H, rows, gates, j0, off);
         j0 += 4;

@@ -1,0 +1,40 @@
+"""bench.py's host-side logic (CPU): the command-line contract for more than
+one GPU, and the kernel-code hash that decides whether the committed HBM
+counter summary still describes the kernels."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_code_hash_ignores_comments_and_whitespace_only(tmp_path):
+    src = open(bench.KERNEL_SOURCE).read()
+    base = bench.kernel_source_hash()
+    edited = tmp_path / "k.hip"
+    edited.write_text("// a new leading comment\n" + src.replace("\n", "\n\n", 5) + "\n/* tail */\n")
+    assert bench.kernel_source_hash(str(edited)) == base
+    changed = tmp_path / "k2.hip"
+    changed.write_text(src.replace("kThreads = 256", "kThreads = 512", 1))
+    assert "kThreads = 256" in src
+    assert bench.kernel_source_hash(str(changed)) != base
+
+
+def test_committed_counter_summary_is_plausible():
+    # null when the kernels changed since the counters were taken; otherwise
+    # the combine's HBM bytes sit near its algorithmic bytes
+    import synth
+    traffic = bench.measured_traffic()
+    if traffic is not None:
+        wl = synth.BY_NAME["prefill"]
+        algo = wl.T * (2 * wl.H * (wl.k + 1) + 8 * wl.k)
+        assert 0.9 * algo < traffic < 1.5 * algo
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode != 0
+    assert "one GPU" in (res.stdout + res.stderr)
