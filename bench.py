@@ -392,13 +392,34 @@ def calibrate_copy(nbytes: int, reps: int) -> None:
     print(json.dumps({"calibration_copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def shape_workload(spec: str):
+    """A workload of any shape: ``shape:T=4096,H=2048,E=128,k=8,ep=8`` with
+    optional ``routing=zipf1.2`` and ``combine=weighted|unweighted|fused``.
+    Every region gets as many rows as the routing sends it (cap from the
+    route counts), the rung is T, and the expert stage is the identity."""
+    import synth
+    fields = {}
+    for item in spec.split(":", 1)[1].split(","):
+        key, _, value = item.partition("=")
+        fields[key.strip()] = value.strip()
+    unknown = set(fields) - {"T", "H", "E", "k", "ep", "routing", "combine"}
+    if unknown or not {"T", "H", "E", "k", "ep"} <= set(fields):
+        raise SystemExit(f"bad shape {spec!r}: give T, H, E, k, ep (and optionally routing, combine)")
+    T, H, E, k, ep = (int(fields[n]) for n in ("T", "H", "E", "k", "ep"))
+    return synth.Workload(name="shape", T=T, H=H, E=E, k=k, ep=ep, cap=None, R=T,
+                          routing=fields.get("routing", "uniform"), expert="identity",
+                          combine=fields.get("combine", "unweighted"))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill",
-                    help="headline workload (a _region / _fp8 suffix selects a variant)")
+                    help="headline workload: tiny, decode, prefill, skewed, fused, or "
+                         "shape:T=..,H=..,E=..,k=..,ep=..[,routing=..][,combine=..]; a _region / "
+                         "_fp8 suffix selects a variant")
     ap.add_argument("--extras",
                     default="skewed,decode,fused,prefill_region,skewed_region,prefill_fp8,"
                             "prefill_region_fp8",
@@ -426,13 +447,17 @@ def main() -> int:
     def variant(name):
         """workload name with optional _region / _fp8 suffixes"""
         base, *mods = name.split("_")
-        return synth.BY_NAME[base], dict(layout="region" if "region" in mods else "copy",
-                                         payload="fp8" if "fp8" in mods else "bf16")
+        wl = shape_workload(base) if base.startswith("shape:") else synth.BY_NAME[base]
+        return wl, dict(layout="region" if "region" in mods else "copy",
+                        payload="fp8" if "fp8" in mods else "bf16")
 
     wl, opts = variant(args.workload)
     main_res = measure(wl, args.steps, args.warmup, args.cold_iters, **opts)
     extras = {}
-    for name in [n for n in args.extras.split(",") if n and n != args.workload]:
+    # workload names are comma-separated; a shape spec has commas of its own,
+    # so split only where the next workload's name begins
+    names = re.split(r",(?=(?:tiny|decode|prefill|skewed|fused|shape:))", args.extras)
+    for name in [n for n in names if n and n != args.workload]:
         ewl, eopts = variant(name)
         extras[name] = measure(ewl, max(args.steps // 2, 5), max(args.warmup // 2, 2),
                                args.cold_iters, graph=ewl.name == "decode", **eopts)
@@ -452,7 +477,7 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 tokens, uniform distinct top-8 routing)",
+        "data": f"synthetic (seeded N(0,1) bf16 tokens, {wl.routing} distinct top-{wl.k} routing)",
         "config": {"workload": main_res["workload"], "tokens": wl.T, "hidden": wl.H,
                    "top_k": wl.k, "experts": wl.E, "ep_size": wl.ep,
                    "step": "dispatch -> identity expert stage -> combine"},
@@ -460,7 +485,9 @@ def main() -> int:
         "hbm_frac": main_res["step_hbm_frac"],
         "roofline": {"bound": "hbm", "kernel": "combine_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(),
+                     # the committed counters describe the prefill combine only
+                     "traffic": measured_traffic() if (wl.name, opts["layout"], opts["payload"])
+                     == ("prefill", "copy", "bf16") else None,
                      "algorithmic_bytes_per_launch": main_res["combine_bytes"],
                      "launch_ms_mean": comb_ms},
         "kernels": {"dispatch_ms_mean": main_res["dispatch_ms_mean"],

@@ -38,3 +38,17 @@ def test_more_than_one_gpu_exits_with_a_message():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode != 0
     assert "one GPU" in (res.stdout + res.stderr)
+
+
+def test_shape_workloads_parse():
+    wl = bench.shape_workload("shape:T=4096,H=2048,E=128,k=8,ep=8")
+    assert (wl.T, wl.H, wl.E, wl.k, wl.ep, wl.R, wl.cap) == (4096, 2048, 128, 8, 8, 4096, None)
+    assert wl.routing == "uniform" and wl.combine == "unweighted" and wl.expert == "identity"
+    wl = bench.shape_workload("shape:T=64,H=128,E=8,k=2,ep=4,routing=zipf1.2,combine=weighted")
+    assert wl.routing == "zipf1.2" and wl.combine == "weighted"
+    for bad in ("shape:T=64,H=128", "shape:T=64,H=128,E=8,k=2,ep=4,colour=blue"):
+        try:
+            bench.shape_workload(bad)
+        except SystemExit:
+            continue
+        raise AssertionError(f"{bad} accepted")
