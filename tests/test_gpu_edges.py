@@ -66,7 +66,7 @@ def roundtrip(x, ids, w, y, E, ep, cap, R=None, fused=False, eps=1e-6, seed=0):
     return run
 
 
-@pytest.mark.parametrize("case", [
+ROUNDTRIP_CASES = [
     # (name, T, H, k, E, ep)
     ("ragged_rows_and_vectors", 37, 136, 3, 12, 4),
     ("one_vector_rows", 5, 8, 2, 4, 2),
@@ -79,7 +79,13 @@ def roundtrip(x, ids, w, y, E, ep, cap, R=None, fused=False, eps=1e-6, seed=0):
     ("many_chunks_ragged", 4099, 24, 6, 36, 6),
     ("single_launch_limit", 256, 128, 8, 64, 8),     # 2048 copies: one-launch dispatch
     ("two_kernel_threshold", 257, 128, 8, 64, 8),    # 2056 copies: routing kernel + copy
-])
+    # the routing kernel loads its chunk's ids 4 tiles of 256 at a time:
+    ("full_and_partial_tile_group", 9000, 16, 8, 64, 8),   # 1128 copies per chunk: 4 + 1 tiles
+    ("five_tile_groups", 40000, 8, 8, 64, 8),              # 5000 copies per chunk: 20 tiles
+]
+
+
+@pytest.mark.parametrize("case", ROUNDTRIP_CASES, ids=[c[0] for c in ROUNDTRIP_CASES])
 def test_roundtrip_shapes(case):
     name, T, H, k, E, ep = case
     say("roundtrip", name, T, H, k, E, ep)

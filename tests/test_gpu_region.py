@@ -67,7 +67,7 @@ def test_region_layout_full_size(name):
         assert abs(per_token - 5.2947) < 0.05
 
 
-@pytest.mark.parametrize("case", [
+REGION_EDGE_CASES = [
     # (name, T, H, k, E, ep, p_missing)
     ("duplicates_and_gaps", 61, 136, 6, 12, 4, 0.15),
     ("one_region", 17, 64, 4, 8, 1, 0.0),
@@ -75,7 +75,12 @@ def test_region_layout_full_size(name):
     ("wide_rows", 5, 16384, 8, 32, 4, 0.1),
     ("two_kernel_path", 1200, 64, 8, 64, 8, 0.05),
     ("max_topk", 24, 64, 64, 512, 256, 0.0),
-])
+    ("tile_groups_wave_form", 9000, 16, 8, 64, 8, 0.05),     # k divides 64: ballot test
+    ("tile_groups_k6", 12000, 16, 6, 36, 6, 0.05),           # k = 6: ids re-read
+]
+
+
+@pytest.mark.parametrize("case", REGION_EDGE_CASES, ids=[c[0] for c in REGION_EDGE_CASES])
 def test_region_layout_edges(case):
     name, T, H, k, E, ep, pm = case
     say("region edge", name)
