@@ -47,7 +47,8 @@ int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
              int32_t *status, void *scratch, size_t scratch_bytes) {
     if (h == nullptr) return MOE_ERR_ARG;
     if (layout != MOE_LAYOUT_PER_COPY && layout != MOE_LAYOUT_PER_REGION) return MOE_ERR_ARG;
-    if (max_tokens < 1 || hidden < 8 || hidden % 8 != 0) return MOE_ERR_ARG;
+    if (max_tokens < 1 || hidden < 8 || hidden > MOE_MAX_HIDDEN || hidden % 8 != 0)
+        return MOE_ERR_ARG;
     if (top_k < 1 || top_k > MOE_MAX_TOP_K) return MOE_ERR_ARG;
     if (ep_size < 1 || ep_size > MOE_MAX_EP) return MOE_ERR_ARG;
     if (num_experts < ep_size || num_experts % ep_size != 0) return MOE_ERR_ARG;

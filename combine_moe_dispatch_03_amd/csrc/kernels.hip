@@ -38,11 +38,15 @@ namespace {
 
 constexpr int kThreads = 256;            // 4 wave64 per workgroup
 constexpr int kWaves = kThreads / 64;
-// Combine outputs (out, residual_out, normed) stored non-temporally: each
-// row is written once here and read by the next layer, not by this kernel
-// (measured at the prefill shape: combine 91.9 -> 89.6 us, and 102 -> 90 us
-// with a cold Infinity Cache).
-constexpr bool kOutNT = true;
+// Cache policy of the combine's output stores (out, residual_out, normed):
+// each row is written once here and read by the next layer, not by this
+// kernel.  The policy bits of a gfx950 vector memory instruction are sc0 = 1,
+// nt = 2, sc1 = 16.  Measured at the prefill shape (combine after a dispatch):
+// plain stores 91.8 us, non-temporal 90.1 us, sc1 86.0-86.6 us; the gathered
+// loads stay non-temporal (every policy with nt measured the same, the others
+// 5 us slower), and so do the dispatch's workspace stores (sc1 there is 10 %
+// slower).
+constexpr int kOutPolicy = 16;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -83,12 +87,15 @@ __device__ __forceinline__ void store16(uint16_t *p, const u32x4 &v) {
     *reinterpret_cast<u32x4 *>(p) = v;
 }
 
-template <bool NT>
-__device__ __forceinline__ void store_out16(uint16_t *p, const u32x4 &v) {
-    if (NT)
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-    else
-        *reinterpret_cast<u32x4 *>(p) = v;
+// A buffer resource over one output row of H bf16 values (raw addressing,
+// the gfx9 default data format word); `row` is uniform across the wave.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(uint16_t *row, int H) {
+    return __builtin_amdgcn_make_buffer_rsrc(row, 0, H * (int)sizeof(uint16_t), 0x00020000);
+}
+
+// 16-byte store of element offset `off` of an output row, with kOutPolicy.
+__device__ __forceinline__ void store_out16(__amdgpu_buffer_rsrc_t row, int64_t off, const u32x4 &v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, row, (int)(off * sizeof(uint16_t)), 0, kOutPolicy);
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -649,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     if constexpr (!FUSED) {
 #pragma unroll
         for (int q = 0; q < VPT; ++q)
-            if (col[q] < vpr) store_out16<kOutNT>(a.out + row_off + off[q], pack8(acc[q]));
+            if (col[q] < vpr) store_out16(row_rsrc(a.out + row_off, a.H), off[q], pack8(acc[q]));
         return;
     } else {
         // s = sum + residual (fp32); residual_out = bf16(s); sum of squares.
@@ -666,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
             if (col[q] < vpr) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(acc[q][e], acc[q][e], ss);
-                store_out16<kOutNT>(a.residual_out + row_off + off[q], pack8(acc[q]));
+                store_out16(row_rsrc(a.residual_out + row_off, a.H), off[q], pack8(acc[q]));
             }
         }
 #pragma unroll
@@ -687,7 +694,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
             unpack8(gv[q], g);
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[q][e] = (acc[q][e] * inv) * g[e];
-            store_out16<kOutNT>(a.normed + row_off + off[q], pack8(acc[q]));
+            store_out16(row_rsrc(a.normed + row_off, a.H), off[q], pack8(acc[q]));
         }
     }
 }

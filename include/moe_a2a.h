@@ -74,6 +74,7 @@ extern "C" {
 #define MOE_MAX_EP          256     /* destination regions                     */
 #define MOE_MAX_TOP_K        64     /* routed copies per token                 */
 #define MOE_MAX_FUSED_HIDDEN 16384  /* hidden size of the fused epilogue       */
+#define MOE_MAX_HIDDEN     1048576  /* hidden size (a row stays under 2^31 B)  */
 
 /*
  * moe_handle -- host memory, owned by the caller.  Filled by moe_init; the
@@ -118,7 +119,7 @@ size_t moe_scratch_bytes(int32_t max_tokens, int32_t top_k, int32_t ep_size);
  * the ladder maximum.
  *   h                    host, caller-owned; overwritten
  *   max_tokens           >= 1, largest T any dispatch may pass
- *   hidden               >= 8 and a multiple of 8
+ *   hidden               8 .. MOE_MAX_HIDDEN, a multiple of 8
  *   top_k                1 .. MOE_MAX_TOP_K
  *   num_experts          multiple of ep_size
  *   ep_size              1 .. MOE_MAX_EP
