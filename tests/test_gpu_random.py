@@ -6,18 +6,19 @@ top-12, 1 to 16 regions of 1 to 8 experts, both layouts, unrouted copies and
 repeated experts, and now and then a capacity too small for the routing (an
 overflow: reported, the copies past capacity dropped).  Dispatch must match
 bit for bit and the combine (weighted for the per-copy layout, the
-per-region rank-sum otherwise) within 1 bf16 ulp.
+per-region rank-sum otherwise) within 1 bf16 ulp.  Twenty more cases run
+the fused residual + RMSNorm epilogue and twenty the FP8 payload (codes and
+scales bit-exact).
 """
 import numpy as np
 import pytest
-import torch
 
 import combine_moe_dispatch_03_amd as moe
 import oracle
 import pins
 import synth
 from gpu_harness import (assert_bf16_close, check_dispatch, expert_stage_gpu, expert_stage_gpu_by_row,
-                         expert_stage_oracle, gpu_dispatch, say, to_dev, to_u16)
+                         expert_stage_oracle, gpu_dispatch, say, to_dev, to_dev_bf16, to_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -65,3 +66,33 @@ def test_random_shape_against_oracle(seed):
         want = orc.combine(ref.ws, ref.slot_index, None, False, H, layout="region")
     assert_bf16_close(to_u16(got), want, f"random case {seed} combine")
     assert run.h.handle.phase == 0
+
+
+@pytest.mark.parametrize("seed", range(40, 60))
+def test_random_shape_fused_epilogue(seed):
+    c = draw_case(seed)
+    T, H, k, E, ep, epr, cap = c["T"], c["H"], c["k"], c["E"], c["ep"], c["epr"], c["cap"]
+    say("random fused case", seed, {n: c[n] for n in ("T", "H", "k", "E", "ep", "cap")})
+    rng = np.random.default_rng(seed)
+    res = pins.random_bf16(rng, (T, H))
+    gamma = pins.torch_bf16_bits(rng.uniform(0.5, 1.5, H).astype(np.float32))
+    orc = oracle.load()
+    ref = orc.dispatch(c["x"], c["ids"], ep, epr, cap)
+    run = gpu_dispatch(c["x"], c["ids"], E, ep, cap, R=max(T, 1), max_tokens=max(T, 1))
+    assert run.bits == ref.status
+    expert_stage_oracle(ref, c["y"])
+    expert_stage_gpu(run, c["y"])
+    r_out, normed = moe.moe_combine_residual_rmsnorm(run.h, run.ws, to_dev(c["w"]), True,
+                                                     to_dev_bf16(res), to_dev_bf16(gamma), 1e-6)
+    want_r, want_n = orc.combine_residual_rmsnorm(ref.ws, ref.slot_index, c["w"], True, res,
+                                                  gamma, 1e-6)
+    assert_bf16_close(to_u16(r_out), want_r, "residual_out")
+    assert_bf16_close(to_u16(normed), want_n, "normed")
+
+
+@pytest.mark.parametrize("seed", range(60, 80))
+def test_random_shape_fp8_dispatch(seed):
+    from test_gpu_fp8 import fp8_check
+    c = draw_case(seed)
+    say("random fp8 case", seed, {n: c[n] for n in ("T", "H", "k", "E", "ep", "layout", "cap")})
+    fp8_check(c["x"], c["ids"], c["E"], c["ep"], c["cap"], R=max(c["T"], 1), layout=c["layout"])
