@@ -440,7 +440,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build's workload runs on one GPU's share "
+        print("bench.py measures one GPU: the library runs the exchange on one GPU "
               "(the destination regions are partitions of local HBM); --gpus must be 1.",
               file=sys.stderr)
         return 2
