@@ -734,10 +734,15 @@ int column_blocks(int32_t H, int vpt) {
 // keep the register count near 200.
 constexpr bool kCopyNT = true;
 constexpr bool kCombineNT = true;
-// The fused epilogue keeps the residual and gamma in registers too; groups of
-// 4 rows measured best for it (6.23 vs 6.07 TB/s with 8).
-template <int VPT, bool FUSED> constexpr int combine_group() {
-    return (FUSED || VPT >= 8) ? 4 : 8;
+// Rows per gather group.  Eight is best only for the plain per-copy combine
+// with more than four rows per token; everywhere else groups of 4 measured
+// better: the fused epilogue keeps the residual and gamma in registers too
+// (6.23 vs 6.07 TB/s with 8), and with few rows per token (top-k <= 4, or
+// the per-region layout's ~5.3 distinct rows at top-8) the smaller register
+// footprint lets more waves run (T = 4096, H = 7168: top-2 33.4 -> 31.3 us,
+// top-4 49.9 -> 48.4 us, per-region top-8 65.2 -> 62.8 us).
+int combine_group(int vpt, bool fused, const CombineArgs &a) {
+    return (fused || vpt >= 8 || a.k <= 4 || a.per_region) ? 4 : 8;
 }
 
 template <int VPT, bool FP8>
@@ -758,15 +763,25 @@ void launch_copy(const DispatchArgs &a, int vpt, dim3 grid, hipStream_t s, bool 
     }
 }
 
-template <int VPT, bool FUSED>
-void launch_combine_vpt(const CombineArgs &a, dim3 grid, hipStream_t s) {
-    constexpr int JU = combine_group<VPT, FUSED>();
+template <int VPT, int JU, bool FUSED>
+void launch_combine_group(const CombineArgs &a, dim3 grid, hipStream_t s) {
     if (a.weighted)
         hipLaunchKernelGGL((combine_kernel<VPT, JU, true, FUSED, kCombineNT>), grid,
                            dim3(kThreads), 0, s, a);
     else
         hipLaunchKernelGGL((combine_kernel<VPT, JU, false, FUSED, kCombineNT>), grid,
                            dim3(kThreads), 0, s, a);
+}
+
+template <int VPT, bool FUSED>
+void launch_combine_vpt(const CombineArgs &a, dim3 grid, hipStream_t s) {
+    if constexpr (!FUSED && VPT < 8) {
+        if (combine_group(VPT, FUSED, a) == 8) {
+            launch_combine_group<VPT, 8, FUSED>(a, grid, s);
+            return;
+        }
+    }
+    launch_combine_group<VPT, 4, FUSED>(a, grid, s);
 }
 
 }  // namespace
