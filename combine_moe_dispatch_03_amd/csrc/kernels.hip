@@ -42,11 +42,19 @@ constexpr int kWaves = kThreads / 64;
 // each row is written once here and read by the next layer, not by this
 // kernel.  The policy bits of a gfx950 vector memory instruction are sc0 = 1,
 // nt = 2, sc1 = 16.  Measured at the prefill shape (combine after a dispatch):
-// plain stores 91.8 us, non-temporal 90.1 us, sc1 86.0-86.6 us; the gathered
-// loads stay non-temporal (every policy with nt measured the same, the others
-// 5 us slower), and so do the dispatch's workspace stores (sc1 there is 10 %
-// slower).
-constexpr int kOutPolicy = 16;
+// plain stores 91.8 us, non-temporal 90.1 us, sc1 86.0-86.6 us.  With sc1 the
+// rows stay in the 256 MB Infinity Cache, which only pays while a launch's
+// outputs fit there beside the rest of the step: at H = 7168, top-8, a step
+// (dispatch + combine) gains 4-8 us up to T = 8192 (117 MB of output) but
+// loses 35-85 us from T = 10240 (147 MB) on, because the next kernel pays for
+// writing the rows back (dispatch 230 -> 268 us at T = 10240).  So outputs up
+// to kOutCachedBytes per launch are stored with sc1 and larger ones
+// non-temporally.  The gathered loads stay non-temporal (every policy with nt
+// measured the same, the others 5 us slower), and so do the dispatch's
+// workspace stores (sc1 there is 10 % slower).
+constexpr int kPolicyNT = 2;
+constexpr int kPolicySC1 = 16;
+constexpr int64_t kOutCachedBytes = int64_t(120) << 20;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -93,9 +101,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(uint16_t *row, int H)
     return __builtin_amdgcn_make_buffer_rsrc(row, 0, H * (int)sizeof(uint16_t), 0x00020000);
 }
 
-// 16-byte store of element offset `off` of an output row, with kOutPolicy.
-__device__ __forceinline__ void store_out16(__amdgpu_buffer_rsrc_t row, int64_t off, const u32x4 &v) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, row, (int)(off * sizeof(uint16_t)), 0, kOutPolicy);
+// 16-byte store of element offset `off` of an output row; `cached` (uniform
+// across the launch) selects sc1 over non-temporal.
+__device__ __forceinline__ void store_out16(__amdgpu_buffer_rsrc_t row, int64_t off, const u32x4 &v,
+                                            bool cached) {
+    const int byte_off = (int)(off * sizeof(uint16_t));
+    if (cached)
+        __builtin_amdgcn_raw_buffer_store_b128(v, row, byte_off, 0, kPolicySC1);
+    else
+        __builtin_amdgcn_raw_buffer_store_b128(v, row, byte_off, 0, kPolicyNT);
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -653,10 +667,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     if (j0 < nv) gather_group<1, VPT, WEIGHTED, NT>(acc, a.y, a.H, rows, gates, j0, off);
 
     const int64_t row_off = (int64_t)t * a.H;
+    const bool cached = a.out_cached != 0;
     if constexpr (!FUSED) {
 #pragma unroll
         for (int q = 0; q < VPT; ++q)
-            if (col[q] < vpr) store_out16(row_rsrc(a.out + row_off, a.H), off[q], pack8(acc[q]));
+            if (col[q] < vpr) store_out16(row_rsrc(a.out + row_off, a.H), off[q], pack8(acc[q]), cached);
         return;
     } else {
         // s = sum + residual (fp32); residual_out = bf16(s); sum of squares.
@@ -673,7 +688,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
             if (col[q] < vpr) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(acc[q][e], acc[q][e], ss);
-                store_out16(row_rsrc(a.residual_out + row_off, a.H), off[q], pack8(acc[q]));
+                store_out16(row_rsrc(a.residual_out + row_off, a.H), off[q], pack8(acc[q]), cached);
             }
         }
 #pragma unroll
@@ -694,7 +709,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
             unpack8(gv[q], g);
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[q][e] = (acc[q][e] * inv) * g[e];
-            store_out16(row_rsrc(a.normed + row_off, a.H), off[q], pack8(acc[q]));
+            store_out16(row_rsrc(a.normed + row_off, a.H), off[q], pack8(acc[q]), cached);
         }
     }
 }
@@ -816,8 +831,11 @@ hipError_t launch_dispatch_copy(const DispatchArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineArgs &a, bool fused, hipStream_t s) {
-    if (a.T == 0) return hipSuccess;
+hipError_t launch_combine(const CombineArgs &args, bool fused, hipStream_t s) {
+    if (args.T == 0) return hipSuccess;
+    CombineArgs a = args;
+    const int64_t out_bytes = (int64_t)a.T * a.H * (int64_t)sizeof(uint16_t) * (fused ? 2 : 1);
+    a.out_cached = out_bytes <= kOutCachedBytes;
     const int vpt = fused ? full_row_vpt(a.H) : streaming_vpt(a.T, a.H);
     const dim3 grid(a.T, fused ? 1 : column_blocks(a.H, vpt));
     if (fused) {

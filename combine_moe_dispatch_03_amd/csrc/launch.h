@@ -76,6 +76,7 @@ struct CombineArgs {
     float eps;
     int32_t T, H, k, weighted;
     int32_t per_region;      // 1: add each distinct row of a token once
+    int32_t out_cached;      // set by launch_combine: output store cache policy (see kernels.hip)
 };
 
 hipError_t launch_route(const RouteArgs &a, int32_t n_chunks, hipStream_t s);

@@ -264,3 +264,19 @@ def test_page_staged_sum_on_gpu():
     assert (out == pins.exact_bits(float(g["expected"][0][0]))).all()
     # the missing region's row was never written and never read
     assert bool((run.ws[3].view(torch.int16) == CANARY).all())
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["combine", "fused"])
+def test_outputs_past_the_cached_store_limit(fused):
+    # launches writing more than 120 MiB of output use non-temporal stores
+    # instead of cache-resident ones: T * H * 2 bytes (twice that when fused)
+    T = 4608 if fused else 9216
+    H, k, E, ep = 7168, 2, 16, 4
+    assert T * H * 2 * (2 if fused else 1) > 120 << 20
+    say("outputs past the cached-store limit", "fused" if fused else "combine", T)
+    rng = np.random.default_rng(77)
+    x = pins.random_bf16(rng, (T, H))
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    y = pins.random_bf16(rng, (T * k, H))
+    roundtrip(x, ids, w, y, E, ep, cap=T * k, fused=fused)
