@@ -16,6 +16,8 @@ oracle, and a seed sweep against it.
   fused epilogue) within 1 ulp of the oracle.
 * The combine reads expert outputs from a buffer other than the dispatch
   workspace and leaves the workspace as dispatched.
+* Two handles driven on two streams at once give the same bytes as each
+  driven alone (no state outside a handle).
 """
 import numpy as np
 import pytest
@@ -170,3 +172,39 @@ def test_combine_reads_a_separate_expert_output_buffer(name):
         assert_bf16_close(got, orc.combine(ref.ws, ref.slot_index, inp.weights, True, wl.H),
                           f"{name} combine")
     assert torch.equal(run.ws.view(torch.int16), dispatched.view(torch.int16))
+
+
+def test_two_handles_on_two_streams():
+    # the library keeps no state outside a handle and its buffers: two
+    # handles driven on two streams at once give the same bytes as each
+    # driven alone
+    wl = synth.BY_NAME["fused"]
+    inp = synth.make_inputs(wl, 5)
+    say("two handles on two streams")
+    x, ids, w = to_dev_bf16(inp.x), to_dev(inp.ids), to_dev(inp.weights)
+    ids2 = torch.flip(ids, dims=[0]).contiguous()
+
+    def make():
+        h = moe.MoeA2A(wl.T, wl.H, wl.k, wl.E, wl.ep, wl.cap)
+        return h, h.new_workspace(0), torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+
+    def run(h, ws, out, ids_, stream):
+        moe.moe_dispatch(h, x, ids_, wl.R, ws, stream=stream)
+        moe.moe_combine(h, ws, w, True, out=out, stream=stream)
+
+    (h1, ws1, o1), (h2, ws2, o2) = make(), make()
+    cur = torch.cuda.current_stream()
+    run(h1, ws1, o1, ids, cur)
+    run(h2, ws2, o2, ids2, cur)
+    torch.cuda.synchronize()
+    want1, want2 = o1.clone(), o2.clone()
+    o1.zero_(); o2.zero_()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(cur); s2.wait_stream(cur)
+    for _ in range(3):
+        run(h1, ws1, o1, ids, s1)
+        run(h2, ws2, o2, ids2, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), want1.view(torch.int16))
+    assert torch.equal(o2.view(torch.int16), want2.view(torch.int16))
+    assert moe.moe_sync_status(h1)[0] == moe.MOE_OK and moe.moe_sync_status(h2)[0] == moe.MOE_OK
