@@ -280,3 +280,51 @@ def test_outputs_past_the_cached_store_limit(fused):
     w = rng.random((T, k)).astype(np.float32)
     y = pins.random_bf16(rng, (T * k, H))
     roundtrip(x, ids, w, y, E, ep, cap=T * k, fused=fused)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["combine", "fused"])
+def test_nonfinite_expert_outputs_propagate(fused):
+    # NaN and +-Inf entries in the expert outputs propagate as IEEE arithmetic
+    # says on both sides (Inf - Inf and 0 * Inf give NaN; an Inf in a row
+    # makes the RMSNorm of that row 0 or NaN).  Where either output is NaN
+    # both must be (NaN bits may differ: the sign of a NaN produced by
+    # arithmetic is unspecified); everything else within 1 ulp.
+    from oracle import compare
+    T, H, k, E, ep = 64, 256, 4, 16, 4
+    rng = np.random.default_rng(91)
+    x = pins.random_bf16(rng, (T, H))
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    w[::7, 0] = 0.0                                  # 0 * Inf where an Inf lands there
+    y = pins.random_bf16(rng, (T * k, H))
+    for bits, share in ((0x7FC0, 0.002), (0x7F80, 0.003), (0xFF80, 0.003)):
+        y[rng.random(y.shape) < share] = bits
+    say("non-finite expert outputs", "fused" if fused else "combine")
+    orc = oracle.load()
+    ref = orc.dispatch(x, ids, ep, E // ep, T * k)
+    expert_stage_oracle(ref, y)
+
+    def close(got, want, what):
+        gn, wn = compare.is_nan_bits(got), compare.is_nan_bits(want)
+        assert np.array_equal(gn, wn), f"{what}: NaN positions differ ({int(gn.sum())} vs {int(wn.sum())})"
+        d = compare.ulp_distance(np.where(gn, 0, got).astype(np.uint16), np.where(wn, 0, want).astype(np.uint16))
+        assert int(d.max()) <= 1, f"{what}: {int(d.max())} ulp"
+        return int(gn.sum())
+
+    for weighted in (False, True):
+        run = gpu_dispatch(x, ids, E, ep, T * k)
+        expert_stage_gpu(run, y)
+        if fused:
+            res = pins.random_bf16(rng, (T, H))
+            gamma = pins.torch_bf16_bits(rng.uniform(0.5, 1.5, H).astype(np.float32))
+            r_out, normed = moe.moe_combine_residual_rmsnorm(
+                run.h, run.ws, to_dev(w) if weighted else None, weighted, to_dev_bf16(res),
+                to_dev_bf16(gamma), 1e-6)
+            want_r, want_n = orc.combine_residual_rmsnorm(ref.ws, ref.slot_index, w, weighted, res,
+                                                          gamma, 1e-6)
+            close(to_u16(r_out), want_r, "residual_out")
+            n = close(to_u16(normed), want_n, "normed")
+        else:
+            got = to_u16(moe.moe_combine(run.h, run.ws, to_dev(w) if weighted else None, weighted))
+            n = close(got, orc.combine(ref.ws, ref.slot_index, w, weighted, H), "combine")
+        assert n > 0                                  # the case does produce NaNs
