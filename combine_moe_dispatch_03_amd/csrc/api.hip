@@ -33,7 +33,8 @@ size_t moe_workspace_bytes(int32_t ep_size, int32_t max_tokens_per_rank, int32_t
 }
 
 size_t moe_scratch_bytes(int32_t max_tokens, int32_t top_k, int32_t ep_size) {
-    if (max_tokens < 1 || top_k < 1 || top_k > MOE_MAX_TOP_K || ep_size < 1 || ep_size > MOE_MAX_EP)
+    if (max_tokens < 1 || max_tokens > MOE_MAX_TOKENS || top_k < 1 || top_k > MOE_MAX_TOP_K ||
+        ep_size < 1 || ep_size > MOE_MAX_EP)
         return 0;
     const int64_t items = (int64_t)max_tokens * top_k;
     if (items > INT32_MAX) return 0;
@@ -47,7 +48,9 @@ int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
              int32_t *status, void *scratch, size_t scratch_bytes) {
     if (h == nullptr) return MOE_ERR_ARG;
     if (layout != MOE_LAYOUT_PER_COPY && layout != MOE_LAYOUT_PER_REGION) return MOE_ERR_ARG;
-    if (max_tokens < 1 || hidden < 8 || hidden > MOE_MAX_HIDDEN || hidden % 8 != 0)
+    if (max_tokens < 1 || max_tokens > MOE_MAX_TOKENS)
+        return MOE_ERR_ARG;
+    if (hidden < 8 || hidden > MOE_MAX_HIDDEN || hidden % 8 != 0)
         return MOE_ERR_ARG;
     if (top_k < 1 || top_k > MOE_MAX_TOP_K) return MOE_ERR_ARG;
     if (ep_size < 1 || ep_size > MOE_MAX_EP) return MOE_ERR_ARG;

@@ -75,6 +75,8 @@ extern "C" {
 #define MOE_MAX_TOP_K        64     /* routed copies per token                 */
 #define MOE_MAX_FUSED_HIDDEN 16384  /* hidden size of the fused epilogue       */
 #define MOE_MAX_HIDDEN     1048576  /* hidden size (a row stays under 2^31 B)  */
+#define MOE_MAX_TOKENS    16777216  /* tokens per handle: one 256-lane block    */
+                                    /* each, and a launch holds < 2^32 lanes   */
 
 /*
  * moe_handle -- host memory, owned by the caller.  Filled by moe_init; the
@@ -118,7 +120,7 @@ size_t moe_scratch_bytes(int32_t max_tokens, int32_t top_k, int32_t ep_size);
  * workspace_size_per_rank, hidden_size); the workspace is sized once from
  * the ladder maximum.
  *   h                    host, caller-owned; overwritten
- *   max_tokens           >= 1, largest T any dispatch may pass
+ *   max_tokens           1 .. MOE_MAX_TOKENS, largest T any dispatch may pass
  *   hidden               8 .. MOE_MAX_HIDDEN, a multiple of 8
  *   top_k                1 .. MOE_MAX_TOP_K
  *   num_experts          multiple of ep_size
@@ -180,6 +182,8 @@ int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
  *   amax  = max_h |x[t, h]|,   scale = amax / 448,
  *   q[h]  = e4m3_nearest_even( x[t, h] * (448 / amax) )      (fp32 ops)
  * so x ~ e4m3_value(q) * scale; an all-zero row gets scale 0 and zero codes.
+ * x must be finite: a row holding an infinity or a NaN gets codes and a
+ * scale that mean nothing (the copies and index maps are still exact).
  *   workspace  device [ep, cap, H] uint8 codes, 16-byte aligned
  *   scales     device [ep, cap] fp32, 4-byte aligned; scales[r*cap + s] is
  *              the scale of row (r, s), written for valid rows only

@@ -53,7 +53,7 @@ def test_handle_layout_and_constants_match_header(tmp_path):
     prog += [f'printf("%zu\\n", offsetof(moe_handle, {f}));' for f in fields]
     consts = ["MOE_OK", "MOE_ERR_ARG", "MOE_ERR_PHASE", "MOE_ERR_OVERFLOW", "MOE_ERR_EXPERT_ID",
               "MOE_ERR_HIP", "MOE_STATUS_OVERFLOW", "MOE_STATUS_EXPERT_ID", "MOE_MAX_EP",
-              "MOE_MAX_TOP_K", "MOE_MAX_FUSED_HIDDEN", "MOE_MAX_HIDDEN", "MOE_LAYOUT_PER_COPY",
+              "MOE_MAX_TOP_K", "MOE_MAX_FUSED_HIDDEN", "MOE_MAX_HIDDEN", "MOE_MAX_TOKENS", "MOE_LAYOUT_PER_COPY",
               "MOE_LAYOUT_PER_REGION"]
     prog += [f'printf("%d\\n", (int){c});' for c in consts]
     prog += ["return 0;}"]
@@ -90,10 +90,13 @@ def test_sizes(lib):
     assert lib.moe_scratch_bytes(16, 65, 8) == 0
     assert lib.moe_scratch_bytes(16, 8, 257) == 0
     assert lib.moe_scratch_bytes(1 << 30, 8, 8) == 0      # T*k beyond int32
+    assert lib.moe_scratch_bytes((1 << 24) + 1, 1, 1) == 0  # more tokens than a launch holds
+    assert lib.moe_scratch_bytes(1 << 24, 1, 1) > 0
 
 
 @pytest.mark.parametrize("args", [
-    dict(max_tokens=0), dict(H=0), dict(H=12), dict(H=4), dict(H=(1 << 20) + 8), dict(k=0), dict(k=65),
+    dict(max_tokens=0), dict(max_tokens=(1 << 24) + 1), dict(H=0), dict(H=12), dict(H=4),
+    dict(H=(1 << 20) + 8), dict(k=0), dict(k=65),
     dict(ep=0), dict(ep=257), dict(E=7), dict(E=2), dict(cap=0),
     dict(ep=8, E=8, cap=1 << 29), dict(layout=2), dict(layout=-1),
 ])
