@@ -147,21 +147,28 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None, numel=None):
-    # one combined test on the common path; the messages are built only on failure
-    if (isinstance(t, torch.Tensor) and t.dtype is dtype and t.is_cuda and t.is_contiguous()
-            and (shape is None or t.shape == shape) and (numel is None or t.numel() == numel)):
-        return
-    _need_failed(t, name, dtype, shape, numel)
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, dev: int, shape=None, numel=None):
+    # One combined test on the common path (get_device() is -1 off the GPU);
+    # the messages are built only on failure.  Each tensor attribute read
+    # costs ~0.1 us, and a decode step checks six tensors.
+    try:
+        if (t.dtype is dtype and t.get_device() == dev and t.is_contiguous()
+                and (shape is None or t.shape == shape) and (numel is None or t.numel() == numel)):
+            return
+    except AttributeError:
+        pass
+    _need_failed(t, name, dtype, dev, shape, numel)
 
 
-def _need_failed(t, name, dtype, shape, numel):
+def _need_failed(t, name, dtype, dev, shape, numel):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
+    if t.get_device() != dev:
+        raise ValueError(f"{name} must be on the handle's device cuda:{dev}, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
@@ -223,23 +230,17 @@ class MoeA2A:
         self.device_index = dev.index if dev.index is not None else torch.cuda.current_device()
         self.ref = ctypes.byref(self.handle)     # built once, passed on ctypes calls
         self.addr = ctypes.addressof(self.handle)  # passed to the _moe_fast calls
+        # Sizes fixed by moe_init, kept as plain ints: the per-call checks read
+        # them, and a ctypes field read costs several times an attribute read.
+        self.hidden = hidden
+        self.top_k = top_k
+        self.ep_size = ep_size
+        self.cap = max_tokens_per_rank
+        self.workspace_numel = ep_size * max_tokens_per_rank * hidden
+        self.layout = layout
 
-    # shapes
-    @property
-    def hidden(self) -> int: return self.handle.hidden
-    @property
-    def top_k(self) -> int: return self.handle.top_k
-    @property
-    def ep_size(self) -> int: return self.handle.ep_size
-    @property
-    def cap(self) -> int: return self.handle.max_tokens_per_rank
-    @property
-    def workspace_numel(self) -> int:
-        return self.handle.ep_size * self.handle.max_tokens_per_rank * self.handle.hidden
     @property
     def num_tokens(self) -> int: return self.handle.num_tokens
-    @property
-    def layout(self) -> str: return "region" if self.handle.layout == MOE_LAYOUT_PER_REGION else "copy"
 
     def new_workspace(self, fill_bits: Optional[int] = None) -> torch.Tensor:
         """A [ep, cap, H] bf16 workspace; optionally every element set to one
@@ -276,9 +277,9 @@ def moe_dispatch(h: MoeA2A, x: torch.Tensor, topk_ids: torch.Tensor,
                  stream=None) -> None:
     """Route every routed copy of x into ``workspace`` ([ep, cap, H] bf16)."""
     T = x.shape[0] if x.dim() == 2 else 0
-    _need(x, "x", torch.bfloat16, shape=(T, h.hidden))
-    _need(topk_ids, "topk_ids", torch.int32, shape=(T, h.top_k))
-    _need(workspace, "workspace", torch.bfloat16, numel=h.workspace_numel)
+    _need(x, "x", torch.bfloat16, h.device_index, shape=(T, h.hidden))
+    _need(topk_ids, "topk_ids", torch.int32, h.device_index, shape=(T, h.top_k))
+    _need(workspace, "workspace", torch.bfloat16, h.device_index, numel=h.workspace_numel)
     _check(_fast().dispatch(h.addr, _ptr(x), _ptr(topk_ids), T, runtime_max_tokens_per_rank,
                             _ptr(workspace), _stream(stream, h.device_index)), "moe_dispatch")
 
@@ -289,10 +290,10 @@ def moe_dispatch_fp8(h: MoeA2A, x: torch.Tensor, topk_ids: torch.Tensor,
     """Route every copy with an FP8 (e4m3) payload: codes into ``workspace``
     ([ep, cap, H] uint8), one fp32 scale per row into ``scales`` ([ep, cap])."""
     T = x.shape[0] if x.dim() == 2 else 0
-    _need(x, "x", torch.bfloat16, shape=(T, h.hidden))
-    _need(topk_ids, "topk_ids", torch.int32, shape=(T, h.top_k))
-    _need(workspace, "workspace", torch.uint8, numel=h.workspace_numel)
-    _need(scales, "scales", torch.float32, numel=h.ep_size * h.cap)
+    _need(x, "x", torch.bfloat16, h.device_index, shape=(T, h.hidden))
+    _need(topk_ids, "topk_ids", torch.int32, h.device_index, shape=(T, h.top_k))
+    _need(workspace, "workspace", torch.uint8, h.device_index, numel=h.workspace_numel)
+    _need(scales, "scales", torch.float32, h.device_index, numel=h.ep_size * h.cap)
     _check(_fast().dispatch_fp8(h.addr, _ptr(x), _ptr(topk_ids), T, runtime_max_tokens_per_rank,
                                 _ptr(workspace), _ptr(scales), _stream(stream, h.device_index)),
            "moe_dispatch_fp8")
@@ -304,12 +305,12 @@ def moe_combine(h: MoeA2A, expert_out: torch.Tensor, topk_weights: Optional[torc
     """out[t] = bf16(sum_j c_j * expert_out[slot(t, j)]), reduced once in fp32."""
     T = h.handle.num_tokens
     weighted = (topk_weights is not None) if weighted is None else bool(weighted)
-    _need(expert_out, "expert_out", torch.bfloat16, numel=h.workspace_numel)
+    _need(expert_out, "expert_out", torch.bfloat16, h.device_index, numel=h.workspace_numel)
     if weighted:
-        _need(topk_weights, "topk_weights", torch.float32, shape=(T, h.top_k))
+        _need(topk_weights, "topk_weights", torch.float32, h.device_index, shape=(T, h.top_k))
     if out is None:
         out = torch.empty((T, h.hidden), dtype=torch.bfloat16, device=expert_out.device)
-    _need(out, "out", torch.bfloat16, shape=(T, h.hidden))
+    _need(out, "out", torch.bfloat16, h.device_index, shape=(T, h.hidden))
     _check(_fast().combine(h.addr, _ptr(expert_out), _ptr(topk_weights) if weighted else None,
                            int(weighted), _ptr(out), _stream(stream, h.device_index)),
            "moe_combine")
@@ -326,17 +327,17 @@ def moe_combine_residual_rmsnorm(h: MoeA2A, expert_out: torch.Tensor,
 
     Returns (residual_out, normed); ``residual_out`` may be ``residual``."""
     T, H = h.handle.num_tokens, h.hidden
-    _need(expert_out, "expert_out", torch.bfloat16, numel=h.workspace_numel)
+    _need(expert_out, "expert_out", torch.bfloat16, h.device_index, numel=h.workspace_numel)
     if weighted:
-        _need(topk_weights, "topk_weights", torch.float32, shape=(T, h.top_k))
-    _need(residual, "residual", torch.bfloat16, shape=(T, H))
-    _need(gamma, "gamma", torch.bfloat16, shape=(H,))
+        _need(topk_weights, "topk_weights", torch.float32, h.device_index, shape=(T, h.top_k))
+    _need(residual, "residual", torch.bfloat16, h.device_index, shape=(T, H))
+    _need(gamma, "gamma", torch.bfloat16, h.device_index, shape=(H,))
     if residual_out is None:
         residual_out = torch.empty_like(residual)
     if normed is None:
         normed = torch.empty_like(residual)
-    _need(residual_out, "residual_out", torch.bfloat16, shape=(T, H))
-    _need(normed, "normed", torch.bfloat16, shape=(T, H))
+    _need(residual_out, "residual_out", torch.bfloat16, h.device_index, shape=(T, H))
+    _need(normed, "normed", torch.bfloat16, h.device_index, shape=(T, H))
     _check(_fast().combine_residual_rmsnorm(
         h.addr, _ptr(expert_out), _ptr(topk_weights) if weighted else None,
         int(bool(weighted)), _ptr(residual), _ptr(residual_out), _ptr(gamma), float(eps),
@@ -347,7 +348,7 @@ def moe_combine_residual_rmsnorm(h: MoeA2A, expert_out: torch.Tensor,
 def moe_route_counts(h: MoeA2A, topk_ids: torch.Tensor, stream=None) -> torch.Tensor:
     """Per-region copy counts of a routing (for sizing max_tokens_per_rank)."""
     T = topk_ids.shape[0]
-    _need(topk_ids, "topk_ids", torch.int32, shape=(T, h.top_k))
+    _need(topk_ids, "topk_ids", torch.int32, h.device_index, shape=(T, h.top_k))
     _check(_fast().route_counts(h.addr, _ptr(topk_ids), T, _stream(stream, h.device_index)),
            "moe_route_counts")
     return h.counts

@@ -20,7 +20,7 @@ def test_need_rejects(case, exc, text):
     t = {"not_a_tensor": [1, 2], "wrong_dtype": torch.zeros(4, 8, dtype=torch.float32),
          "on_cpu": torch.zeros(4, 8, dtype=torch.bfloat16)}[case]
     with pytest.raises(exc, match=text):
-        moe._need(t, "x", torch.bfloat16, shape=(4, 8))
+        moe._need(t, "x", torch.bfloat16, 0, shape=(4, 8))
 
 
 def test_explicit_stream_handles_pass_through():
@@ -33,13 +33,16 @@ def test_explicit_stream_handles_pass_through():
 @pytest.mark.gpu
 def test_need_rejects_shape_layout_and_size_on_gpu():
     t = torch.zeros(4, 8, dtype=torch.bfloat16, device="cuda")
-    moe._need(t, "x", torch.bfloat16, shape=(4, 8), numel=32)
+    moe._need(t, "x", torch.bfloat16, 0, shape=(4, 8), numel=32)
     with pytest.raises(ValueError, match=r"must have shape \(4, 9\)"):
-        moe._need(t, "x", torch.bfloat16, shape=(4, 9))
+        moe._need(t, "x", torch.bfloat16, 0, shape=(4, 9))
     with pytest.raises(ValueError, match="must be contiguous"):
-        moe._need(t.t(), "x", torch.bfloat16, shape=(8, 4))
+        moe._need(t.t(), "x", torch.bfloat16, 0, shape=(8, 4))
     with pytest.raises(ValueError, match="must have 33 elements"):
-        moe._need(t, "x", torch.bfloat16, numel=33)
+        moe._need(t, "x", torch.bfloat16, 0, numel=33)
+    # a handle bound to another device index rejects this device's tensors
+    with pytest.raises(ValueError, match="must be on the handle's device cuda:1"):
+        moe._need(t, "x", torch.bfloat16, 1, shape=(4, 8))
 
 
 @pytest.mark.gpu
