@@ -74,6 +74,7 @@ ROUNDTRIP_CASES = [
     ("top1", 33, 256, 1, 16, 8),
     ("single_token_decode_row", 1, 7168, 8, 256, 8),
     ("few_tokens_wide_rows", 3, 16384, 8, 64, 8),
+    ("max_hidden", 3, 1 << 20, 2, 4, 2),               # MOE_MAX_HIDDEN: 2 MiB rows, 512 column blocks
     ("odd_hidden", 7, 9000, 5, 40, 5),
     ("max_regions_max_topk", 24, 64, 64, 512, 256),
     ("many_chunks_ragged", 4099, 24, 6, 36, 6),
