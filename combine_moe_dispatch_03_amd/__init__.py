@@ -48,7 +48,7 @@ MOE_MAX_EP = 256
 MOE_MAX_TOP_K = 64
 MOE_MAX_FUSED_HIDDEN = 16384
 MOE_MAX_HIDDEN = 1048576
-MOE_MAX_TOKENS = 16777216
+MOE_MAX_TOKENS = 8388608
 
 EXPORTED = (
     "moe_workspace_bytes", "moe_scratch_bytes", "moe_init", "moe_dispatch", "moe_dispatch_fp8",

@@ -130,6 +130,7 @@ static moe::DispatchArgs dispatch_args(moe_handle *h, const uint16_t *x, const i
     da.fp8 = 0;
     da.ws8 = nullptr;
     da.scales = nullptr;
+    da.t_base = 0;
     return da;
 }
 

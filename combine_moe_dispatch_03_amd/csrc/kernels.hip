@@ -6,10 +6,12 @@
 //  route_rank_kernel     per chunk of tokens: each routed copy's rank among
 //                        the chunk's copies to the same region (a stable
 //                        wave-ballot scan), and the chunk's region histogram.
-//  dispatch_copy_kernel  per token (x column block): the slot of each copy
-//                        (chunk prefix + rank), the index maps, and the
-//                        16-byte row copies x[t] -> workspace rows.  The
-//                        source row is read once and written k times.
+//  dispatch_copy_kernel  per pair of routed copies (x column block): the
+//                        slots of its token's copies (chunk prefix + rank),
+//                        the index maps, and the 16-byte row copies x[t] ->
+//                        workspace rows.  A token's blocks run on one XCD, so
+//                        its source row comes from that XCD's L2 after the
+//                        first read.
 //  dispatch_small_kernel the whole dispatch in one launch for small batches
 //                        (decode): each block counts the earlier copies
 //                        itself instead of reading route_rank_kernel's output.
@@ -29,6 +31,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "launch.h"
 #include "moe_a2a.h"
@@ -127,6 +131,27 @@ __device__ __forceinline__ void add_region_sums(int32_t *base, const int32_t *hi
     } else {
         for (int i = tid; i < n; i += kThreads) atomicAdd(&base[i % ep], hist[i]);
     }
+}
+
+// cbase[j] += sum of hist[c*ep + dests[j]] over chunks c < n_chunks, for the
+// token's copies j < k with dests[j] >= 0 (LDS, all threads): the copies of
+// earlier chunks in each copy's own region.  kThreads / kp lanes share a copy
+// (kp = k rounded up to a power of two), each summing a stride of chunks in a
+// register and adding it with one LDS atomic; k x n_chunks loads in all,
+// against ep x n_chunks for add_region_sums.
+__device__ __forceinline__ void add_copy_sums(int32_t *cbase, const int32_t *dests,
+                                              const int32_t *hist, int n_chunks, int ep, int k,
+                                              int tid) {
+    int kp = 1;
+    while (kp < k) kp <<= 1;
+    const int lanes = kThreads / kp;
+    const int j = tid / lanes, sub = tid % lanes;
+    if (j >= k) return;
+    const int d = dests[j];
+    if (d < 0) return;
+    int sum = 0;
+    for (int c = sub; c < n_chunks; c += lanes) sum += hist[(int64_t)c * ep + d];
+    if (sum != 0) atomicAdd(&cbase[j], sum);
 }
 
 // Lanes of this wave bound for the same region as this lane (d >= 0), found
@@ -264,13 +289,14 @@ __global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
 
 // ---------------------------------------------------------------------------
 // Dispatch helpers.
-// Rows of token t's copies from the region prefix `base` (copies of earlier
-// tokens) and each copy's rank after them; writes slot_index / src_index
-// (column block 0 only) and, in copy_rows, the rows this block must fill.
-// Under the per-region layout a copy whose region already has a row for this
-// token takes that row and fills nothing.  Ends with a block barrier.
+// Rows of token t's copies: thread tid < k holds copy tid's region d,
+// `before` (copies of earlier tokens in region d) and its rank after them;
+// writes slot_index / src_index (when cb == 0) and, in copy_rows, the rows
+// this block must fill.  Under the per-region layout a copy whose region
+// already has a row for this token takes that row and fills nothing.  Ends
+// with a block barrier.
 __device__ __forceinline__ void assign_rows(const DispatchArgs &a, int d, int tid, int cb,
-                                            int64_t f, const int32_t *base, int rank,
+                                            int64_t f, int before, int rank,
                                             const int32_t *dests, int32_t *rows,
                                             int32_t *copy_rows) {
     int first = tid;
@@ -280,7 +306,7 @@ __device__ __forceinline__ void assign_rows(const DispatchArgs &a, int d, int ti
     if (tid < a.k && first == tid) {
         int row = -1;
         if (d >= 0) {
-            const int s = base[d] + rank;
+            const int s = before + rank;
             if (s < a.cap)
                 row = d * a.cap + s;
             else if (cb == 0)
@@ -302,13 +328,13 @@ __device__ __forceinline__ void assign_rows(const DispatchArgs &a, int d, int ti
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Payload writers: the token's row (VPT vectors of 8 bf16 per thread, lanes
-// with col >= vpr hold a duplicate vector and store nothing) goes to every
-// row in copy_rows.
+// with col >= vpr hold a duplicate vector and store nothing) goes to the rows
+// copy_rows[j0 .. j1-1] (-1 = nothing to write).
 template <int VPT, bool NT>
 __device__ __forceinline__ void store_rows_bf16(const DispatchArgs &a, const u32x4 (&v)[VPT],
                                                 const int (&col)[VPT], const int64_t (&off)[VPT],
-                                                int vpr, const int32_t *copy_rows) {
-    for (int j = 0; j < a.k; ++j) {
+                                                int vpr, const int32_t *copy_rows, int j0, int j1) {
+    for (int j = j0; j < j1; ++j) {
         const int row = uniform(copy_rows[j]);
         if (row < 0) continue;
         uint16_t *dst = a.ws + (int64_t)row * a.H;
@@ -333,7 +359,7 @@ template <int VPT, bool NT>
 __device__ __forceinline__ void store_rows_fp8(const DispatchArgs &a, const u32x4 (&v)[VPT],
                                                const int (&col)[VPT], const int64_t (&off)[VPT],
                                                int vpr, const int32_t *copy_rows, float *red,
-                                               int tid) {
+                                               int tid, int j0, int j1) {
     float m = 0.0f;
 #pragma unroll
     for (int q = 0; q < VPT; ++q) {
@@ -363,7 +389,7 @@ __device__ __forceinline__ void store_rows_fp8(const DispatchArgs &a, const u32x
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6] * inv, f[7] * inv, hi, true);
         qv[q] = u32x2{(uint32_t)lo, (uint32_t)hi};
     }
-    for (int j = 0; j < a.k; ++j) {
+    for (int j = j0; j < j1; ++j) {
         const int row = uniform(copy_rows[j]);
         if (row < 0) continue;
         uint8_t *dst = a.ws8 + (int64_t)row * a.H;
@@ -380,28 +406,52 @@ __device__ __forceinline__ void store_rows_fp8(const DispatchArgs &a, const u32x
     }
 }
 
-// dispatch_copy_kernel<VPT, NT, FP8>: grid = (T, column blocks); each thread
-// moves VPT 16-byte vectors of the token's row, vector v of block cb at
-// (cb*VPT + v)*256 + tid, so every vector step is one coalesced 4 KB stripe.
+// dispatch_copy_kernel<VPT, NT, FP8, C>: grid = (blocks of C copies, column
+// blocks), a launch covering tokens t_base ... ; each thread moves VPT 16-byte
+// vectors of the token's row, vector v of block cb at (cb*VPT + v)*256 + tid,
+// so every vector step is one coalesced 4 KB stripe.
+// Block order: block b holds copy group (b/8) % n of token
+// t_base + ((b/8) / n)*8 + b%8, n = ceil(k/C).  Workgroups go round-robin
+// over the 8 XCDs, so the n blocks of a token (8 apart) share an XCD: its L2
+// serves the source row after the first read.  Measured at T = 4096,
+// H = 7168, top-8 (copy alone): one token per block (C = k) 90.4-91.0 us; one
+// copy per block 84.2-85.8 us in this order but 131 us in token-major order
+// (then each copy's block fetches the row into another XCD's L2); two copies
+// per block 85.7-86.6 us; four 88.0 us.  In the dispatch -> combine loop
+// (dispatch us, warm / after a 1 GiB cache-evicting read, T = 4096):
+//            one block per token   C = 1        C = 2        C = 4
+//   bf16     98.4 / 109            89 / 131     95 / 98.5    95 / 110
+//   region   68.2 / 79             69 / 108     65 / 75      67 / 81
+//   fp8      55.1 / 64             80 / 103     53 / 70      54 / 60
+// With C = 1 a token's 8 blocks miss on the same source lines at once, which
+// costs more than the split gains once the row is not in the Infinity Cache;
+// so bf16 payloads use C = 2 and the fp8 payload (each block also finds the
+// row's scale and converts the whole row) C = 4.
+// Every block computes the slots of all its token's copies (a few hundred
+// bytes from L2); only group 0, column block 0 writes the index maps.
 // The source loads are issued first (they do not depend on the slots) and
 // unconditionally (lanes past the row end re-read the row's last vector and
 // store nothing), so they are all in flight while the slots are computed.
 // NT marks the workspace stores non-temporal; FP8 writes e4m3 codes and a
-// row scale instead of the bf16 row.
-template <int VPT, bool NT, bool FP8>
+// row scale instead of the bf16 row (each block finds the row's scale).
+template <int VPT, bool NT, bool FP8, int C>
 __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a) {
     __shared__ int32_t base[MOE_MAX_EP];
+    __shared__ int32_t cbase[MOE_MAX_TOP_K];
     __shared__ int32_t dests[MOE_MAX_TOP_K];
     __shared__ int32_t rows[MOE_MAX_TOP_K];
     __shared__ int32_t copy_rows[MOE_MAX_TOP_K];
     __shared__ float red[kWaves];
 
     const int tid = threadIdx.x;
-    const int t = blockIdx.x;
     const int cb = blockIdx.y;
     const int ep = a.ep;
+    const int n = (a.k + C - 1) / C;            // copy groups per token
+    const int b = blockIdx.x;
+    const int grp = (b >> 3) % n;
+    const int t = a.t_base + ((b >> 3) / n) * 8 + (b & 7);
 
-    if (t == 0 && cb == 0) {                    // region totals over all chunks
+    if (a.t_base == 0 && b == 0 && cb == 0) {   // region totals over all chunks
         for (int r = tid; r < ep; r += kThreads) base[r] = 0;
         __syncthreads();
         add_region_sums(base, a.hist, a.n_chunks * ep, ep, tid);
@@ -435,17 +485,36 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
         dests[tid] = d;
     }
 
-    // Slots of this token's copies: copies of earlier chunks come first.
-    for (int r = tid; r < ep; r += kThreads) base[r] = 0;
+    // Slots of this token's copies: copies of earlier chunks come first,
+    // summed per region, or per copy when there are more regions than copies
+    // (for the per-region layout, more than twice as many).  Measured with
+    // 16 regions, top-8: per-copy sums took the skewed dispatch from 197 to
+    // 188 us after a cache-evicting read (warm equal) but slowed the skewed
+    // per-region dispatch from 86 to 88 us warm and 119 to 127 us cold; with
+    // 256 regions they lifted T = 4096 from 56.5 to 64.7 % of the HBM peak
+    // cold.
+    int kp = 1;
+    while (kp < a.k) kp <<= 1;
+    const bool by_copy = a.per_region ? 2 * kp < ep : kp < ep;
+    if (by_copy) {
+        if (tid < a.k) cbase[tid] = 0;
+    } else {
+        for (int r = tid; r < ep; r += kThreads) base[r] = 0;
+    }
     __syncthreads();
     const int chunk = t / a.tokens_per_chunk;
-    add_region_sums(base, a.hist, chunk * ep, ep, tid);
-    __syncthreads();
-    assign_rows(a, d, tid, cb, f, base, rank, dests, rows, copy_rows);
-    if constexpr (FP8)
-        store_rows_fp8<VPT, NT>(a, v, col, off, vpr, copy_rows, red, tid);
+    if (by_copy)
+        add_copy_sums(cbase, dests, a.hist, chunk, ep, a.k, tid);
     else
-        store_rows_bf16<VPT, NT>(a, v, col, off, vpr, copy_rows);
+        add_region_sums(base, a.hist, chunk * ep, ep, tid);
+    __syncthreads();
+    const int before = d < 0 ? 0 : by_copy ? cbase[tid] : base[d];
+    assign_rows(a, d, tid, cb | grp, f, before, rank, dests, rows, copy_rows);
+    const int j0 = grp * C, j1 = min(a.k, j0 + C);
+    if constexpr (FP8)
+        store_rows_fp8<VPT, NT>(a, v, col, off, vpr, copy_rows, red, tid, j0, j1);
+    else
+        store_rows_bf16<VPT, NT>(a, v, col, off, vpr, copy_rows, j0, j1);
 }
 
 template <bool NT>
@@ -562,11 +631,11 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
     if (tid < a.k && d >= 0)
         for (int j = 0; j < tid; ++j) rank += (dests[j] == d);
     __syncthreads();
-    assign_rows(a, d, tid, cb, f, cnt, rank, dests, rows, copy_rows);
+    assign_rows(a, d, tid, cb, f, d < 0 ? 0 : cnt[d], rank, dests, rows, copy_rows);
     if constexpr (FP8)
-        store_rows_fp8<VPT, NT>(a, v, col, off, vpr, copy_rows, red, tid);
+        store_rows_fp8<VPT, NT>(a, v, col, off, vpr, copy_rows, red, tid, 0, a.k);
     else
-        store_rows_bf16<VPT, NT>(a, v, col, off, vpr, copy_rows);
+        store_rows_bf16<VPT, NT>(a, v, col, off, vpr, copy_rows, 0, a.k);
 }
 
 // G rows starting at compacted copy j0: all G x VPT loads, then the adds in
@@ -723,8 +792,9 @@ int full_row_vpt(int32_t H) {
 }
 
 // Vectors per thread for the streaming kernels: a whole row per block when
-// there are enough tokens to fill the chip, smaller blocks otherwise.
-int streaming_vpt(int32_t T, int32_t H) {
+// there are enough rows (T of them, one per block) to fill the chip, smaller
+// blocks otherwise.
+int streaming_vpt(int64_t T, int32_t H) {
     constexpr int64_t kWantBlocks = 1024;      // 256 CUs x 4
     const int vpr = H / 8;
     int vpt = full_row_vpt(H);
@@ -748,6 +818,18 @@ int column_blocks(int32_t H, int vpt) {
 // combine shape.  Wider rows (8 vectors per thread) use groups of 4 rows to
 // keep the register count near 200.
 constexpr bool kCopyNT = true;
+// Copies per dispatch_copy_kernel block (bf16 and fp8 payloads), and the
+// most blocks along x in one launch (a launch must hold fewer than 2^32
+// lanes).
+constexpr int kCopiesPerBlock = 2;
+constexpr int kCopiesPerBlockFp8 = 4;
+// Smaller rows (under 8 KB of bf16) keep one block per token: after a cache-
+// evicting read, T = 4096, H = 2048, top-8 copies ran at 48.8 % of the HBM
+// peak split in pairs against 60.8 % whole (T = 32768: 54.9 % against 68.7 %;
+// warm steps gain 1-2 points from the split).  At H = 4096 the split is even
+// cold (64.5 against 64.6 %) and 4 points ahead warm.
+constexpr int kSplitMinHidden = 4096;
+constexpr int64_t kMaxBlocksX = int64_t(1) << 22;
 constexpr bool kCombineNT = true;
 // Rows per gather group.  Eight is best only for the plain per-copy combine
 // with more than four rows per token; everywhere else groups of 4 measured
@@ -761,20 +843,27 @@ int combine_group(int vpt, bool fused, const CombineArgs &a) {
 }
 
 template <int VPT, bool FP8>
-void launch_copy_vpt(const DispatchArgs &a, dim3 grid, hipStream_t s, bool small) {
+void launch_copy_vpt(const DispatchArgs &a, dim3 grid, hipStream_t s, bool small, int c) {
+    constexpr int kSplit = FP8 ? kCopiesPerBlockFp8 : kCopiesPerBlock;
     if (small)
         hipLaunchKernelGGL((dispatch_small_kernel<VPT, kCopyNT, FP8>), grid, dim3(kThreads), 0, s, a);
+    else if (c == kSplit)
+        hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT, FP8, kSplit>), grid,
+                           dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT, FP8>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT, FP8, MOE_MAX_TOP_K>), grid,
+                           dim3(kThreads), 0, s, a);
 }
 
+// c: copies per dispatch_copy_kernel block (kCopiesPerBlock[Fp8], or
+// MOE_MAX_TOP_K for a whole token).
 template <bool FP8>
-void launch_copy(const DispatchArgs &a, int vpt, dim3 grid, hipStream_t s, bool small) {
+void launch_copy(const DispatchArgs &a, int vpt, dim3 grid, hipStream_t s, bool small, int c) {
     switch (vpt) {
-        case 1: launch_copy_vpt<1, FP8>(a, grid, s, small); break;
-        case 2: launch_copy_vpt<2, FP8>(a, grid, s, small); break;
-        case 4: launch_copy_vpt<4, FP8>(a, grid, s, small); break;
-        default: launch_copy_vpt<8, FP8>(a, grid, s, small); break;
+        case 1: launch_copy_vpt<1, FP8>(a, grid, s, small, c); break;
+        case 2: launch_copy_vpt<2, FP8>(a, grid, s, small, c); break;
+        case 4: launch_copy_vpt<4, FP8>(a, grid, s, small, c); break;
+        default: launch_copy_vpt<8, FP8>(a, grid, s, small, c); break;
     }
 }
 
@@ -818,17 +907,42 @@ bool dispatch_is_small(int32_t num_tokens, int32_t top_k) {
     return (int64_t)num_tokens * top_k <= kSmallItems;
 }
 
-hipError_t launch_dispatch_copy(const DispatchArgs &a, hipStream_t s) {
-    // the fp8 payload needs the whole row in a block for its scale
-    const int vpt = a.fp8 ? full_row_vpt(a.H) : streaming_vpt(a.T, a.H);
-    const dim3 grid(a.T > 0 && !a.count_only ? a.T : 1,
-                    a.T > 0 && !a.count_only ? column_blocks(a.H, vpt) : 1);
+hipError_t launch_dispatch_copy(const DispatchArgs &args, hipStream_t s) {
+    DispatchArgs a = args;
+    a.t_base = 0;
     const bool small = !a.count_only && dispatch_is_small(a.T, a.k);
-    if (a.fp8)
-        launch_copy<true>(a, vpt, grid, s, small);
-    else
-        launch_copy<false>(a, vpt, grid, s, small);
-    return hipGetLastError();
+    if (small || a.count_only || a.T == 0) {    // one block per token, or the totals only
+        const int vpt = a.fp8 ? full_row_vpt(a.H) : streaming_vpt(a.T, a.H);
+        const dim3 grid(a.T > 0 && !a.count_only ? a.T : 1,
+                        a.T > 0 && !a.count_only ? column_blocks(a.H, vpt) : 1);
+        if (a.fp8)
+            launch_copy<true>(a, vpt, grid, s, small, MOE_MAX_TOP_K);
+        else
+            launch_copy<false>(a, vpt, grid, s, small, MOE_MAX_TOP_K);
+        return hipGetLastError();
+    }
+    // Blocks of c copies in XCD order (dispatch_copy_kernel), over tokens
+    // padded to a multiple of 8, in launches of at most kMaxBlocksX blocks
+    // along x.  Rows under kSplitMinHidden stay one block per token.  The
+    // fp8 payload needs the whole row in a block for its scale.
+    const int c = a.H < kSplitMinHidden ? MOE_MAX_TOP_K
+                                        : a.fp8 ? kCopiesPerBlockFp8 : kCopiesPerBlock;
+    const int n = (a.k + c - 1) / c;
+    const int64_t t_pad = ((int64_t)a.T + 7) / 8 * 8;
+    const int vpt = a.fp8 ? full_row_vpt(a.H) : streaming_vpt(t_pad * n, a.H);
+    const int64_t slab = std::max<int64_t>(8, kMaxBlocksX / n / 8 * 8);    // tokens per launch
+    for (int64_t t0 = 0; t0 < a.T; t0 += slab) {
+        a.t_base = (int32_t)t0;
+        const int64_t tokens = std::min<int64_t>(slab, t_pad - t0);
+        const dim3 grid((uint32_t)(tokens * n), column_blocks(a.H, vpt));
+        if (a.fp8)
+            launch_copy<true>(a, vpt, grid, s, false, c);
+        else
+            launch_copy<false>(a, vpt, grid, s, false, c);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_combine(const CombineArgs &args, bool fused, hipStream_t s) {

@@ -62,6 +62,7 @@ struct DispatchArgs {
     int32_t fp8;             // 1: payload is e4m3 rows in ws8 plus one scale per row
     uint8_t *ws8;            // [ep, cap, H] e4m3 (fp8 payload)
     float *scales;           // [ep, cap]    row scales (fp8 payload)
+    int32_t t_base;          // first token of this launch (set by launch_dispatch_copy)
 };
 
 struct CombineArgs {

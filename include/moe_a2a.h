@@ -75,8 +75,9 @@ extern "C" {
 #define MOE_MAX_TOP_K        64     /* routed copies per token                 */
 #define MOE_MAX_FUSED_HIDDEN 16384  /* hidden size of the fused epilogue       */
 #define MOE_MAX_HIDDEN     1048576  /* hidden size (a row stays under 2^31 B)  */
-#define MOE_MAX_TOKENS    16777216  /* tokens per handle: one 256-lane block    */
-                                    /* each, and a launch holds < 2^32 lanes   */
+#define MOE_MAX_TOKENS     8388608  /* tokens per handle: the combine runs one */
+                                    /* 256-lane block per token, and a launch */
+                                    /* holds fewer than 2^32 lanes            */
 
 /*
  * moe_handle -- host memory, owned by the caller.  Filled by moe_init; the

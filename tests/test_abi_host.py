@@ -90,12 +90,12 @@ def test_sizes(lib):
     assert lib.moe_scratch_bytes(16, 65, 8) == 0
     assert lib.moe_scratch_bytes(16, 8, 257) == 0
     assert lib.moe_scratch_bytes(1 << 30, 8, 8) == 0      # T*k beyond int32
-    assert lib.moe_scratch_bytes((1 << 24) + 1, 1, 1) == 0  # more tokens than a launch holds
-    assert lib.moe_scratch_bytes(1 << 24, 1, 1) > 0
+    assert lib.moe_scratch_bytes((1 << 23) + 1, 1, 1) == 0  # past MOE_MAX_TOKENS
+    assert lib.moe_scratch_bytes(1 << 23, 1, 1) > 0
 
 
 @pytest.mark.parametrize("args", [
-    dict(max_tokens=0), dict(max_tokens=(1 << 24) + 1), dict(H=0), dict(H=12), dict(H=4),
+    dict(max_tokens=0), dict(max_tokens=(1 << 23) + 1), dict(H=0), dict(H=12), dict(H=4),
     dict(H=(1 << 20) + 8), dict(k=0), dict(k=65),
     dict(ep=0), dict(ep=257), dict(E=7), dict(E=2), dict(cap=0),
     dict(ep=8, E=8, cap=1 << 29), dict(layout=2), dict(layout=-1),

@@ -83,6 +83,7 @@ ROUNDTRIP_CASES = [
     # the routing kernel loads its chunk's ids 4 tiles of 256 at a time:
     ("full_and_partial_tile_group", 9000, 16, 8, 64, 8),   # 1128 copies per chunk: 4 + 1 tiles
     ("five_tile_groups", 40000, 8, 8, 64, 8),              # 5000 copies per chunk: 20 tiles
+    ("copy_sums_small_rows", 3000, 64, 3, 48, 16),         # more regions than copies
 ]
 
 
@@ -93,6 +94,45 @@ def test_roundtrip_shapes(case):
     x, ids, w, y = random_case(zlib.crc32(name.encode()), T, H, k, E, ep, p_missing=0.1,
                               duplicates=True)
     roundtrip(x, ids, w, y, E, ep, cap=T * k)
+
+
+# Rows of at least 8 KB go to the copy kernel two copies per block (a token's
+# blocks share an XCD): ragged top-k (a last block with one copy), ragged
+# rows, more regions than copies (per-copy prefix sums) and fewer (per-region
+# sums), and rows over two column blocks.  cap is sized from the routing.
+SPLIT_CASES = [
+    # (name, T, H, k, E, ep)
+    ("pairs_region_sums_ragged", 389, 4104, 7, 40, 4),
+    ("pairs_copy_sums", 301, 4096, 7, 64, 16),
+    ("pairs_top64_many_regions", 40, 4096, 64, 512, 256),
+    ("pairs_two_column_blocks", 300, 32768, 7, 56, 8),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_copy_pairs_shapes(case):
+    name, T, H, k, E, ep = case
+    say("copy pairs", name, T, H, k, E, ep)
+    x, ids, w, y = random_case(zlib.crc32(name.encode()), T, H, k, E, ep, p_missing=0.1,
+                              duplicates=True)
+    dest = np.where(ids >= 0, ids // (E // ep), -1).reshape(-1)
+    cap = int(np.bincount(dest[dest >= 0], minlength=ep).max()) + 3
+    roundtrip(x, ids, w, y, E, ep, cap=cap)
+
+
+def test_copy_split_over_two_launches():
+    # The copy kernel's launches hold at most 2^22 blocks along x; small rows
+    # run one block per token, so 2^22 + 13 tokens at top-1 take two launches
+    # (the second starts at token 2^22, mid-chunk, with a padded tail).
+    T, H, k, E, ep = (1 << 22) + 13, 8, 1, 4, 2
+    say("two copy launches", T, H, k, E, ep)
+    rng = np.random.default_rng(22)
+    x = pins.random_bf16(rng, (T, H))
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[rng.random(ids.shape) < 0.05] = -1
+    w = rng.random((T, k)).astype(np.float32)
+    y = pins.random_bf16(rng, (T * k, H))
+    roundtrip(x, ids, w, y, E, ep, cap=T // 2 + 32768)
 
 
 @pytest.mark.parametrize("H", [136, 7168, 9000, 16384])

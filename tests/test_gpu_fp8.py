@@ -91,6 +91,20 @@ def test_fp8_ragged_and_two_kernel_shapes(T, H):
     fp8_check(x, ids, 24, 4, T, layout="region")
 
 
+@pytest.mark.parametrize("k", [8, 6])
+def test_fp8_split_blocks(k):
+    # rows of 8 KB and more: the fp8 copy runs four copies per block (two
+    # blocks a token here, the second partial for top-6)
+    T, H, E, ep = 300, 4096, 64, 8
+    say("fp8 split blocks", T, H, k)
+    rng = np.random.default_rng(100 + k)
+    x = pins.random_bf16(rng, (T, H))
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids[rng.random(ids.shape) < 0.05] = -1
+    fp8_check(x, ids, E, ep, T * k)
+    fp8_check(x, ids, E, ep, T, layout="region")
+
+
 def test_fp8_bad_ids_and_overflow():
     say("fp8 bad ids / overflow")
     rng = np.random.default_rng(9)

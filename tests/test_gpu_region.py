@@ -77,6 +77,11 @@ REGION_EDGE_CASES = [
     ("max_topk", 24, 64, 64, 512, 256, 0.0),
     ("tile_groups_wave_form", 9000, 16, 8, 64, 8, 0.05),     # k divides 64: ballot test
     ("tile_groups_k6", 12000, 16, 6, 36, 6, 0.05),           # k = 6: ids re-read
+    # rows of 8 KB and more: two copies per copy-kernel block
+    ("pairs_region_sums_16", 400, 4096, 8, 64, 16, 0.05),    # regions = 2 x copies
+    ("pairs_region_sums", 300, 4104, 7, 28, 4, 0.1),         # fewer regions, ragged row
+    ("pairs_copy_sums_32_regions", 300, 4096, 8, 64, 32, 0.05),   # regions > 2 x copies
+    ("copy_sums_small_rows", 1200, 64, 4, 128, 64, 0.05),    # whole-token blocks, per-copy sums
 ]
 
 
