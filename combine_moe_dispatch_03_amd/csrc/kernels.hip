@@ -6,12 +6,13 @@
 //  route_rank_kernel     per chunk of tokens: each routed copy's rank among
 //                        the chunk's copies to the same region (a stable
 //                        wave-ballot scan), and the chunk's region histogram.
-//  dispatch_copy_kernel  per pair of routed copies (x column block): the
-//                        slots of its token's copies (chunk prefix + rank),
-//                        the index maps, and the 16-byte row copies x[t] ->
-//                        workspace rows.  A token's blocks run on one XCD, so
-//                        its source row comes from that XCD's L2 after the
-//                        first read.
+//  dispatch_copy_kernel  per pair of routed copies (four for the fp8
+//                        payload, a whole token for rows under 8 KB; x column
+//                        block): the slots of its token's copies (chunk
+//                        prefix + rank), the index maps, and the 16-byte row
+//                        copies x[t] -> workspace rows.  A token's blocks run
+//                        on one XCD, so its source row comes from that XCD's
+//                        L2 after the first read.
 //  dispatch_small_kernel the whole dispatch in one launch for small batches
 //                        (decode): each block counts the earlier copies
 //                        itself instead of reading route_rank_kernel's output.
