@@ -96,10 +96,6 @@ __device__ __forceinline__ u32x4 load16(const uint16_t *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
-__device__ __forceinline__ void store16(uint16_t *p, const u32x4 &v) {
-    *reinterpret_cast<u32x4 *>(p) = v;
-}
-
 // A buffer resource over one output row of H bf16 values (raw addressing,
 // the gfx9 default data format word); `row` is uniform across the wave.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(uint16_t *row, int H) {
