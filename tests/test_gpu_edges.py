@@ -106,6 +106,7 @@ SPLIT_CASES = [
     ("pairs_copy_sums", 301, 4096, 7, 64, 16),
     ("pairs_top64_many_regions", 40, 4096, 64, 512, 256),
     ("pairs_two_column_blocks", 300, 32768, 7, 56, 8),
+    ("pairs_top1", 2100, 4096, 1, 8, 4),                   # one copy: a single half-full block
 ]
 
 

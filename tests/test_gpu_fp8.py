@@ -91,11 +91,13 @@ def test_fp8_ragged_and_two_kernel_shapes(T, H):
     fp8_check(x, ids, 24, 4, T, layout="region")
 
 
-@pytest.mark.parametrize("k", [8, 6])
+@pytest.mark.parametrize("k", [8, 6, 3])
 def test_fp8_split_blocks(k):
     # rows of 8 KB and more: the fp8 copy runs four copies per block (two
-    # blocks a token here, the second partial for top-6)
-    T, H, E, ep = 300, 4096, 64, 8
+    # blocks a token at top-8 and top-6, the second partial for top-6; one
+    # partial block at top-3); enough tokens for the two-kernel path
+    H, E, ep = 4096, 64, 8
+    T = max(300, 2100 // k)
     say("fp8 split blocks", T, H, k)
     rng = np.random.default_rng(100 + k)
     x = pins.random_bf16(rng, (T, H))
