@@ -674,7 +674,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     __shared__ int32_t rows[MOE_MAX_TOP_K];
     __shared__ float gates[MOE_MAX_TOP_K];
     __shared__ int32_t n_valid;
-    __shared__ float partial[kWaves];
+    __shared__ double partial[kWaves];
 
     const int tid = threadIdx.x;
     const int t = blockIdx.x;
@@ -740,8 +740,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
             if (col[q] < vpr) store_out16(row_rsrc(a.out + row_off, a.H), off[q], pack8(acc[q]), cached);
         return;
     } else {
-        // s = sum + residual (fp32); residual_out = bf16(s); sum of squares.
-        float ss = 0.0f;
+        // s = sum + residual (fp32); residual_out = bf16(s).  The sum of
+        // squares, its root and the normalising product are taken in fp64:
+        // in fp32, s^2 summed over a row overflows once the elements pass
+        // ~2e17 (bf16 reaches 3e38) and, with eps = 0, underflows for tiny
+        // rows, where fp64 covers the whole bf16 range.  The fp64 product
+        // is rounded to fp32, then to bf16 (both nearest-even).  The fp64
+        // work is a few dozen operations per thread in a memory-bound kernel.
+        double ss = 0.0;
         u32x4 rv[VPT];
 #pragma unroll
         for (int q = 0; q < VPT; ++q) rv[q] = load16(a.residual + row_off + off[q]);
@@ -753,7 +759,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
             for (int e = 0; e < 8; ++e) acc[q][e] = acc[q][e] + r[e];
             if (col[q] < vpr) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(acc[q][e], acc[q][e], ss);
+                for (int e = 0; e < 8; ++e)
+                    ss = __builtin_fma((double)acc[q][e], (double)acc[q][e], ss);
                 store_out16(row_rsrc(a.residual_out + row_off, a.H), off[q], pack8(acc[q]), cached);
             }
         }
@@ -764,17 +771,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 #pragma unroll
         for (int q = 0; q < VPT; ++q) gv[q] = load16(a.gamma + off[q]);
         __syncthreads();
-        float total = 0.0f;
+        double total = 0.0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) total += partial[w];
-        const float inv = 1.0f / __builtin_sqrtf(total / (float)a.H + a.eps);
+        const double inv = 1.0 / __builtin_sqrt(total / (double)a.H + (double)a.eps);
 #pragma unroll
         for (int q = 0; q < VPT; ++q) {
             if (col[q] >= vpr) continue;
             float g[8];
             unpack8(gv[q], g);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[q][e] = (acc[q][e] * inv) * g[e];
+            for (int e = 0; e < 8; ++e)
+                acc[q][e] = (float)(((double)acc[q][e] * inv) * (double)g[e]);
             store_out16(row_rsrc(a.normed + row_off, a.H), off[q], pack8(acc[q]), cached);
         }
     }

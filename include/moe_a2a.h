@@ -221,9 +221,12 @@ int moe_combine(moe_handle *h, const uint16_t *expert_out, const float *topk_wei
 
 /*
  * moe_combine_residual_rmsnorm -- combine, residual add and RMSNorm in one
- * pass ([FUSE]).  With s = (fp32 combine sum) + residual, in fp32:
+ * pass ([FUSE]).  With s = (fp32 combine sum) + residual:
  *   residual_out = bf16(s)
  *   normed       = bf16( s / sqrt(mean_h(s^2) + eps) * gamma )
+ * where the mean of squares, the root and the product are taken in fp64 (so
+ * rows anywhere in bf16's range normalise) and the result is rounded to fp32,
+ * then to bf16.  With eps = 0 a row of zeros gives NaN (0/0).
  *   residual     device [T, H] bf16, 16-byte aligned
  *   residual_out device [T, H] bf16; may be the same buffer as residual
  *   gamma        device [H] bf16, 16-byte aligned

@@ -324,6 +324,53 @@ def test_outputs_past_the_cached_store_limit(fused):
     roundtrip(x, ids, w, y, E, ep, cap=T * k, fused=fused)
 
 
+@pytest.mark.parametrize("eps", [1e-6, 0.0], ids=["eps_1e-6", "eps_0"])
+def test_fused_epilogue_over_the_whole_bf16_range(eps):
+    # The epilogue takes the sum of squares, its root and the normalising
+    # product in fp64, so rows far from fp32's comfortable range still match
+    # the oracle (fp64): elements near 2^100 and 2^120 (their squares
+    # overflow fp32), near 2^-100 and 2^-120 (their squares underflow fp32;
+    # with eps = 0 nothing else keeps the root off zero), a token with no
+    # copy and a zero residual (eps > 0: +0; eps = 0: 0/0, NaN on both sides)
+    # and ordinary rows.
+    from oracle import compare
+    T, H, k, E, ep = 8, 256, 2, 4, 2
+    rng = np.random.default_rng(123)
+    x = pins.random_bf16(rng, (T, H))
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids[2] = -1
+    w = rng.random((T, k)).astype(np.float32)
+    scale = np.ones(T, np.float32)
+    scale[[0, 1, 5, 6]] = np.float32(2.0 ** 100), np.float32(2.0 ** -100), np.float32(2.0 ** 120), \
+        np.float32(2.0 ** -120)
+    yf = rng.standard_normal((T * k, H)).astype(np.float32) * np.repeat(scale, k)[:, None]
+    rf = rng.standard_normal((T, H)).astype(np.float32) * scale[:, None]
+    rf[2] = 0.0
+    y, res = pins.torch_bf16_bits(yf), pins.torch_bf16_bits(rf)
+    gamma = pins.torch_bf16_bits(rng.uniform(0.5, 1.5, H).astype(np.float32))
+    say("fused epilogue over the bf16 range", "eps", eps)
+    orc = oracle.load()
+    ref = orc.dispatch(x, ids, ep, E // ep, T * k)
+    expert_stage_oracle(ref, y)
+    run = gpu_dispatch(x, ids, E, ep, T * k)
+    expert_stage_gpu(run, y)
+    r_out, normed = moe.moe_combine_residual_rmsnorm(run.h, run.ws, to_dev(w), True,
+                                                     to_dev_bf16(res), to_dev_bf16(gamma), eps)
+    want_r, want_n = orc.combine_residual_rmsnorm(ref.ws, ref.slot_index, w, True, res, gamma, eps)
+    assert_bf16_close(to_u16(r_out), want_r, "residual_out")
+    got = to_u16(normed)
+    gn, wn = compare.is_nan_bits(got), compare.is_nan_bits(want_n)
+    assert np.array_equal(gn, wn), "NaN positions differ"
+    assert bool(gn[2].all()) == (eps == 0.0) and not gn[[0, 1, 3, 4, 5, 6, 7]].any()
+    assert_bf16_close(np.where(gn, 0, got).astype(np.uint16),
+                      np.where(wn, 0, want_n).astype(np.uint16), "normed")
+    # the huge rows (and, without eps, the tiny ones) normalise to unit scale
+    vals = (got.astype(np.uint32) << 16).view(np.float32)
+    rows = [0, 5] + ([1, 6] if eps == 0.0 else [])
+    rms = np.sqrt(np.mean(vals[rows].astype(np.float64) ** 2, axis=1))
+    assert ((rms > 0.5) & (rms < 2.0)).all(), rms
+
+
 @pytest.mark.parametrize("fused", [False, True], ids=["combine", "fused"])
 def test_nonfinite_expert_outputs_propagate(fused):
     # NaN and +-Inf entries in the expert outputs propagate as IEEE arithmetic
