@@ -379,6 +379,67 @@ def cpu_baseline(wl, seconds: float = 10.0, seed: int = 0) -> dict:
             "cpu_model": _cpu_model(), "host_cpus_visible": os.cpu_count()}
 
 
+def cpu_baseline_all_cores(wl, threads: int, seconds: float = 10.0, seed: int = 0) -> dict:
+    """The same oracle on every host core it may use: ``threads`` threads each
+    run dispatch + combine over their own copy of the batch, back to back,
+    for about ``seconds`` of wall time (the oracle's C calls release the
+    interpreter lock, so the threads run in parallel).  Independent batches
+    in parallel, not a parallel oracle: the oracle's code is unchanged."""
+    import threading
+
+    import oracle
+    import synth
+
+    import numpy as np
+
+    orc = oracle.load()
+    inp = synth.make_inputs(wl, seed)
+    weighted = wl.combine in ("weighted", "both", "fused")
+    cap = wl.cap
+    if cap is None:
+        cap = int(orc.dispatch(np.zeros((wl.T, 1), np.uint16), inp.ids, wl.ep, wl.epr,
+                               wl.T * wl.k).counts.max())
+    reps = [0] * threads
+    start = threading.Barrier(threads + 1)
+    deadline = [0.0]
+
+    def worker(i):
+        x, ids, w = inp.x.copy(), inp.ids.copy(), inp.weights.copy()
+        start.wait()
+        while True:
+            d = orc.dispatch(x, ids, wl.ep, wl.epr, cap)
+            orc.combine(d.ws, d.slot_index, w, weighted, wl.H)
+            del d
+            reps[i] += 1
+            if time.perf_counter() >= deadline[0]:
+                return
+
+    pool = [threading.Thread(target=worker, args=(i,)) for i in range(threads)]
+    for th in pool:
+        th.start()
+    t0 = time.perf_counter()
+    deadline[0] = t0 + seconds
+    start.wait()
+    for th in pool:
+        th.join()
+    wall = time.perf_counter() - t0
+    return {"value": wl.T * sum(reps) / wall, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the full {wl.name} workload ({wl.T} tokens, dispatch + combine) on "
+                      f"{threads} threads, each running its own copy of the batch; "
+                      f"{sum(reps)} batches in {wall:.1f} s of wall time, scalar C",
+            "cpu_model": _cpu_model()}
+
+
+def host_cores() -> int:
+    """Cores this process may run on, at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -438,6 +499,9 @@ def main() -> int:
                     help="launches timed after an untimed 1 GiB cache-evicting read, per kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the all-cores CPU baseline (0: every core this process "
+                         "may use, at most 16; 1 skips it)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -517,6 +581,9 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        threads = args.cpu_threads or host_cores()
+        if threads > 1:
+            line["cpu_baseline_all_cores"] = cpu_baseline_all_cores(wl, threads, args.cpu_seconds)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -52,3 +52,16 @@ def test_shape_workloads_parse():
         except SystemExit:
             continue
         raise AssertionError(f"{bad} accepted")
+
+
+def test_cpu_baselines_on_the_tiny_workload():
+    # both CPU legs run the oracle on the same batch; the all-cores one
+    # counts every thread's batches over the wall time
+    import synth
+    wl = synth.BY_NAME["tiny"]
+    one = bench.cpu_baseline(wl, seconds=0.2)
+    many = bench.cpu_baseline_all_cores(wl, threads=2, seconds=0.2)
+    assert one["cores"] == 1 and many["cores"] == 2
+    for res in (one, many):
+        assert res["kind"] == "oracle" and res["unit"] == "tokens/s" and res["value"] > 0
+    assert 1 <= bench.host_cores() <= 16
