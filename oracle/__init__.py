@@ -54,6 +54,11 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_combine_residual_rmsnorm_region.argtypes = [
         _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_float, _P, _P, _P, _P]
     lib.oracle_combine_residual_rmsnorm_region.restype = ctypes.c_int
+    lib.oracle_partials_reduce.argtypes = [_P, _I64, _I64, _I64, _P]
+    lib.oracle_partials_reduce.restype = ctypes.c_int
+    lib.oracle_partials_reduce_residual_rmsnorm.argtypes = [
+        _P, _I64, _I64, _I64, _P, _P, ctypes.c_float, _P, _P, _P, _P]
+    lib.oracle_partials_reduce_residual_rmsnorm.restype = ctypes.c_int
     lib.oracle_quantize_e4m3_rows.argtypes = [_P, _I64, _I64, _P, _P]
     lib.oracle_quantize_e4m3_rows.restype = None
     for name in ("oracle_bf16_to_f32_array", "oracle_f32_to_bf16_array",
@@ -202,6 +207,33 @@ class Oracle:
                 T, H, k, residual.ctypes.data, gamma.ctypes.data, float(eps),
                 res_out.ctypes.data, normed.ctypes.data,
                 nf64.ctypes.data if want_f64 else None, scratch.ctypes.data)
+        return (res_out, normed, nf64) if want_f64 else (res_out, normed)
+
+    def partials_reduce(self, partials: np.ndarray) -> np.ndarray:
+        """Sum of P partial hidden states [P, T, H] (bf16 patterns) -> [T, H]:
+        fp32 in rank order, one narrowing."""
+        partials = np.ascontiguousarray(partials, dtype=np.uint16)
+        P, T, H = partials.shape
+        out = np.empty((T, H), dtype=np.uint16)
+        self.lib.oracle_partials_reduce(partials.ctypes.data, P, T, H, out.ctypes.data)
+        return out
+
+    def partials_reduce_residual_rmsnorm(self, partials: np.ndarray, residual: np.ndarray,
+                                         gamma: np.ndarray, eps: float, want_f64: bool = False):
+        """The sum of the partials, + residual, RMSNorm; returns
+        (residual_out, normed[, normed_f64])."""
+        partials = np.ascontiguousarray(partials, dtype=np.uint16)
+        residual = np.ascontiguousarray(residual, dtype=np.uint16)
+        gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+        P, T, H = partials.shape
+        res_out = np.empty((T, H), dtype=np.uint16)
+        normed = np.empty((T, H), dtype=np.uint16)
+        nf64 = np.empty((T, H), dtype=np.float64) if want_f64 else None
+        scratch = np.empty(H, dtype=np.float32)
+        self.lib.oracle_partials_reduce_residual_rmsnorm(
+            partials.ctypes.data, P, T, H, residual.ctypes.data, gamma.ctypes.data, float(eps),
+            res_out.ctypes.data, normed.ctypes.data, nf64.ctypes.data if want_f64 else None,
+            scratch.ctypes.data)
         return (res_out, normed, nf64) if want_f64 else (res_out, normed)
 
 

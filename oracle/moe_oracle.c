@@ -41,6 +41,10 @@
  *    narrowed first); residual_out = bf16(s); the mean of squares, the
  *    reciprocal square root and the scaling by gamma in fp64 (the oracle is
  *    the more precise side), eps inside the square root, mean over H;
+ *  - reduction of tensor-parallel partials ([FUSE]'s all-reduce, local
+ *    half): the P partials [P, T, H] are summed in fp32 in rank order and
+ *    narrowed once, and the fused form applies the combine's epilogue to that
+ *    sum;
  *  - per-region layout (the FlashInfer form): one row per (token, region),
  *    taken by the token's first copy to that region; the row's message (the
  *    region's gated, fp32-summed, once-narrowed expert outputs) is added once,
@@ -320,6 +324,61 @@ int oracle_combine_residual_rmsnorm_region(const uint16_t *y, const int32_t *slo
 {
     fused_rows(y, slot_index, NULL, 0, 1, T, H, k, residual, gamma, eps, residual_out, normed,
                normed_f64, s_scratch);
+    return 0;
+}
+
+/* ---- reduction stage of a one-shot all-reduce + residual + RMSNorm ([FUSE]) --
+ * Under tensor parallelism every rank ends a layer with a partial hidden state
+ * and an all-reduce sums them; [FUSE] replaces that all-reduce followed by
+ * the residual add and RMSNorm with one kernel.  On one GPU the exchange is
+ * done once all P partials sit in local memory, partials[p, t, h], and what
+ * remains is their sum.  The same "reduce once, narrow once" reading as the
+ * combine:
+ *   acc[t, h] = sum over p = 0..P-1 of f32(partials[p, t, h])   (fp32, p order)
+ *   out       = bf16(acc)                                      (plain reduce)
+ * and, fused, the epilogue of the combine above with acc in place of the
+ * combine's sum. */
+static float partials_accumulate(const uint16_t *partials, int64_t P, int64_t T,
+                                 int64_t H, int64_t t, int64_t h)
+{
+    float acc = 0.0f;
+    for (int64_t p = 0; p < P; ++p)
+        acc = acc + oracle_bf16_to_f32(partials[(p * T + t) * H + h]);
+    return acc;
+}
+
+int oracle_partials_reduce(const uint16_t *partials, int64_t P, int64_t T, int64_t H,
+                           uint16_t *out)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h)
+            out[t * H + h] = oracle_f32_to_bf16(partials_accumulate(partials, P, T, H, t, h));
+    return 0;
+}
+
+int oracle_partials_reduce_residual_rmsnorm(const uint16_t *partials, int64_t P, int64_t T,
+                                            int64_t H, const uint16_t *residual,
+                                            const uint16_t *gamma, float eps,
+                                            uint16_t *residual_out, uint16_t *normed,
+                                            double *normed_f64, float *s_scratch)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        double sumsq = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            float sum = partials_accumulate(partials, P, T, H, t, h);
+            float s = sum + oracle_bf16_to_f32(residual[t * H + h]);
+            s_scratch[h] = s;
+            sumsq += (double)s * (double)s;
+        }
+        double rinv = 1.0 / sqrt(sumsq / (double)H + (double)eps);
+        for (int64_t h = 0; h < H; ++h) {
+            double n = (double)s_scratch[h] * rinv * (double)oracle_bf16_to_f32(gamma[h]);
+            residual_out[t * H + h] = oracle_f32_to_bf16(s_scratch[h]);
+            normed[t * H + h] = oracle_f64_to_bf16(n);
+            if (normed_f64)
+                normed_f64[t * H + h] = n;
+        }
+    }
     return 0;
 }
 

@@ -496,6 +496,102 @@ def pin_rmsnorm_scale_invariance(o):
     assert np.array_equal(torch_bf16_bits(torch_bf16_value(r1) * 2), r2)
 
 
+# ------------------------------------- reduction of tensor-parallel partials
+# magik.net "Fusing the Allreduce: A Precision Investigation into FlashInfer's
+# Verify-Path Optimization", section "The Message Itself: Explanation and
+# Probe": the all-reduce of the hidden states and the residual add + RMSNorm
+# that follows become one kernel.  On one GPU the P partials [P, T, H] are
+# local and their sum is one reduction, the same "fp32, one narrowing" sum as
+# the combine; the pages' reduction probes apply to it unchanged (each
+# partial standing for one contribution).
+
+def _partials_rows(partials):
+    """The partials as the brute force's rows: partial p of token t is row
+    (p, t) of a workspace with cap = T."""
+    P, T, _ = partials.shape
+    rows = {(p, t): list(partials[p, t]) for p in range(P) for t in range(T)}
+    slot = [[p * T + t for p in range(P)] for t in range(T)]
+    return rows, slot
+
+
+def pin_partials_power_of_two(o):
+    g = read_golden("power_of_two_probe.txt")
+    vals = [float(v) for v in g["contributions"][0]]
+    T, H = 3, 16
+    partials = np.stack([np.full((T, H), exact_bits(v), np.uint16) for v in vals])
+    want = exact_bits(float(g["expected"][0][0]))
+    assert (o.partials_reduce(partials) == want).all()
+    res = np.zeros((T, H), np.uint16)
+    gamma = np.full(H, exact_bits(1.0), np.uint16)
+    r_out, _ = o.partials_reduce_residual_rmsnorm(partials, res, gamma, 1e-6)
+    assert (r_out == want).all()
+
+
+def pin_partials_reduction_probe(o):
+    g = read_golden("reduction_probe.txt")
+    vals = [float(v) for v in g["contributions"][0]]
+    partials = np.stack([np.full((1, 8), exact_bits(v), np.uint16) for v in vals])
+    out = o.partials_reduce(partials)
+    assert (out == exact_bits(float(g["fp32_then_narrow"][0][0]))).all(), hex(out[0, 0])
+    assert (out != exact_bits(float(g["bf16_pairwise_tree"][0][0]))).all()
+    assert (out != exact_bits(float(g["bf16_sequential"][0][0]))).all()
+
+
+def pin_partials_closed_forms(o):
+    rng = np.random.default_rng(21)
+    T, H = 5, 64
+    x = random_bf16(rng, (T, H))
+    # one partial: the all-reduce of one rank is its own value
+    assert np.array_equal(o.partials_reduce(x[None]), x)
+    # P identical partials, P a power of two: exactly P * x
+    for P in (2, 4, 8):
+        want = torch_bf16_bits(torch_bf16_value(x) * np.float32(P))
+        assert np.array_equal(o.partials_reduce(np.stack([x] * P)), want), P
+    # a partial and its negation cancel exactly; the others survive
+    y = random_bf16(rng, (T, H))
+    neg = x ^ np.uint16(0x8000)
+    assert np.array_equal(o.partials_reduce(np.stack([x, y, neg])), y)
+
+
+def pin_partials_textbook(o):
+    # numpy fp32, partials added in rank order, torch's nearest-even narrowing;
+    # then the textbook fp64 RMSNorm of (sum + residual)
+    rng = np.random.default_rng(22)
+    P, T, H = 6, 4, 256
+    partials = random_bf16(rng, (P, T, H))
+    acc = np.zeros((T, H), dtype=np.float32)
+    for p in range(P):
+        acc = (acc + torch_bf16_value(partials[p])).astype(np.float32)
+    assert np.array_equal(o.partials_reduce(partials), torch_bf16_bits(acc))
+    res = random_bf16(rng, (T, H))
+    gamma = torch_bf16_bits(rng.uniform(0.5, 1.5, H).astype(np.float32))
+    eps = 1e-6
+    r_out, normed, n64 = o.partials_reduce_residual_rmsnorm(partials, res, gamma, eps,
+                                                            want_f64=True)
+    s = (acc + torch_bf16_value(res)).astype(np.float32)
+    assert np.array_equal(r_out, torch_bf16_bits(s))
+    s64 = s.astype(np.float64)
+    ref = s64 / np.sqrt((s64 ** 2).mean(axis=1, keepdims=True) + np.float32(eps)) \
+        * torch_bf16_value(gamma).astype(np.float64)
+    assert np.allclose(n64, ref, rtol=1e-12, atol=0)
+    assert compare.ulp_distance(normed, torch_bf16_bits(ref.astype(np.float32))).max() <= 1
+
+
+def pin_partials_brute(o):
+    rng = np.random.default_rng(23)
+    P, T, H = 3, 2, 8
+    partials = random_bf16(rng, (P, T, H))
+    rows, slot = _partials_rows(partials)
+    assert o.partials_reduce(partials).tolist() == brute.combine(rows, slot, None, False, T, H, T)
+    res = random_bf16(rng, (T, H))
+    gamma = torch_bf16_bits(rng.uniform(0.5, 1.5, H).astype(np.float32))
+    r_out, normed = o.partials_reduce_residual_rmsnorm(partials, res, gamma, 1e-6)
+    want_r, want_n = brute.combine_residual_rmsnorm(rows, slot, None, False, res.tolist(),
+                                                    gamma.tolist(), 1e-6, T, H, T)
+    assert r_out.tolist() == want_r
+    assert normed.tolist() == want_n
+
+
 # --------------------------------------------------- per-region layout pins
 # The FlashInfer form the pages measure: one row per (token, region), the
 # region's experts return one message per token, the combine adds each

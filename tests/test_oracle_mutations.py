@@ -103,6 +103,25 @@ MUTATIONS = [
      "slot_index[f] = slot_index[f];"),
     ("region_copies_wrong_token", "memcpy(ws + row * H, x + t * H,",
      "memcpy(ws + row * H, x + (t + 1 == T ? 0 : t + 1) * H,"),
+    # reduction of tensor-parallel partials
+    ("partials_drop_last", "for (int64_t p = 0; p < P; ++p)", "for (int64_t p = 0; p < P - 1; ++p)"),
+    ("partials_bf16_accumulator",
+     "acc = acc + oracle_bf16_to_f32(partials[(p * T + t) * H + h]);",
+     "acc = oracle_bf16_to_f32(oracle_f32_to_bf16(acc + oracle_bf16_to_f32(partials[(p * T + t) * H + h])));"),
+    ("partials_token_major",
+     "acc = acc + oracle_bf16_to_f32(partials[(p * T + t) * H + h]);",
+     "acc = acc + oracle_bf16_to_f32(partials[(t * P + p) * H + h]);"),
+    ("partials_residual_not_added",
+     "float s = sum + oracle_bf16_to_f32(residual[t * H + h]);", "float s = sum;"),
+    ("partials_eps_outside_sqrt",
+     "double rinv = 1.0 / sqrt(sumsq / (double)H + (double)eps);",
+     "double rinv = 1.0 / (sqrt(sumsq / (double)H) + (double)eps);"),
+    ("partials_gamma_dropped",
+     "double n = (double)s_scratch[h] * rinv * (double)oracle_bf16_to_f32(gamma[h]);",
+     "double n = (double)s_scratch[h] * rinv;"),
+    ("partials_residual_out_from_sum_only",
+     "residual_out[t * H + h] = oracle_f32_to_bf16(s_scratch[h]);",
+     "residual_out[t * H + h] = oracle_f32_to_bf16(s_scratch[h] - oracle_bf16_to_f32(residual[t * H + h]));", 1),
     # FP8 payload
     ("e4m3_truncates", "double r = isinf(a) ? INFINITY : ldexp(nearbyint(ldexp(a, -qexp)), qexp);",
      "double r = isinf(a) ? INFINITY : ldexp(floor(ldexp(a, -qexp)), qexp);"),
