@@ -322,6 +322,93 @@ def measure(wl, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0,
     return res_d
 
 
+def measure_partials(pw, steps: int, warmup: int, cold_iters: int = 100, seed: int = 0) -> dict:
+    """The partials reduction fused with residual + RMSNorm (the local half of
+    a tensor-parallel all-reduce and the norm after it, one kernel), and the
+    plain reduction, at one shape: warm steps back to back, per-launch HIP
+    events, and cold launches after a cache-evicting read."""
+    import numpy as np
+    import torch
+
+    import combine_moe_dispatch_03_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    partials, residual, gamma = synth.make_partials(pw, seed)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    pd, rd, gd = up(partials), up(residual), up(gamma)
+    ro, nd, od = torch.empty_like(rd), torch.empty_like(rd), torch.empty_like(rd)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    hev = HipEvents()
+
+    def fused():
+        moe.moe_partials_reduce_residual_rmsnorm(pd, rd, gd, pw.eps, residual_out=ro, normed=nd,
+                                                 stream=stream)
+
+    def plain():
+        moe.moe_partials_reduce(pd, out=od, stream=stream)
+
+    for _ in range(warmup):
+        fused()
+        plain()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fused()
+    torch.cuda.synchronize(dev)
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    def timed(fn, n, flush=None):
+        evs = [[hev.create() for _ in range(2)] for _ in range(n)]
+        for e in evs:
+            if flush is not None:
+                flush.max()
+            hev.record(e[0], sh)
+            fn()
+            hev.record(e[1], sh)
+        torch.cuda.synchronize(dev)
+        out = [hev.elapsed_ms(e[0], e[1]) for e in evs]
+        for e in evs:
+            for ev in e:
+                hev.destroy(ev)
+        return out
+
+    f_ms = timed(fused, steps)
+    r_ms = timed(plain, steps)
+    b = pw.algorithmic_bytes()
+    res = {
+        "workload": f"partials: P={pw.P} tensor-parallel partials of T={pw.T} H={pw.H}, summed "
+                    f"once + residual + RMSNorm (eps {pw.eps:g}) in one kernel",
+        "ms_per_step": ms,
+        "tokens_per_s": pw.T / (ms / 1e3),
+        "step_gbs": b["fused"] / (ms / 1e3) / 1e9,
+        "step_hbm_frac": b["fused"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "fused_ms_mean": float(np.mean(f_ms)), "fused_ms_p50": float(np.median(f_ms)),
+        "fused_bytes": b["fused"],
+        "fused_gbs": b["fused"] / (float(np.mean(f_ms)) / 1e3) / 1e9,
+        "reduce_ms_mean": float(np.mean(r_ms)), "reduce_ms_p50": float(np.median(r_ms)),
+        "reduce_bytes": b["reduce"],
+        "reduce_gbs": b["reduce"] / (float(np.mean(r_ms)) / 1e3) / 1e9,
+        "cold": None,
+    }
+    if cold_iters > 0:
+        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        c_ms = timed(fused, cold_iters, flush)
+        del flush
+        c50 = float(np.median(c_ms))
+        res["cold"] = {"iters": cold_iters, "flush_bytes": 1 << 30, "fused_ms_p50": c50,
+                       "fused_ms_mean": float(np.mean(c_ms)),
+                       "fused_gbs_p50": b["fused"] / (c50 / 1e3) / 1e9,
+                       "hbm_frac_p50": b["fused"] / (c50 / 1e3) / 1e9 / HBM_PEAK_GBS}
+    del pd, rd, gd, ro, nd, od
+    torch.cuda.empty_cache()
+    return res
+
+
 def region_bytes(wl, rows: int) -> dict:
     """Algorithmic bytes under the per-region layout with ``rows`` rows sent:
     dispatch reads x and ids, writes the rows, slot_index and src_index;
@@ -492,9 +579,11 @@ def main() -> int:
                          "_fp8 suffix selects a variant")
     ap.add_argument("--extras",
                     default="skewed,decode,fused,prefill_region,skewed_region,prefill_fp8,"
-                            "prefill_region_fp8",
+                            "prefill_region_fp8,partials",
                     help="comma-separated workloads also measured (empty for none); a "
-                         "_region suffix runs the per-region layout, _fp8 the fp8 payload")
+                         "_region suffix runs the per-region layout, _fp8 the fp8 payload; "
+                         "partials is the tensor-parallel partials reduction fused with "
+                         "residual + RMSNorm")
     ap.add_argument("--cold-iters", type=int, default=100,
                     help="launches timed after an untimed 1 GiB cache-evicting read, per kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -529,8 +618,12 @@ def main() -> int:
     extras = {}
     # workload names are comma-separated; a shape spec has commas of its own,
     # so split only where the next workload's name begins
-    names = re.split(r",(?=(?:tiny|decode|prefill|skewed|fused|shape:))", args.extras)
+    names = re.split(r",(?=(?:tiny|decode|prefill|skewed|fused|partials|shape:))", args.extras)
     for name in [n for n in names if n and n != args.workload]:
+        if name == "partials":
+            extras[name] = measure_partials(synth.PARTIALS, max(args.steps // 2, 5),
+                                            max(args.warmup // 2, 2), args.cold_iters)
+            continue
         ewl, eopts = variant(name)
         extras[name] = measure(ewl, max(args.steps // 2, 5), max(args.warmup // 2, 2),
                                args.cold_iters, graph=ewl.name == "decode", **eopts)

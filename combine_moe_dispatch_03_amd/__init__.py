@@ -15,9 +15,11 @@ Functions carry the C names:
 
   moe_dispatch, moe_dispatch_fp8, moe_combine, moe_combine_residual_rmsnorm, moe_route_counts,
   moe_sync_status, moe_reset, moe_output_is_reduced, moe_strerror,
-  moe_workspace_bytes, moe_scratch_bytes
+  moe_workspace_bytes, moe_scratch_bytes,
+  moe_partials_reduce, moe_partials_reduce_residual_rmsnorm
 
-and ``MoeA2A`` owns one ``moe_handle`` plus the device buffers it binds.
+and ``MoeA2A`` owns one ``moe_handle`` plus the device buffers it binds (the
+two partials functions take no handle).
 """
 from __future__ import annotations
 
@@ -49,12 +51,14 @@ MOE_MAX_TOP_K = 64
 MOE_MAX_FUSED_HIDDEN = 16384
 MOE_MAX_HIDDEN = 1048576
 MOE_MAX_TOKENS = 8388608
+MOE_MAX_PARTIALS = 64
 
 EXPORTED = (
     "moe_workspace_bytes", "moe_scratch_bytes", "moe_init", "moe_dispatch", "moe_dispatch_fp8",
     "moe_combine",
     "moe_combine_residual_rmsnorm", "moe_route_counts", "moe_sync_status", "moe_reset",
-    "moe_output_is_reduced", "moe_strerror",
+    "moe_output_is_reduced", "moe_strerror", "moe_partials_reduce",
+    "moe_partials_reduce_residual_rmsnorm",
 )
 
 
@@ -106,6 +110,9 @@ def library() -> ctypes.CDLL:
             "moe_reset": (ctypes.c_int, [H]),
             "moe_output_is_reduced": (ctypes.c_int, []),
             "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+            "moe_partials_reduce": (ctypes.c_int, [P, I32, I32, I32, P, P]),
+            "moe_partials_reduce_residual_rmsnorm": (
+                ctypes.c_int, [P, I32, I32, I32, P, P, P, ctypes.c_float, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -367,8 +374,55 @@ def moe_reset(h: MoeA2A) -> None:
     _check(library().moe_reset(h.ref), "moe_reset")
 
 
+def _need_partials(partials: torch.Tensor) -> Tuple[int, int, int, int]:
+    """(P, T, H, device index) of a [P, T, H] bf16 device tensor."""
+    if not isinstance(partials, torch.Tensor) or partials.dim() != 3:
+        raise ValueError("partials must be a [P, T, H] tensor")
+    dev = partials.get_device()
+    _need(partials, "partials", torch.bfloat16, dev)
+    P, T, H = partials.shape
+    return P, T, H, dev
+
+
+def moe_partials_reduce(partials: torch.Tensor, out: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """Sum of P partial hidden states [P, T, H] (the reduction stage of an
+    all-reduce, on one GPU): out = bf16(fp32 sum in rank order)."""
+    P, T, H, dev = _need_partials(partials)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=partials.device)
+    _need(out, "out", torch.bfloat16, dev, shape=(T, H))
+    _check(library().moe_partials_reduce(_ptr(partials), P, T, H, _ptr(out), _stream(stream, dev)),
+           "moe_partials_reduce")
+    return out
+
+
+def moe_partials_reduce_residual_rmsnorm(partials: torch.Tensor, residual: torch.Tensor,
+                                         gamma: torch.Tensor, eps: float,
+                                         residual_out: Optional[torch.Tensor] = None,
+                                         normed: Optional[torch.Tensor] = None,
+                                         stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Sum of the partials, residual add and RMSNorm in one pass.
+
+    Returns (residual_out, normed); ``residual_out`` may be ``residual``."""
+    P, T, H, dev = _need_partials(partials)
+    _need(residual, "residual", torch.bfloat16, dev, shape=(T, H))
+    _need(gamma, "gamma", torch.bfloat16, dev, shape=(H,))
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    if normed is None:
+        normed = torch.empty_like(residual)
+    _need(residual_out, "residual_out", torch.bfloat16, dev, shape=(T, H))
+    _need(normed, "normed", torch.bfloat16, dev, shape=(T, H))
+    _check(library().moe_partials_reduce_residual_rmsnorm(
+        _ptr(partials), P, T, H, _ptr(residual), _ptr(residual_out), _ptr(gamma), float(eps),
+        _ptr(normed), _stream(stream, dev)), "moe_partials_reduce_residual_rmsnorm")
+    return residual_out, normed
+
+
 __all__ = [
     "MoeA2A", "MoeError", "MoeHandle", "library", "moe_dispatch", "moe_dispatch_fp8", "moe_combine",
     "moe_combine_residual_rmsnorm", "moe_route_counts", "moe_sync_status", "moe_reset",
     "moe_output_is_reduced", "moe_strerror", "moe_workspace_bytes", "moe_scratch_bytes",
+    "moe_partials_reduce", "moe_partials_reduce_residual_rmsnorm",
 ]

@@ -266,6 +266,60 @@ int moe_combine_residual_rmsnorm(moe_handle *h, const uint16_t *expert_out,
     return MOE_OK;
 }
 
+static int partials_checks(const uint16_t *partials, int32_t num_partials, int32_t num_tokens,
+                           int32_t hidden, int32_t max_hidden) {
+    if (num_partials < 1 || num_partials > MOE_MAX_PARTIALS) return MOE_ERR_ARG;
+    if (num_tokens < 0 || num_tokens > MOE_MAX_TOKENS) return MOE_ERR_ARG;
+    if (hidden < 8 || hidden > max_hidden || hidden % 8 != 0) return MOE_ERR_ARG;
+    if ((int64_t)num_partials * num_tokens > INT32_MAX) return MOE_ERR_ARG;
+    if (num_tokens > 0 && !dev_ok(partials, 16)) return MOE_ERR_ARG;
+    return MOE_OK;
+}
+
+static moe::CombineArgs partials_args(const uint16_t *partials, int32_t num_partials,
+                                      int32_t num_tokens, int32_t hidden) {
+    moe::CombineArgs ca;
+    memset(&ca, 0, sizeof ca);
+    ca.y = partials;
+    ca.T = num_tokens;
+    ca.H = hidden;
+    ca.k = num_partials;
+    ca.partials = 1;
+    return ca;
+}
+
+int moe_partials_reduce(const uint16_t *partials, int32_t num_partials, int32_t num_tokens,
+                        int32_t hidden, uint16_t *out, void *stream) {
+    int rc = partials_checks(partials, num_partials, num_tokens, hidden, MOE_MAX_HIDDEN);
+    if (rc != MOE_OK) return rc;
+    if (num_tokens > 0 && !dev_ok(out, 16)) return MOE_ERR_ARG;
+    moe::CombineArgs ca = partials_args(partials, num_partials, num_tokens, hidden);
+    ca.out = out;
+    return moe::launch_combine(ca, false, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_partials_reduce_residual_rmsnorm(const uint16_t *partials, int32_t num_partials,
+                                         int32_t num_tokens, int32_t hidden,
+                                         const uint16_t *residual, uint16_t *residual_out,
+                                         const uint16_t *gamma, float eps, uint16_t *normed,
+                                         void *stream) {
+    int rc = partials_checks(partials, num_partials, num_tokens, hidden, MOE_MAX_FUSED_HIDDEN);
+    if (rc != MOE_OK) return rc;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return MOE_ERR_ARG;
+    if (num_tokens > 0 && (!dev_ok(residual, 16) || !dev_ok(residual_out, 16) ||
+                           !dev_ok(gamma, 16) || !dev_ok(normed, 16)))
+        return MOE_ERR_ARG;
+    moe::CombineArgs ca = partials_args(partials, num_partials, num_tokens, hidden);
+    ca.residual = residual;
+    ca.residual_out = residual_out;
+    ca.gamma = gamma;
+    ca.normed = normed;
+    ca.eps = eps;
+    return moe::launch_combine(ca, true, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MOE_OK : MOE_ERR_HIP;
+}
+
 int moe_sync_status(moe_handle *h, void *stream, int32_t *bits) {
     if (h == nullptr || h->status == nullptr) return MOE_ERR_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -16,7 +16,8 @@
 //  dispatch_small_kernel the whole dispatch in one launch for small batches
 //                        (decode): each block counts the earlier copies
 //                        itself instead of reading route_rank_kernel's output.
-//  combine_kernel        per token (x column block): gathers the k rows,
+//  combine_kernel        per token (x column block): gathers the k rows
+//                        (routed copies, or the partials of an all-reduce),
 //                        accumulates in fp32 in j order, narrows once to
 //                        bf16 (nearest-even); optionally adds the residual
 //                        and applies RMSNorm with a block-reduced sum of
@@ -40,6 +41,9 @@
 
 namespace moe {
 namespace {
+
+static_assert(MOE_MAX_PARTIALS <= MOE_MAX_TOP_K, "partials use the combine's per-token row arrays");
+static_assert(MOE_MAX_TOP_K <= 64, "one wave compacts a token's rows");
 
 constexpr int kThreads = 256;            // 4 wave64 per workgroup
 constexpr int kWaves = kThreads / 64;
@@ -657,7 +661,9 @@ __device__ __forceinline__ void gather_group(float (&acc)[VPT][8], const uint16_
 // combine_kernel<VPT, JU, WEIGHTED, FUSED, NT>: grid = (T, column blocks);
 // FUSED runs with one column block so the whole row is in the workgroup.
 //
-// Wave 0 first compacts the token's valid copies (slot_index >= 0) into LDS,
+// With `partials` set the k rows of token t are the partial sums j*T + t of
+// a [k, T, H] buffer (the local reduction of an all-reduce), all valid.
+// Otherwise wave 0 first compacts the token's valid copies (slot_index >= 0) into LDS,
 // keeping j order, so only rows holding valid copies are ever read (padding
 // rows never are).  Under the per-region layout a row named by an earlier
 // copy of the token is dropped: each region's message is added once.  Rows
@@ -681,7 +687,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     const int cb = blockIdx.y;
     const int k = a.k;
 
-    if (tid < k) all_rows[tid] = a.slot_index[(int64_t)t * k + tid];
+    if (tid < k) all_rows[tid] = a.partials ? tid * a.T + t : a.slot_index[(int64_t)t * k + tid];
     __syncthreads();
     if (tid < 64) {                             // wave 0: compact valid copies
         int row = -1;

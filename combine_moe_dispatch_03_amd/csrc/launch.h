@@ -77,6 +77,8 @@ struct CombineArgs {
     float eps;
     int32_t T, H, k, weighted;
     int32_t per_region;      // 1: add each distinct row of a token once
+    int32_t partials;        // 1: y holds [k, T, H] partials; row j of token t is j*T + t
+                             //    (slot_index unused, every row valid)
     int32_t out_cached;      // set by launch_combine: output store cache policy (see kernels.hip)
 };
 

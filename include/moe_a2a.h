@@ -75,6 +75,7 @@ extern "C" {
 #define MOE_MAX_TOP_K        64     /* routed copies per token                 */
 #define MOE_MAX_FUSED_HIDDEN 16384  /* hidden size of the fused epilogue       */
 #define MOE_MAX_HIDDEN     1048576  /* hidden size (a row stays under 2^31 B)  */
+#define MOE_MAX_PARTIALS     64     /* partials summed by moe_partials_reduce* */
 #define MOE_MAX_TOKENS     8388608  /* tokens per handle: the combine runs one */
                                     /* 256-lane block per token, and a launch */
                                     /* holds fewer than 2^32 lanes            */
@@ -239,6 +240,48 @@ int moe_combine_residual_rmsnorm(moe_handle *h, const uint16_t *expert_out,
                                  const uint16_t *residual, uint16_t *residual_out,
                                  const uint16_t *gamma, float eps, uint16_t *normed,
                                  void *stream);
+
+/*
+ * moe_partials_reduce -- the reduction stage of a one-shot all-reduce under
+ * tensor parallelism, on one GPU.  [FUSE] section "The Message Itself:
+ * Explanation and Probe": each rank ends a layer with a partial hidden state
+ * and an all-reduce sums them before the residual add and RMSNorm.  Once the
+ * P partials sit in local memory (here they are simply a buffer the caller
+ * fills), the sum is one reduction, taken like the combine's:
+ *   out[t, h] = bf16( sum over p = 0..P-1 of f32(partials[p, t, h]) )
+ * in fp32 in rank order, one nearest-even narrowing.  No handle, no phase.
+ *   partials     device [P, T, H] bf16, 16-byte aligned
+ *   num_partials P, 1 .. MOE_MAX_PARTIALS
+ *   num_tokens   T, 0 .. MOE_MAX_TOKENS, with P * T < 2^31
+ *   hidden       H, 8 .. MOE_MAX_HIDDEN, a multiple of 8
+ *   out          device [T, H] bf16, 16-byte aligned, not overlapping
+ *                partials; overwritten
+ * Asynchronous on `stream`.  Returns MOE_OK, MOE_ERR_ARG (checked before
+ * anything is enqueued) or MOE_ERR_HIP (the launch failed; no handle keeps
+ * the HIP code, hipGetLastError has already been read).
+ */
+int moe_partials_reduce(const uint16_t *partials, int32_t num_partials, int32_t num_tokens,
+                        int32_t hidden, uint16_t *out, void *stream);
+
+/*
+ * moe_partials_reduce_residual_rmsnorm -- moe_partials_reduce fused with the
+ * residual add and RMSNorm, the single kernel [FUSE] describes in place of
+ * an all-reduce followed by the norm.  With s = (fp32 sum of the partials)
+ * + residual, the outputs are those of moe_combine_residual_rmsnorm:
+ *   residual_out = bf16(s),  normed = bf16( s / sqrt(mean_h(s^2) + eps) * gamma )
+ *   residual     device [T, H] bf16, 16-byte aligned
+ *   residual_out device [T, H] bf16; may be the same buffer as residual
+ *   gamma        device [H] bf16, 16-byte aligned
+ *   eps          finite, >= 0
+ *   normed       device [T, H] bf16, 16-byte aligned
+ * Other arguments, limits and errors as moe_partials_reduce; requires
+ * H <= MOE_MAX_FUSED_HIDDEN.
+ */
+int moe_partials_reduce_residual_rmsnorm(const uint16_t *partials, int32_t num_partials,
+                                         int32_t num_tokens, int32_t hidden,
+                                         const uint16_t *residual, uint16_t *residual_out,
+                                         const uint16_t *gamma, float eps, uint16_t *normed,
+                                         void *stream);
 
 /*
  * moe_route_counts -- only the per-region copy counts of a routing, so a

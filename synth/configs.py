@@ -78,3 +78,26 @@ FUSED = Workload("fused", T=2048, H=7168, E=256, k=8, ep=8, cap=16384, R=2048,
 
 ALL = (TINY, DECODE, PREFILL, SKEWED, FUSED)
 BY_NAME = {w.name: w for w in ALL}
+
+
+@dataclass(frozen=True)
+class PartialsWorkload:
+    """The local reduction of a tensor-parallel all-reduce fused with the
+    residual add and RMSNorm: P ranks' partial hidden states [P, T, H] sit in
+    local memory and are summed once, then normalised."""
+    name: str
+    P: int
+    T: int
+    H: int
+    eps: float = 1e-6
+
+    def algorithmic_bytes(self) -> dict:
+        """reduce: read P rows, write one = 2H(P+1) per token;
+        fused : read P rows and the residual, write residual and normed,
+                gamma once                  = 2H(P+3) per token + 2H"""
+        T, H, P = self.T, self.H, self.P
+        return {"reduce": T * 2 * H * (P + 1), "fused": T * 2 * H * (P + 3) + 2 * H}
+
+
+# eight tensor-parallel ranks, at the fused workload's token count and hidden size
+PARTIALS = PartialsWorkload("partials", P=8, T=2048, H=7168)

@@ -28,6 +28,10 @@ Synthetic expert stages (per routed copy f = t*k + j, expert e = ids[t, j]):
                                 combine itself runs unweighted)
   gaussian                      y_f ~ N(0,1) i.i.d., bf16
 
+Partials workload (``make_partials``, its own ``default_rng(seed)``):
+``partials`` N(0,1) [P, T, H] bf16, ``residual`` N(0,1) [T, H] bf16,
+``gamma`` U(0.5,1.5) [H] bf16, drawn in that order.
+
 All bf16 values are carried as ``uint16`` bit patterns.
 """
 from __future__ import annotations
@@ -38,7 +42,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from .configs import Workload
+from .configs import PartialsWorkload, Workload
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -147,3 +151,14 @@ def region_messages(ids: np.ndarray, weights: np.ndarray, y_rows: np.ndarray, ep
             acc = np.where(same, (acc + term).astype(np.float32), acc)
         out[first, j] = f32_to_bf16_bits(acc)
     return out.reshape(T * k, H)
+
+
+def make_partials(pw: PartialsWorkload, seed: int = 0):
+    """(partials [P, T, H], residual [T, H], gamma [H]) as bf16 patterns."""
+    rng = np.random.default_rng(seed)
+    partials = np.empty((pw.P, pw.T, pw.H), dtype=np.uint16)
+    for p in range(pw.P):
+        partials[p] = f32_to_bf16_bits(rng.standard_normal((pw.T, pw.H), dtype=np.float32))
+    residual = f32_to_bf16_bits(rng.standard_normal((pw.T, pw.H), dtype=np.float32))
+    gamma = f32_to_bf16_bits(rng.uniform(0.5, 1.5, size=pw.H).astype(np.float32))
+    return partials, residual, gamma

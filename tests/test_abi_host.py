@@ -53,7 +53,7 @@ def test_handle_layout_and_constants_match_header(tmp_path):
     prog += [f'printf("%zu\\n", offsetof(moe_handle, {f}));' for f in fields]
     consts = ["MOE_OK", "MOE_ERR_ARG", "MOE_ERR_PHASE", "MOE_ERR_OVERFLOW", "MOE_ERR_EXPERT_ID",
               "MOE_ERR_HIP", "MOE_STATUS_OVERFLOW", "MOE_STATUS_EXPERT_ID", "MOE_MAX_EP",
-              "MOE_MAX_TOP_K", "MOE_MAX_FUSED_HIDDEN", "MOE_MAX_HIDDEN", "MOE_MAX_TOKENS", "MOE_LAYOUT_PER_COPY",
+              "MOE_MAX_TOP_K", "MOE_MAX_FUSED_HIDDEN", "MOE_MAX_HIDDEN", "MOE_MAX_TOKENS", "MOE_MAX_PARTIALS", "MOE_LAYOUT_PER_COPY",
               "MOE_LAYOUT_PER_REGION"]
     prog += [f'printf("%d\\n", (int){c});' for c in consts]
     prog += ["return 0;}"]
@@ -202,3 +202,27 @@ def test_strerror_and_reduced_flag(lib):
     assert moe.moe_output_is_reduced() is True
     assert lib.moe_reset(None) == moe.MOE_ERR_ARG
     assert lib.moe_sync_status(None, None, None) == moe.MOE_ERR_ARG
+
+
+def test_partials_argument_checks(lib):
+    r = lambda src, P, T, H, out: lib.moe_partials_reduce(src, P, T, H, out, None)
+    assert r(FAKE, 0, 8, 128, FAKE) == moe.MOE_ERR_ARG                 # no partials
+    assert r(FAKE, 65, 8, 128, FAKE) == moe.MOE_ERR_ARG                # past MOE_MAX_PARTIALS
+    assert r(FAKE, 8, -1, 128, FAKE) == moe.MOE_ERR_ARG
+    assert r(FAKE, 1, (1 << 23) + 1, 128, FAKE) == moe.MOE_ERR_ARG     # past MOE_MAX_TOKENS
+    assert r(FAKE, 8, 8, 12, FAKE) == moe.MOE_ERR_ARG                  # H % 8
+    assert r(FAKE, 8, 8, 0, FAKE) == moe.MOE_ERR_ARG
+    assert r(FAKE, 8, 8, (1 << 20) + 8, FAKE) == moe.MOE_ERR_ARG
+    assert r(FAKE + 8, 8, 8, 128, FAKE) == moe.MOE_ERR_ARG             # partials misaligned
+    assert r(None, 8, 8, 128, FAKE) == moe.MOE_ERR_ARG
+    assert r(FAKE, 8, 8, 128, FAKE + 8) == moe.MOE_ERR_ARG             # out misaligned
+    assert r(FAKE, 8, 8, 128, None) == moe.MOE_ERR_ARG
+    f = lambda H, res, res_out, gamma, eps, normed: lib.moe_partials_reduce_residual_rmsnorm(
+        FAKE, 8, 8, H, res, res_out, gamma, eps, normed, None)
+    assert f(16392, FAKE, FAKE, FAKE, 1e-6, FAKE) == moe.MOE_ERR_ARG   # past MOE_MAX_FUSED_HIDDEN
+    assert f(128, FAKE, FAKE, FAKE, float("nan"), FAKE) == moe.MOE_ERR_ARG
+    assert f(128, FAKE, FAKE, FAKE, -1e-6, FAKE) == moe.MOE_ERR_ARG
+    assert f(128, FAKE + 8, FAKE, FAKE, 1e-6, FAKE) == moe.MOE_ERR_ARG
+    assert f(128, FAKE, None, FAKE, 1e-6, FAKE) == moe.MOE_ERR_ARG
+    assert f(128, FAKE, FAKE, FAKE + 2, 1e-6, FAKE) == moe.MOE_ERR_ARG
+    assert f(128, FAKE, FAKE, FAKE, 1e-6, None) == moe.MOE_ERR_ARG
