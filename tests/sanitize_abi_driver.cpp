@@ -46,6 +46,11 @@ hipError_t launch_dispatch_copy(const DispatchArgs &a, hipStream_t) {
 }
 hipError_t launch_combine(const CombineArgs &a, bool fused, hipStream_t) {
     if (a.T < 0 || a.k < 1 || (fused && (!a.residual || !a.gamma || !a.normed))) std::abort();
+    // a partials reduction binds no handle: no slot_index, unweighted, every row p*T + t
+    if (a.partials && (a.slot_index || a.weighted || a.per_region || a.w ||
+                       (int64_t)a.k * a.T > INT32_MAX || (a.T > 0 && (!a.y || (!fused && !a.out)))))
+        std::abort();
+    if (!a.partials && !a.slot_index) std::abort();
     ++launches;
     return hipSuccess;
 }
@@ -110,6 +115,18 @@ int main() {
     CHECK(moe_combine(&g, ws, w, 1, out, nullptr) == MOE_ERR_ARG);
     LAUNCHES(moe_combine(&g, ws, nullptr, 0, out, nullptr), 1);
     for (int code = -6; code <= 1; ++code) CHECK(moe_strerror(code) != nullptr);
+
+    // partials reduction: no handle, one launch per call, nothing for an empty batch
+    // beyond the (skipped-inside) launch call, checks before anything is enqueued
+    LAUNCHES(moe_partials_reduce(ws, 8, 4, H, out, nullptr), 1);
+    LAUNCHES(moe_partials_reduce_residual_rmsnorm(ws, 8, 4, H, out, out, out, 1e-6f, out,
+                                                  nullptr), 1);
+    LAUNCHES(moe_partials_reduce(nullptr, 8, 0, H, nullptr, nullptr), 1);
+    CHECK(moe_partials_reduce(ws, 0, 4, H, out, nullptr) == MOE_ERR_ARG);
+    CHECK(moe_partials_reduce(ws, MOE_MAX_PARTIALS + 1, 4, H, out, nullptr) == MOE_ERR_ARG);
+    CHECK(moe_partials_reduce(ws + 1, 8, 4, H, out, nullptr) == MOE_ERR_ARG);
+    CHECK(moe_partials_reduce_residual_rmsnorm(ws, 8, 4, MOE_MAX_FUSED_HIDDEN + 8, out, out, out,
+                                               1e-6f, out, nullptr) == MOE_ERR_ARG);
     std::printf("sanitized ABI driver: ok (%d launches, sync_status rc %d)\n", moe::launches, rc);
     return 0;
 }

@@ -21,6 +21,10 @@ int oracle_combine_residual_rmsnorm(const uint16_t *, const int32_t *, const flo
 int oracle_combine_residual_rmsnorm_region(const uint16_t *, const int32_t *, int64_t, int64_t,
                                            int64_t, const uint16_t *, const uint16_t *, float,
                                            uint16_t *, uint16_t *, double *, float *);
+int oracle_partials_reduce(const uint16_t *, int64_t, int64_t, int64_t, uint16_t *);
+int oracle_partials_reduce_residual_rmsnorm(const uint16_t *, int64_t, int64_t, int64_t,
+                                            const uint16_t *, const uint16_t *, float, uint16_t *,
+                                            uint16_t *, double *, float *);
 uint16_t oracle_f64_to_bf16(double);
 float oracle_e4m3_to_f32(uint8_t);
 uint8_t oracle_f32_to_e4m3(float);
@@ -75,6 +79,13 @@ static void run(int64_t T, int64_t H, int64_t k, int64_t ep, int64_t epr, int64_
         }
     }
     oracle_quantize_e4m3_rows(x, T, H, q, scale);
+    /* partials reduction: k partials of [T, H], buffers sized exactly */
+    uint16_t *parts = malloc(sizeof(uint16_t) * (size_t)(k * T * H) + 1);
+    for (int64_t i = 0; i < k * T * H; ++i) parts[i] = x[i % (T * H > 0 ? T * H : 1)];
+    oracle_partials_reduce(parts, k, T, H, out);
+    oracle_partials_reduce_residual_rmsnorm(parts, k, T, H, res, gamma, 1e-6f, res, normed, n64,
+                                            scratch);
+    free(parts);
     free(x); free(ids); free(ws); free(counts); free(slot); free(src); free(w); free(out);
     free(res); free(normed); free(gamma); free(n64); free(scratch); free(q); free(scale);
 }
