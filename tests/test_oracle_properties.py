@@ -6,8 +6,9 @@ experts per region, capacity), the share of unrouted copies and of ids
 outside [-1, E), and a seed for the values, and every drawn case must agree
 bit for bit with oracle/brute.py: dispatch (counts, status, slot_index,
 src_index, rows) in both layouts, the weighted and unweighted combine, the
-per-region combine and the fused residual + RMSNorm epilogue.  Runs are
-derandomized, so the suite is reproducible.
+per-region combine and the fused residual + RMSNorm epilogue; and for the
+reduction of P tensor-parallel partials (plain and fused), random P, T, H,
+eps and value scale.  Runs are derandomized, so the suite is reproducible.
 """
 import numpy as np
 from hypothesis import given, settings
@@ -104,3 +105,24 @@ def test_fused_epilogue_matches_brute_force(c, eps):
                                                         T, H, cap)
         assert r_out.tolist() == want_r
         assert normed.tolist() == want_n
+
+
+@settings(max_examples=30, deadline=None, derandomize=True)
+@given(st.integers(1, 9), st.integers(0, 4), st.sampled_from([1, 2, 8]),
+       st.sampled_from([0.0, 1e-6, 0.25]), st.integers(0, 2 ** 31 - 1))
+def test_partials_reduction_matches_brute_force(P, T, H, eps, seed):
+    # partial p of token t is row (p, t) of a workspace with cap = T
+    orc = oracle.load()
+    rng = np.random.default_rng(seed)
+    partials = random_bf16(rng, (P, T, H), scale=float(rng.choice([1.0, 1e-3, 1e3])))
+    rows = {(p, t): list(partials[p, t]) for p in range(P) for t in range(T)}
+    slot = [[p * T + t for p in range(P)] for t in range(T)]
+    cap = max(T, 1)
+    assert orc.partials_reduce(partials).tolist() == brute.combine(rows, slot, None, False, T, H, cap)
+    res = random_bf16(rng, (T, H))
+    gamma = torch_bf16_bits(rng.uniform(0.5, 1.5, H).astype(np.float32))
+    r_out, normed = orc.partials_reduce_residual_rmsnorm(partials, res, gamma, eps)
+    want_r, want_n = brute.combine_residual_rmsnorm(rows, slot, None, False, res.tolist(),
+                                                    gamma.tolist(), eps, T, H, cap)
+    assert r_out.tolist() == want_r
+    assert normed.tolist() == want_n
