@@ -74,3 +74,37 @@ def test_graph_replays_match_eager(name, layout, fused):
         for a, b in zip(got, want):
             assert np.array_equal(a, b), f"replay {rep} differs"
     assert moe.moe_sync_status(h) == (moe.MOE_OK, 0)
+
+
+def test_partials_graph_replays_match_eager():
+    # the partials reduction fused with residual + RMSNorm, then the plain
+    # reduction, captured together
+    P, T, H = 8, 512, 7168
+    say("graph", "partials", P, T, H)
+    partials, residual, gamma = synth.make_partials(synth.PartialsWorkload("graph", P, T, H), 3)
+    pd, rd, gd = to_dev_bf16(partials), to_dev_bf16(residual), to_dev_bf16(gamma)
+    ro, nd, od = torch.empty_like(rd), torch.empty_like(rd), torch.empty_like(rd)
+
+    def step():
+        moe.moe_partials_reduce_residual_rmsnorm(pd, rd, gd, 1e-6, residual_out=ro, normed=nd)
+        moe.moe_partials_reduce(pd, out=od)
+
+    step()
+    torch.cuda.synchronize()
+    want = [to_u16(ro), to_u16(nd), to_u16(od)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (ro, nd, od):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip([to_u16(ro), to_u16(nd), to_u16(od)], want):
+            assert np.array_equal(a, b), f"replay {rep} differs"
