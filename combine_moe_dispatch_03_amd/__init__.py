@@ -126,9 +126,10 @@ _fast_mod = None
 
 def _fast():
     """The ``_moe_fast`` extension: the per-call entry points (dispatch,
-    dispatch_fp8, combine, combine_residual_rmsnorm, route_counts) with their
-    argument conversion in C, a few microseconds cheaper per call than ctypes.
-    It calls the same functions of the same loaded library."""
+    dispatch_fp8, combine, combine_residual_rmsnorm, route_counts and the two
+    partials reductions) with their argument conversion in C, a few
+    microseconds cheaper per call than ctypes.  It calls the same functions
+    of the same loaded library."""
     global _fast_mod
     if _fast_mod is None:
         library()                       # the library first: one copy, loaded by path
@@ -392,7 +393,7 @@ def moe_partials_reduce(partials: torch.Tensor, out: Optional[torch.Tensor] = No
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=partials.device)
     _need(out, "out", torch.bfloat16, dev, shape=(T, H))
-    _check(library().moe_partials_reduce(_ptr(partials), P, T, H, _ptr(out), _stream(stream, dev)),
+    _check(_fast().partials_reduce(_ptr(partials), P, T, H, _ptr(out), _stream(stream, dev)),
            "moe_partials_reduce")
     return out
 
@@ -414,7 +415,7 @@ def moe_partials_reduce_residual_rmsnorm(partials: torch.Tensor, residual: torch
         normed = torch.empty_like(residual)
     _need(residual_out, "residual_out", torch.bfloat16, dev, shape=(T, H))
     _need(normed, "normed", torch.bfloat16, dev, shape=(T, H))
-    _check(library().moe_partials_reduce_residual_rmsnorm(
+    _check(_fast().partials_reduce_residual_rmsnorm(
         _ptr(partials), P, T, H, _ptr(residual), _ptr(residual_out), _ptr(gamma), float(eps),
         _ptr(normed), _stream(stream, dev)), "moe_partials_reduce_residual_rmsnorm")
     return residual_out, normed

@@ -18,6 +18,12 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool dev_ok(const void *p, uintptr_t a) { return p != nullptr && aligned(p, a); }
 
+// True if the byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && pa < pb + nb && pb < pa + na;
+}
+
 int hip_fail(moe_handle *h, hipError_t e) {
     h->hip_error = static_cast<int32_t>(e);
     return MOE_ERR_HIP;
@@ -293,6 +299,8 @@ int moe_partials_reduce(const uint16_t *partials, int32_t num_partials, int32_t 
     int rc = partials_checks(partials, num_partials, num_tokens, hidden, MOE_MAX_HIDDEN);
     if (rc != MOE_OK) return rc;
     if (num_tokens > 0 && !dev_ok(out, 16)) return MOE_ERR_ARG;
+    const size_t row_bytes = (size_t)num_tokens * hidden * sizeof(uint16_t);
+    if (overlaps(out, row_bytes, partials, row_bytes * num_partials)) return MOE_ERR_ARG;
     moe::CombineArgs ca = partials_args(partials, num_partials, num_tokens, hidden);
     ca.out = out;
     return moe::launch_combine(ca, false, static_cast<hipStream_t>(stream)) == hipSuccess
@@ -309,6 +317,19 @@ int moe_partials_reduce_residual_rmsnorm(const uint16_t *partials, int32_t num_p
     if (!(eps >= 0.0f) || !isfinite(eps)) return MOE_ERR_ARG;
     if (num_tokens > 0 && (!dev_ok(residual, 16) || !dev_ok(residual_out, 16) ||
                            !dev_ok(gamma, 16) || !dev_ok(normed, 16)))
+        return MOE_ERR_ARG;
+    // outputs must not overlap the inputs they are computed from (residual_out
+    // may be residual itself) or each other
+    const size_t row_bytes = (size_t)num_tokens * hidden * sizeof(uint16_t);
+    const size_t part_bytes = row_bytes * num_partials;
+    const size_t gamma_bytes = (size_t)hidden * sizeof(uint16_t);
+    if (overlaps(residual_out, row_bytes, partials, part_bytes) ||
+        overlaps(normed, row_bytes, partials, part_bytes) ||
+        overlaps(normed, row_bytes, residual, row_bytes) ||
+        overlaps(normed, row_bytes, residual_out, row_bytes) ||
+        overlaps(residual_out, row_bytes, gamma, gamma_bytes) ||
+        overlaps(normed, row_bytes, gamma, gamma_bytes) ||
+        (residual_out != residual && overlaps(residual_out, row_bytes, residual, row_bytes)))
         return MOE_ERR_ARG;
     moe::CombineArgs ca = partials_args(partials, num_partials, num_tokens, hidden);
     ca.residual = residual;

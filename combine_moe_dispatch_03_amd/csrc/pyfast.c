@@ -109,6 +109,40 @@ static PyObject *fast_route_counts(PyObject *self, PyObject *const *args, Py_ssi
     return PyLong_FromLong(moe_route_counts((moe_handle *)h, (const int32_t *)ids, T, stream));
 }
 
+/* partials_reduce(partials, num_partials, num_tokens, hidden, out, stream) */
+static PyObject *fast_partials_reduce(PyObject *self, PyObject *const *args, Py_ssize_t nargs) {
+    void *partials, *out, *stream;
+    int32_t P, T, H;
+    (void)self;
+    if (want_args(nargs, 6, "partials_reduce") || ptr_arg(args[0], &partials) ||
+        i32_arg(args[1], &P) || i32_arg(args[2], &T) || i32_arg(args[3], &H) ||
+        ptr_arg(args[4], &out) || ptr_arg(args[5], &stream))
+        return NULL;
+    return PyLong_FromLong(moe_partials_reduce((const uint16_t *)partials, P, T, H,
+                                               (uint16_t *)out, stream));
+}
+
+/* partials_reduce_residual_rmsnorm(partials, num_partials, num_tokens, hidden, residual,
+ *                                  residual_out, gamma, eps, normed, stream) */
+static PyObject *fast_partials_reduce_residual_rmsnorm(PyObject *self, PyObject *const *args,
+                                                       Py_ssize_t nargs) {
+    void *partials, *res, *res_out, *gamma, *normed, *stream;
+    int32_t P, T, H;
+    double eps;
+    (void)self;
+    if (want_args(nargs, 10, "partials_reduce_residual_rmsnorm") ||
+        ptr_arg(args[0], &partials) || i32_arg(args[1], &P) || i32_arg(args[2], &T) ||
+        i32_arg(args[3], &H) || ptr_arg(args[4], &res) || ptr_arg(args[5], &res_out) ||
+        ptr_arg(args[6], &gamma))
+        return NULL;
+    eps = PyFloat_AsDouble(args[7]);
+    if (eps == -1.0 && PyErr_Occurred()) return NULL;
+    if (ptr_arg(args[8], &normed) || ptr_arg(args[9], &stream)) return NULL;
+    return PyLong_FromLong(moe_partials_reduce_residual_rmsnorm(
+        (const uint16_t *)partials, P, T, H, (const uint16_t *)res, (uint16_t *)res_out,
+        (const uint16_t *)gamma, (float)eps, (uint16_t *)normed, stream));
+}
+
 static PyMethodDef methods[] = {
     {"dispatch", (PyCFunction)(void (*)(void))fast_dispatch, METH_FASTCALL, "moe_dispatch"},
     {"dispatch_fp8", (PyCFunction)(void (*)(void))fast_dispatch_fp8, METH_FASTCALL,
@@ -118,6 +152,11 @@ static PyMethodDef methods[] = {
      METH_FASTCALL, "moe_combine_residual_rmsnorm"},
     {"route_counts", (PyCFunction)(void (*)(void))fast_route_counts, METH_FASTCALL,
      "moe_route_counts"},
+    {"partials_reduce", (PyCFunction)(void (*)(void))fast_partials_reduce, METH_FASTCALL,
+     "moe_partials_reduce"},
+    {"partials_reduce_residual_rmsnorm",
+     (PyCFunction)(void (*)(void))fast_partials_reduce_residual_rmsnorm, METH_FASTCALL,
+     "moe_partials_reduce_residual_rmsnorm"},
     {NULL, NULL, 0, NULL},
 };
 

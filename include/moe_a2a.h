@@ -254,8 +254,8 @@ int moe_combine_residual_rmsnorm(moe_handle *h, const uint16_t *expert_out,
  *   num_partials P, 1 .. MOE_MAX_PARTIALS
  *   num_tokens   T, 0 .. MOE_MAX_TOKENS, with P * T < 2^31
  *   hidden       H, 8 .. MOE_MAX_HIDDEN, a multiple of 8
- *   out          device [T, H] bf16, 16-byte aligned, not overlapping
- *                partials; overwritten
+ *   out          device [T, H] bf16, 16-byte aligned; overwritten; overlapping
+ *                partials is MOE_ERR_ARG
  * Asynchronous on `stream`.  Returns MOE_OK, MOE_ERR_ARG (checked before
  * anything is enqueued) or MOE_ERR_HIP (the launch failed; no handle keeps
  * the HIP code, hipGetLastError has already been read).
@@ -274,8 +274,10 @@ int moe_partials_reduce(const uint16_t *partials, int32_t num_partials, int32_t 
  *   gamma        device [H] bf16, 16-byte aligned
  *   eps          finite, >= 0
  *   normed       device [T, H] bf16, 16-byte aligned
- * Other arguments, limits and errors as moe_partials_reduce; requires
- * H <= MOE_MAX_FUSED_HIDDEN.
+ * The outputs may not overlap partials, gamma or each other, nor (normed)
+ * the residual, and residual_out overlaps the residual only by being the
+ * same buffer; otherwise MOE_ERR_ARG.  Other arguments, limits and errors as
+ * moe_partials_reduce; requires H <= MOE_MAX_FUSED_HIDDEN.
  */
 int moe_partials_reduce_residual_rmsnorm(const uint16_t *partials, int32_t num_partials,
                                          int32_t num_tokens, int32_t hidden,

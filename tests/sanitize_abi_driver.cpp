@@ -119,14 +119,31 @@ int main() {
     // partials reduction: no handle, one launch per call, nothing for an empty batch
     // beyond the (skipped-inside) launch call, checks before anything is enqueued
     LAUNCHES(moe_partials_reduce(ws, 8, 4, H, out, nullptr), 1);
-    LAUNCHES(moe_partials_reduce_residual_rmsnorm(ws, 8, 4, H, out, out, out, 1e-6f, out,
-                                                  nullptr), 1);
+    LAUNCHES(moe_partials_reduce_residual_rmsnorm(ws, 8, 4, H, out, out, out + 1024, 1e-6f,
+                                                  out + 2048, nullptr), 1);
     LAUNCHES(moe_partials_reduce(nullptr, 8, 0, H, nullptr, nullptr), 1);
     CHECK(moe_partials_reduce(ws, 0, 4, H, out, nullptr) == MOE_ERR_ARG);
     CHECK(moe_partials_reduce(ws, MOE_MAX_PARTIALS + 1, 4, H, out, nullptr) == MOE_ERR_ARG);
     CHECK(moe_partials_reduce(ws + 1, 8, 4, H, out, nullptr) == MOE_ERR_ARG);
     CHECK(moe_partials_reduce_residual_rmsnorm(ws, 8, 4, MOE_MAX_FUSED_HIDDEN + 8, out, out, out,
                                                1e-6f, out, nullptr) == MOE_ERR_ARG);
+    // outputs overlapping their inputs or each other are rejected; the
+    // in-place residual (residual_out == residual) is allowed
+    {
+        alignas(16) static uint16_t pool[8 * 4 * 16 + 6 * 4 * 16];
+        const int32_t P = 8, Tn = 4, Hn = 16, n = Tn * Hn;
+        uint16_t *parts = pool, *res = pool + P * n, *nrm = res + n, *gam = nrm + n;
+        CHECK(moe_partials_reduce(parts, P, Tn, Hn, parts + (P - 1) * n + 8, nullptr) == MOE_ERR_ARG);
+        LAUNCHES(moe_partials_reduce(parts, P, Tn, Hn, res, nullptr), 1);
+        LAUNCHES(moe_partials_reduce_residual_rmsnorm(parts, P, Tn, Hn, res, res, gam, 1e-6f, nrm,
+                                                      nullptr), 1);
+        CHECK(moe_partials_reduce_residual_rmsnorm(parts, P, Tn, Hn, res, res, gam, 1e-6f, res,
+                                                   nullptr) == MOE_ERR_ARG);
+        CHECK(moe_partials_reduce_residual_rmsnorm(parts, P, Tn, Hn, res, res + 8, gam, 1e-6f, nrm,
+                                                   nullptr) == MOE_ERR_ARG);
+        CHECK(moe_partials_reduce_residual_rmsnorm(parts, P, Tn, Hn, res, res, nrm, 1e-6f, nrm,
+                                                   nullptr) == MOE_ERR_ARG);
+    }
     std::printf("sanitized ABI driver: ok (%d launches, sync_status rc %d)\n", moe::launches, rc);
     return 0;
 }

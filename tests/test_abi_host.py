@@ -226,3 +226,22 @@ def test_partials_argument_checks(lib):
     assert f(128, FAKE, None, FAKE, 1e-6, FAKE) == moe.MOE_ERR_ARG
     assert f(128, FAKE, FAKE, FAKE + 2, 1e-6, FAKE) == moe.MOE_ERR_ARG
     assert f(128, FAKE, FAKE, FAKE, 1e-6, None) == moe.MOE_ERR_ARG
+
+
+def test_partials_reject_overlapping_outputs(lib):
+    # only rejected calls: a call that passed its checks would launch on fake addresses
+    P, T, H = 8, 4, 128
+    rows = T * H * 2
+    r = lambda out: lib.moe_partials_reduce(FAKE, P, T, H, out, None)
+    assert r(FAKE) == moe.MOE_ERR_ARG                                  # out is the partials
+    assert r(FAKE + P * rows - 16) == moe.MOE_ERR_ARG                  # last 16 bytes shared
+    assert r(FAKE - rows + 16) == moe.MOE_ERR_ARG                      # first 16 bytes shared
+    base = FAKE + 64 * rows            # outputs clear of the partials
+    f = lambda res, res_out, gamma, normed: lib.moe_partials_reduce_residual_rmsnorm(
+        FAKE, P, T, H, res, res_out, gamma, 1e-6, normed, None)
+    assert f(base, FAKE + rows, base + 8 * rows, base + 4 * rows) == moe.MOE_ERR_ARG  # residual_out in partials
+    assert f(base, base + 2 * rows, base + 8 * rows, FAKE) == moe.MOE_ERR_ARG         # normed in partials
+    assert f(base, base, base + 8 * rows, base) == moe.MOE_ERR_ARG                    # normed = residual
+    assert f(base, base + 2 * rows, base + 8 * rows, base + 2 * rows) == moe.MOE_ERR_ARG  # normed = residual_out
+    assert f(base, base + 2 * rows, base + 2 * rows, base + 4 * rows) == moe.MOE_ERR_ARG  # residual_out over gamma
+    assert f(base, base + 16, base + 8 * rows, base + 4 * rows) == moe.MOE_ERR_ARG    # residual_out partly over residual
