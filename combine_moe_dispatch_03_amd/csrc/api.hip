@@ -24,6 +24,21 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     return na > 0 && nb > 0 && pa < pb + nb && pb < pa + na;
 }
 
+// The outputs of a fused epilogue against its inputs: `src` (the gathered
+// rows), the residual, gamma, and each other.  residual_out may be the
+// residual itself (updated in place), but not overlap it otherwise.
+bool fused_outputs_overlap(const void *src, size_t src_bytes, const uint16_t *residual,
+                           const uint16_t *residual_out, const uint16_t *gamma,
+                           const uint16_t *normed, size_t row_bytes, size_t gamma_bytes) {
+    return overlaps(residual_out, row_bytes, src, src_bytes) ||
+           overlaps(normed, row_bytes, src, src_bytes) ||
+           overlaps(normed, row_bytes, residual, row_bytes) ||
+           overlaps(normed, row_bytes, residual_out, row_bytes) ||
+           overlaps(residual_out, row_bytes, gamma, gamma_bytes) ||
+           overlaps(normed, row_bytes, gamma, gamma_bytes) ||
+           (residual_out != residual && overlaps(residual_out, row_bytes, residual, row_bytes));
+}
+
 int hip_fail(moe_handle *h, hipError_t e) {
     h->hip_error = static_cast<int32_t>(e);
     return MOE_ERR_HIP;
@@ -150,6 +165,15 @@ static int dispatch_checks(moe_handle *h, const uint16_t *x, const int32_t *topk
     return MOE_OK;
 }
 
+// Bytes of the token rows a dispatch reads, and of its workspace (bf16 rows,
+// or fp8 codes when elem == 1).
+static size_t token_bytes(const moe_handle *h, int32_t num_tokens) {
+    return (size_t)num_tokens * h->hidden * sizeof(uint16_t);
+}
+static size_t ws_bytes(const moe_handle *h, size_t elem) {
+    return (size_t)h->ep_size * h->max_tokens_per_rank * h->hidden * elem;
+}
+
 static int dispatch_launch(moe_handle *h, moe::DispatchArgs da, const int32_t *topk_ids,
                            int32_t num_tokens, int32_t R, hipStream_t s) {
     moe::RoutePlan plan = moe::plan_route(num_tokens);
@@ -173,6 +197,8 @@ int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
     const int32_t R = runtime_max_tokens_per_rank;
     int rc = dispatch_checks(h, x, topk_ids, num_tokens, R, workspace);
     if (rc != MOE_OK) return rc;
+    if (overlaps(workspace, ws_bytes(h, sizeof(uint16_t)), x, token_bytes(h, num_tokens)))
+        return MOE_ERR_ARG;
     const moe::DispatchArgs da = dispatch_args(h, x, topk_ids, num_tokens, workspace,
                                                moe::plan_route(num_tokens), 0);
     return dispatch_launch(h, da, topk_ids, num_tokens, R, static_cast<hipStream_t>(stream));
@@ -185,6 +211,11 @@ int moe_dispatch_fp8(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
     int rc = dispatch_checks(h, x, topk_ids, num_tokens, R, workspace);
     if (rc != MOE_OK) return rc;
     if (!dev_ok(scales, 4) || h->hidden > MOE_MAX_FUSED_HIDDEN) return MOE_ERR_ARG;
+    const size_t scale_bytes = (size_t)h->ep_size * h->max_tokens_per_rank * sizeof(float);
+    if (overlaps(workspace, ws_bytes(h, 1), x, token_bytes(h, num_tokens)) ||
+        overlaps(scales, scale_bytes, x, token_bytes(h, num_tokens)) ||
+        overlaps(scales, scale_bytes, workspace, ws_bytes(h, 1)))
+        return MOE_ERR_ARG;
     moe::DispatchArgs da = dispatch_args(h, x, topk_ids, num_tokens, nullptr,
                                          moe::plan_route(num_tokens), 0);
     da.fp8 = 1;
@@ -240,6 +271,8 @@ int moe_combine(moe_handle *h, const uint16_t *expert_out, const float *topk_wei
     int rc = combine_common(h, expert_out, topk_weights, weighted);
     if (rc != MOE_OK) return rc;
     if (h->num_tokens > 0 && !dev_ok(out, 16)) return MOE_ERR_ARG;
+    if (overlaps(out, token_bytes(h, h->num_tokens), expert_out, ws_bytes(h, sizeof(uint16_t))))
+        return MOE_ERR_ARG;
     moe::CombineArgs ca = combine_args(h, expert_out, topk_weights, weighted);
     ca.out = out;
     hipError_t e = moe::launch_combine(ca, false, static_cast<hipStream_t>(stream));
@@ -259,6 +292,10 @@ int moe_combine_residual_rmsnorm(moe_handle *h, const uint16_t *expert_out,
     if (!(eps >= 0.0f) || !isfinite(eps)) return MOE_ERR_ARG;
     if (h->num_tokens > 0 && (!dev_ok(residual, 16) || !dev_ok(residual_out, 16) ||
                               !dev_ok(gamma, 16) || !dev_ok(normed, 16)))
+        return MOE_ERR_ARG;
+    if (fused_outputs_overlap(expert_out, ws_bytes(h, sizeof(uint16_t)), residual, residual_out,
+                              gamma, normed, token_bytes(h, h->num_tokens),
+                              (size_t)h->hidden * sizeof(uint16_t)))
         return MOE_ERR_ARG;
     moe::CombineArgs ca = combine_args(h, expert_out, topk_weights, weighted);
     ca.residual = residual;
@@ -318,18 +355,9 @@ int moe_partials_reduce_residual_rmsnorm(const uint16_t *partials, int32_t num_p
     if (num_tokens > 0 && (!dev_ok(residual, 16) || !dev_ok(residual_out, 16) ||
                            !dev_ok(gamma, 16) || !dev_ok(normed, 16)))
         return MOE_ERR_ARG;
-    // outputs must not overlap the inputs they are computed from (residual_out
-    // may be residual itself) or each other
     const size_t row_bytes = (size_t)num_tokens * hidden * sizeof(uint16_t);
-    const size_t part_bytes = row_bytes * num_partials;
-    const size_t gamma_bytes = (size_t)hidden * sizeof(uint16_t);
-    if (overlaps(residual_out, row_bytes, partials, part_bytes) ||
-        overlaps(normed, row_bytes, partials, part_bytes) ||
-        overlaps(normed, row_bytes, residual, row_bytes) ||
-        overlaps(normed, row_bytes, residual_out, row_bytes) ||
-        overlaps(residual_out, row_bytes, gamma, gamma_bytes) ||
-        overlaps(normed, row_bytes, gamma, gamma_bytes) ||
-        (residual_out != residual && overlaps(residual_out, row_bytes, residual, row_bytes)))
+    if (fused_outputs_overlap(partials, row_bytes * num_partials, residual, residual_out, gamma,
+                              normed, row_bytes, (size_t)hidden * sizeof(uint16_t)))
         return MOE_ERR_ARG;
     moe::CombineArgs ca = partials_args(partials, num_partials, num_tokens, hidden);
     ca.residual = residual;

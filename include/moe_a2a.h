@@ -168,6 +168,7 @@ int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
  * Copies past cap are dropped (slot_index -1) and set MOE_STATUS_OVERFLOW;
  * ids outside [-1, E) are dropped and set MOE_STATUS_EXPERT_ID; both are
  * reported by moe_sync_status.
+ * A workspace overlapping x is MOE_ERR_ARG.
  * Returns MOE_OK, MOE_ERR_ARG, MOE_ERR_PHASE (already dispatched) or
  * MOE_ERR_HIP (launch failed).  On success the handle is "dispatched".
  */
@@ -190,7 +191,8 @@ int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
  *   scales     device [ep, cap] fp32, 4-byte aligned; scales[r*cap + s] is
  *              the scale of row (r, s), written for valid rows only
  * Other arguments, outputs (counts, slot_index, src_index), errors and the
- * phase as moe_dispatch; requires H <= MOE_MAX_FUSED_HIDDEN.  The combine
+ * phase as moe_dispatch; requires H <= MOE_MAX_FUSED_HIDDEN; workspace,
+ * scales and x must not overlap (MOE_ERR_ARG).  The combine
  * that follows reads bf16 expert outputs from a buffer of the same
  * [ep, cap, H] layout (the experts dequantise and write it).
  */
@@ -206,7 +208,8 @@ int moe_dispatch_fp8(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
  *                outputs in the dispatch layout (may be the workspace itself)
  *   topk_weights device [T, k] fp32 gates; read only when weighted != 0
  *   weighted     0: out = bf16(sum_j y_j); else out = bf16(sum_j w_j * y_j)
- *   out          device [T, H] bf16, 16-byte aligned; overwritten
+ *   out          device [T, H] bf16, 16-byte aligned; overwritten; overlapping
+ *                expert_out is MOE_ERR_ARG
  * Sum over j = 0..k-1 in order in fp32 (weighted terms as fused
  * multiply-adds), skipping copies with slot_index -1; padding rows are never
  * read.  A token with no valid copy gets +0.
@@ -233,6 +236,9 @@ int moe_combine(moe_handle *h, const uint16_t *expert_out, const float *topk_wei
  *   gamma        device [H] bf16, 16-byte aligned
  *   eps          finite, >= 0
  *   normed       device [T, H] bf16, 16-byte aligned
+ * The outputs may not overlap expert_out, gamma or each other, nor (normed)
+ * the residual, and residual_out overlaps the residual only by being the
+ * same buffer; otherwise MOE_ERR_ARG.
  * Other arguments as moe_combine.  Requires H <= MOE_MAX_FUSED_HIDDEN.
  */
 int moe_combine_residual_rmsnorm(moe_handle *h, const uint16_t *expert_out,

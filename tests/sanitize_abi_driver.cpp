@@ -64,8 +64,12 @@ int main() {
     const int32_t T = 512, H = 128, k = 8, E = 64, ep = 8;
     // aligned host buffers stand in for device memory: the stubs never dereference them
     std::vector<int32_t> counts(ep), src(ep * T), slot(T * k), status(4);
-    alignas(16) static uint16_t x[T * H], ws[1 << 12], out[1 << 12];
-    alignas(16) static uint8_t ws8[1 << 12];
+    // stand-ins sized as the handle declares them (cap = T), so the overlap
+    // checks see the real extents
+    alignas(16) static uint16_t x[T * H], ws[ep * T * H], out[1 << 12];
+    alignas(16) static uint16_t rows[3 * T * H];     // residual | normed | gamma, disjoint
+    uint16_t *res = rows, *nrm = rows + T * H, *gam = rows + 2 * T * H;
+    alignas(16) static uint8_t ws8[ep * T * H];
     static float w[T * k], scales[ep * T];
     static int32_t ids[T * k];
     const size_t sb = moe_scratch_bytes(T, k, ep);
@@ -88,7 +92,7 @@ int main() {
     LAUNCHES(moe_combine(&h, ws, w, 1, out, nullptr), 1);
     CHECK(h.phase == 0);
     LAUNCHES(moe_dispatch(&h, x, ids, 256, 256, ws, nullptr), 1);      // 2048 copies: single launch
-    LAUNCHES(moe_combine_residual_rmsnorm(&h, ws, w, 1, out, out, out, 1e-6f, out, nullptr), 1);
+    LAUNCHES(moe_combine_residual_rmsnorm(&h, ws, w, 1, res, res, gam, 1e-6f, nrm, nullptr), 1);
     LAUNCHES(moe_dispatch(&h, x, ids, 257, 300, ws, nullptr), 2);      // first routed size
     CHECK(moe_reset(&h) == MOE_OK && h.phase == 0);
     LAUNCHES(moe_dispatch_fp8(&h, x, ids, T, T, ws8, scales, nullptr), 2);
@@ -115,6 +119,28 @@ int main() {
     CHECK(moe_combine(&g, ws, w, 1, out, nullptr) == MOE_ERR_ARG);
     LAUNCHES(moe_combine(&g, ws, nullptr, 0, out, nullptr), 1);
     for (int code = -6; code <= 1; ++code) CHECK(moe_strerror(code) != nullptr);
+
+    // buffers overlapping what a call reads are rejected before any launch
+    {
+        moe_handle o;
+        CHECK(moe_init(&o, T, H, k, E, ep, T, MOE_LAYOUT_PER_COPY, counts.data(), src.data(),
+                       slot.data(), status.data(), scratch.data(), sb) == MOE_OK);
+        CHECK(moe_dispatch(&o, ws + 8 * H, ids, 16, 16, ws, nullptr) == MOE_ERR_ARG);  // x inside ws
+        CHECK(moe_dispatch_fp8(&o, x, ids, 16, 16, ws8, reinterpret_cast<float *>(ws8 + 64),
+                               nullptr) == MOE_ERR_ARG);                            // scales inside ws8
+        LAUNCHES(moe_dispatch(&o, x, ids, 16, 16, ws, nullptr), 1);
+        CHECK(moe_combine(&o, ws, nullptr, 0, ws + 16 * H, nullptr) == MOE_ERR_ARG);  // out inside ws
+        CHECK(moe_combine_residual_rmsnorm(&o, ws, nullptr, 0, res, res, gam, 1e-6f, res + 8 * H,
+                                           nullptr) == MOE_ERR_ARG);              // normed over residual
+        CHECK(moe_combine_residual_rmsnorm(&o, ws, nullptr, 0, res, res, gam, 1e-6f, ws + H,
+                                           nullptr) == MOE_ERR_ARG);              // normed inside ws
+        CHECK(moe_combine_residual_rmsnorm(&o, ws, nullptr, 0, res, res + 8, gam, 1e-6f, nrm,
+                                           nullptr) == MOE_ERR_ARG);              // residual_out shifted
+        CHECK(o.phase == 1);
+        LAUNCHES(moe_combine_residual_rmsnorm(&o, ws, nullptr, 0, res, res, gam, 1e-6f, nrm,
+                                              nullptr), 1);                       // in-place residual
+        CHECK(o.phase == 0);
+    }
 
     // partials reduction: no handle, one launch per call, nothing for an empty batch
     // beyond the (skipped-inside) launch call, checks before anything is enqueued

@@ -245,3 +245,22 @@ def test_partials_reject_overlapping_outputs(lib):
     assert f(base, base + 2 * rows, base + 8 * rows, base + 2 * rows) == moe.MOE_ERR_ARG  # normed = residual_out
     assert f(base, base + 2 * rows, base + 2 * rows, base + 4 * rows) == moe.MOE_ERR_ARG  # residual_out over gamma
     assert f(base, base + 16, base + 8 * rows, base + 4 * rows) == moe.MOE_ERR_ARG    # residual_out partly over residual
+
+
+def test_dispatch_and_combine_reject_overlapping_buffers(lib):
+    # only rejected calls (fake addresses); workspace [4, 128, 128] bf16 = 128 KiB at FAKE
+    h = make_handle(lib)
+    far = FAKE + (1 << 24)
+    assert lib.moe_dispatch(ctypes.byref(h), FAKE + 4096, far, 8, 8, FAKE, None) == moe.MOE_ERR_ARG
+    assert lib.moe_dispatch_fp8(ctypes.byref(h), far, far + (1 << 20), 8, 8, FAKE, FAKE + 256,
+                                None) == moe.MOE_ERR_ARG                      # scales inside ws8
+    assert h.phase == 0
+    h.phase, h.num_tokens = 1, 8
+    assert lib.moe_combine(ctypes.byref(h), FAKE, None, 0, FAKE + 4096, None) == moe.MOE_ERR_ARG
+    rows = 8 * 128 * 2
+    f = lambda res, res_out, gamma, normed: lib.moe_combine_residual_rmsnorm(
+        ctypes.byref(h), FAKE, None, 0, res, res_out, gamma, 1e-6, normed, None)
+    assert f(far, far, far + 4 * rows, FAKE + 4096) == moe.MOE_ERR_ARG       # normed inside ws
+    assert f(far, far, far + 4 * rows, far + 16) == moe.MOE_ERR_ARG          # normed over residual
+    assert f(far, far + 16, far + 4 * rows, far + 2 * rows) == moe.MOE_ERR_ARG  # residual_out shifted
+    assert h.phase == 1
