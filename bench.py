@@ -409,6 +409,74 @@ def measure_partials(pw, steps: int, warmup: int, cold_iters: int = 100, seed: i
     return res
 
 
+LADDER_RUNGS = (1, 16, 32, 512, 8192)
+
+
+def measure_ladder(iters: int, warmup: int, rungs=LADDER_RUNGS, seed: int = 0) -> dict:
+    """The pages' decode ladder protocol: one handle and one workspace sized
+    once for the largest rung, each call passing its own rung (T tokens, the
+    first T of one seeded batch at H = 7168, top-8 of 256 experts over 8
+    regions, unweighted combine); per rung the dispatch -> combine roundtrip
+    (identity expert stage) timed with HIP events, p50 and mean."""
+    import numpy as np
+    import torch
+
+    import combine_moe_dispatch_03_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    T_max = max(rungs)
+    wl = synth.Workload("ladder", T=T_max, H=7168, E=256, k=8, ep=8, cap=None, R=T_max,
+                        routing="uniform", expert="identity", combine="unweighted")
+    inp = synth.make_inputs(wl, seed)
+    x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    ids = torch.from_numpy(inp.ids).to(dev)
+    probe = moe.MoeA2A(T_max, wl.H, wl.k, wl.E, wl.ep, 1, device=dev)
+    cap = int(moe.moe_route_counts(probe, ids).max().item())   # the largest rung fills most
+    del probe
+    h = moe.MoeA2A(T_max, wl.H, wl.k, wl.E, wl.ep, cap, device=dev)
+    ws = h.new_workspace()
+    out = torch.empty((T_max, wl.H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    hev = HipEvents()
+    res = {"workload": f"ladder: T in {list(rungs)} of one batch, H=7168 E=256 top-8 ep=8, "
+                       f"workspace sized once (cap={cap} rows per region), each call passing its "
+                       f"rung; dispatch -> identity expert stage -> unweighted combine",
+           "rungs": {}}
+    for T in rungs:
+        xs, ids_t, o = x[:T], ids[:T], out[:T]
+
+        def step():
+            moe.moe_dispatch(h, xs, ids_t, T, ws, stream=stream)
+            moe.moe_combine(h, ws, None, False, out=o, stream=stream)
+
+        for _ in range(warmup):
+            step()
+        code, bits = moe.moe_sync_status(h, stream)
+        if code != moe.MOE_OK:
+            raise RuntimeError(f"ladder rung {T}: device status {bits}")
+        evs = [(hev.create(), hev.create()) for _ in range(iters)]
+        for a, b in evs:
+            hev.record(a, sh)
+            step()
+            hev.record(b, sh)
+        torch.cuda.synchronize(dev)
+        ms = [hev.elapsed_ms(a, b) for a, b in evs]
+        for a, b in evs:
+            hev.destroy(a)
+            hev.destroy(b)
+        b_ = wl.algorithmic_bytes()
+        per_tok = (b_["dispatch"] + b_["combine"]) / wl.T
+        p50 = float(np.median(ms))
+        res["rungs"][str(T)] = {"roundtrip_us_p50": p50 * 1e3, "roundtrip_us_mean": float(np.mean(ms)) * 1e3,
+                                "tokens_per_s_p50": T / (p50 / 1e3),
+                                "gbs_p50": per_tok * T / (p50 / 1e3) / 1e9}
+    del ws, h
+    torch.cuda.empty_cache()
+    return res
+
+
 def region_bytes(wl, rows: int) -> dict:
     """Algorithmic bytes under the per-region layout with ``rows`` rows sent:
     dispatch reads x and ids, writes the rows, slot_index and src_index;
@@ -579,11 +647,12 @@ def main() -> int:
                          "_fp8 suffix selects a variant")
     ap.add_argument("--extras",
                     default="skewed,decode,fused,prefill_region,skewed_region,prefill_fp8,"
-                            "prefill_region_fp8,partials",
+                            "prefill_region_fp8,partials,ladder",
                     help="comma-separated workloads also measured (empty for none); a "
                          "_region suffix runs the per-region layout, _fp8 the fp8 payload; "
                          "partials is the tensor-parallel partials reduction fused with "
-                         "residual + RMSNorm")
+                         "residual + RMSNorm; ladder the roundtrip at T = 1 ... 8192 with the "
+                         "workspace sized once")
     ap.add_argument("--cold-iters", type=int, default=100,
                     help="launches timed after an untimed 1 GiB cache-evicting read, per kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -618,8 +687,12 @@ def main() -> int:
     extras = {}
     # workload names are comma-separated; a shape spec has commas of its own,
     # so split only where the next workload's name begins
-    names = re.split(r",(?=(?:tiny|decode|prefill|skewed|fused|partials|shape:))", args.extras)
+    names = re.split(r",(?=(?:tiny|decode|prefill|skewed|fused|partials|ladder|shape:))",
+                     args.extras)
     for name in [n for n in names if n and n != args.workload]:
+        if name == "ladder":
+            extras[name] = measure_ladder(max(args.steps // 2, 5), max(args.warmup // 2, 2))
+            continue
         if name == "partials":
             extras[name] = measure_partials(synth.PARTIALS, max(args.steps // 2, 5),
                                             max(args.warmup // 2, 2), args.cold_iters)
