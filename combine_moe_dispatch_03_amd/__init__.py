@@ -376,9 +376,12 @@ def moe_reset(h: MoeA2A) -> None:
 
 
 def _need_partials(partials: torch.Tensor) -> Tuple[int, int, int, int]:
-    """(P, T, H, device index) of a [P, T, H] bf16 device tensor."""
+    """(P, T, H, device index) of a [P, T, H] bf16 GPU tensor; the other
+    tensors of the call must be on the same GPU."""
     if not isinstance(partials, torch.Tensor) or partials.dim() != 3:
         raise ValueError("partials must be a [P, T, H] tensor")
+    if not partials.is_cuda:            # get_device() is -1 off the GPU
+        raise ValueError("partials must be on the GPU")
     dev = partials.get_device()
     _need(partials, "partials", torch.bfloat16, dev)
     P, T, H = partials.shape

@@ -23,11 +23,32 @@ def test_need_rejects(case, exc, text):
         moe._need(t, "x", torch.bfloat16, 0, shape=(4, 8))
 
 
+def test_partials_on_the_host_are_rejected_before_the_library():
+    # the partials tensor names the device; a host tensor must not reach a launch
+    cpu = torch.zeros(2, 4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="must be on the GPU"):
+        moe.moe_partials_reduce(cpu)
+    with pytest.raises(ValueError, match="must be on the GPU"):
+        moe.moe_partials_reduce_residual_rmsnorm(cpu, torch.zeros(4, 8, dtype=torch.bfloat16),
+                                                 torch.ones(8, dtype=torch.bfloat16), 1e-6)
+
+
 def test_explicit_stream_handles_pass_through():
     class FakeStream:
         cuda_stream = 0x1234
     assert moe._stream(FakeStream(), 0) == 0x1234
     assert moe._stream(0x5678, 0) == 0x5678
+
+
+@pytest.mark.gpu
+def test_partials_outputs_on_another_device_kind_are_rejected():
+    pd = torch.zeros(2, 4, 8, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="must be on the GPU"):
+        moe.moe_partials_reduce(pd, out=torch.zeros(4, 8, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="must be on the GPU"):
+        moe.moe_partials_reduce_residual_rmsnorm(pd, torch.zeros(4, 8, dtype=torch.bfloat16),
+                                                 torch.ones(8, dtype=torch.bfloat16, device="cuda"),
+                                                 1e-6)
 
 
 @pytest.mark.gpu
