@@ -216,6 +216,8 @@ class MoeA2A:
     def __init__(self, max_tokens: int, hidden: int, top_k: int, num_experts: int,
                  ep_size: int, max_tokens_per_rank: int, device=None, layout: str = "copy"):
         dev = torch.device(device if device is not None else "cuda")
+        if dev.type != "cuda":          # the handle's index buffers are written by kernels
+            raise ValueError(f"MoeA2A needs a GPU device, got {dev}")
         lib = library()
         self.handle = MoeHandle()
         nbytes = lib.moe_scratch_bytes(max_tokens, top_k, ep_size)

@@ -33,6 +33,12 @@ def test_partials_on_the_host_are_rejected_before_the_library():
                                                  torch.ones(8, dtype=torch.bfloat16), 1e-6)
 
 
+def test_handle_on_the_host_is_rejected():
+    # its index buffers are written by the kernels, so they must be device memory
+    with pytest.raises(ValueError, match="needs a GPU device"):
+        moe.MoeA2A(64, 128, 2, 8, 4, 128, device="cpu")
+
+
 def test_explicit_stream_handles_pass_through():
     class FakeStream:
         cuda_stream = 0x1234
