@@ -678,6 +678,10 @@ def main() -> int:
     def variant(name):
         """workload name with optional _region / _fp8 suffixes"""
         base, *mods = name.split("_")
+        if not base.startswith("shape:") and base not in synth.BY_NAME:
+            raise SystemExit(f"unknown workload {name!r}: the headline is one of "
+                             f"{sorted(synth.BY_NAME)} or shape:..., with an optional _region / "
+                             f"_fp8 suffix (partials and ladder are --extras entries)")
         wl = shape_workload(base) if base.startswith("shape:") else synth.BY_NAME[base]
         return wl, dict(layout="region" if "region" in mods else "copy",
                         payload="fp8" if "fp8" in mods else "bf16")

@@ -65,3 +65,10 @@ def test_cpu_baselines_on_the_tiny_workload():
     for res in (one, many):
         assert res["kind"] == "oracle" and res["unit"] == "tokens/s" and res["value"] > 0
     assert 1 <= bench.host_cores() <= 16
+
+
+def test_unknown_workload_exits_with_a_message():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "partials",
+                          "--extras="], capture_output=True, text=True, timeout=120)
+    assert res.returncode != 0
+    assert "unknown workload" in (res.stdout + res.stderr)
