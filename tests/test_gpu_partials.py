@@ -33,6 +33,7 @@ CASES = [
     (5, 1000, 1024),
     (2, 300, 16384),
     (4, 33, 8),
+    (64, 64, 16384),          # the most ranks at the widest fused row
 ]
 
 
@@ -61,6 +62,37 @@ def test_partials_reduce_and_fused(P, T, H):
     assert compare.rel_err(got_n, want_n) <= 1e-2
     # the residual is untouched when residual_out is another buffer
     assert np.array_equal(to_u16(rd), residual)
+
+
+def test_partials_reduce_largest_hidden():
+    # the plain reduction at MOE_MAX_HIDDEN: rows of 2 MiB over many column blocks
+    P, T, H = 3, 2, moe.MOE_MAX_HIDDEN
+    say("partials max hidden", P, T, H)
+    partials, _, _ = _inputs(P, T, H, seed=9)
+    out = moe.moe_partials_reduce(to_dev_bf16(partials))
+    torch.cuda.synchronize()
+    assert_bf16_close(to_u16(out), oracle.load().partials_reduce(partials), "partials reduce")
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_partials_random_shapes(seed):
+    rng = np.random.default_rng(1000 + seed)
+    P = int(rng.integers(1, 17))
+    T = int(rng.integers(0, 400))
+    H = int(rng.choice([8, 64, 136, 1024, 4104, 7168]))
+    eps = float(rng.choice([0.0, 1e-6, 0.5]))
+    say("partials random", seed, "P", P, "T", T, "H", H, "eps", eps)
+    orc = oracle.load()
+    partials, residual, gamma = _inputs(P, T, H, seed=seed)
+    pd = to_dev_bf16(partials)
+    out = moe.moe_partials_reduce(pd)
+    r_out, normed = moe.moe_partials_reduce_residual_rmsnorm(pd, to_dev_bf16(residual),
+                                                             to_dev_bf16(gamma), eps)
+    torch.cuda.synchronize()
+    assert_bf16_close(to_u16(out), orc.partials_reduce(partials), "partials reduce")
+    want_r, want_n = orc.partials_reduce_residual_rmsnorm(partials, residual, gamma, eps)
+    assert_bf16_close(to_u16(r_out), want_r, "residual_out")
+    assert_bf16_close(to_u16(normed), want_n, "normed")
 
 
 def test_partials_empty_batch():
