@@ -12,6 +12,9 @@
  *   every dispatched row equals its token's row;
  *   unweighted combine = (routed copies of t) * x[t];
  *   weighted combine with every gate 1/4 = (routed copies of t) / 4 * x[t].
+ * Then the handle-free partials reduction: 8 partials, partial p holding 2^p
+ * everywhere, sum exactly 255; fused with a zero residual, gamma 1 and eps 0,
+ * residual_out 255 and normed exactly 1.
  * Exit status 0 and "c consumer: ok" on success. */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -136,6 +139,36 @@ int main(void) {
     HIP_CHECK(hipMemcpy(out, dout, sizeof out, hipMemcpyDeviceToHost));
     if (check_combine("weighted", 0.25f)) return 1;
     EXPECT(moe_output_is_reduced() == 1);
+
+    /* the partials reduction: no handle, no phase */
+    {
+        enum { P = 8 };
+        static uint16_t parts[P * T * H], res[T * H], gam[H], nrm[T * H];
+        for (int p = 0; p < P; ++p)
+            for (int i = 0; i < T * H; ++i) parts[p * T * H + i] = bf16_of((float)(1 << p));
+        for (int i = 0; i < H; ++i) gam[i] = bf16_of(1.0f);
+        uint16_t *dparts, *dres, *dgam, *dnrm;
+        HIP_CHECK(hipMalloc((void **)&dparts, sizeof parts));
+        HIP_CHECK(hipMalloc((void **)&dres, sizeof res));
+        HIP_CHECK(hipMalloc((void **)&dgam, sizeof gam));
+        HIP_CHECK(hipMalloc((void **)&dnrm, sizeof nrm));
+        HIP_CHECK(hipMemcpy(dparts, parts, sizeof parts, hipMemcpyHostToDevice));
+        HIP_CHECK(hipMemcpy(dgam, gam, sizeof gam, hipMemcpyHostToDevice));
+        HIP_CHECK(hipMemset(dres, 0, sizeof res));
+        EXPECT(moe_partials_reduce(dparts, P, T, H, dparts + 8, NULL) == MOE_ERR_ARG);
+        MOE_CHECK(moe_partials_reduce(dparts, P, T, H, dout, NULL));
+        HIP_CHECK(hipMemcpy(out, dout, sizeof out, hipMemcpyDeviceToHost));
+        for (int i = 0; i < T * H; ++i) EXPECT(f32_of(out[i]) == 255.0f);
+        MOE_CHECK(moe_partials_reduce_residual_rmsnorm(dparts, P, T, H, dres, dres, dgam, 0.0f,
+                                                       dnrm, NULL));
+        HIP_CHECK(hipMemcpy(res, dres, sizeof res, hipMemcpyDeviceToHost));
+        HIP_CHECK(hipMemcpy(nrm, dnrm, sizeof nrm, hipMemcpyDeviceToHost));
+        for (int i = 0; i < T * H; ++i) EXPECT(f32_of(res[i]) == 255.0f && f32_of(nrm[i]) == 1.0f);
+        HIP_CHECK(hipFree(dparts));
+        HIP_CHECK(hipFree(dres));
+        HIP_CHECK(hipFree(dgam));
+        HIP_CHECK(hipFree(dnrm));
+    }
 
     HIP_CHECK(hipFree(dx));
     HIP_CHECK(hipFree(dws));
