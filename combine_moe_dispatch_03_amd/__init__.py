@@ -15,7 +15,7 @@ Functions carry the C names:
 
   moe_dispatch, moe_dispatch_fp8, moe_combine, moe_combine_residual_rmsnorm, moe_route_counts,
   moe_sync_status, moe_reset, moe_output_is_reduced, moe_strerror,
-  moe_workspace_bytes, moe_scratch_bytes,
+  moe_workspace_bytes, moe_scratch_bytes, moe_last_hip_error,
   moe_partials_reduce, moe_partials_reduce_residual_rmsnorm
 
 and ``MoeA2A`` owns one ``moe_handle`` plus the device buffers it binds (the
@@ -58,7 +58,7 @@ EXPORTED = (
     "moe_combine",
     "moe_combine_residual_rmsnorm", "moe_route_counts", "moe_sync_status", "moe_reset",
     "moe_output_is_reduced", "moe_strerror", "moe_partials_reduce",
-    "moe_partials_reduce_residual_rmsnorm",
+    "moe_partials_reduce_residual_rmsnorm", "moe_last_hip_error",
 )
 
 
@@ -110,6 +110,7 @@ def library() -> ctypes.CDLL:
             "moe_reset": (ctypes.c_int, [H]),
             "moe_output_is_reduced": (ctypes.c_int, []),
             "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+            "moe_last_hip_error": (ctypes.c_int, []),
             "moe_partials_reduce": (ctypes.c_int, [P, I32, I32, I32, P, P]),
             "moe_partials_reduce_residual_rmsnorm": (
                 ctypes.c_int, [P, I32, I32, I32, P, P, P, ctypes.c_float, P, P]),
@@ -206,6 +207,11 @@ def moe_output_is_reduced() -> bool:
 
 def moe_strerror(code: int) -> str:
     return library().moe_strerror(code).decode()
+
+
+def moe_last_hip_error() -> int:
+    """hipError_t behind this thread's most recent MOE_ERR_HIP (0 if none)."""
+    return library().moe_last_hip_error()
 
 
 class MoeA2A:
@@ -430,5 +436,5 @@ __all__ = [
     "MoeA2A", "MoeError", "MoeHandle", "library", "moe_dispatch", "moe_dispatch_fp8", "moe_combine",
     "moe_combine_residual_rmsnorm", "moe_route_counts", "moe_sync_status", "moe_reset",
     "moe_output_is_reduced", "moe_strerror", "moe_workspace_bytes", "moe_scratch_bytes",
-    "moe_partials_reduce", "moe_partials_reduce_residual_rmsnorm",
+    "moe_partials_reduce", "moe_partials_reduce_residual_rmsnorm", "moe_last_hip_error",
 ]

@@ -39,9 +39,24 @@ bool fused_outputs_overlap(const void *src, size_t src_bytes, const uint16_t *re
            (residual_out != residual && overlaps(residual_out, row_bytes, residual, row_bytes));
 }
 
+// The hipError_t behind the calling thread's last MOE_ERR_HIP.
+thread_local int32_t g_last_hip_error = 0;
+
 int hip_fail(moe_handle *h, hipError_t e) {
-    h->hip_error = static_cast<int32_t>(e);
+    g_last_hip_error = static_cast<int32_t>(e);
+    if (h != nullptr) h->hip_error = static_cast<int32_t>(e);
     return MOE_ERR_HIP;
+}
+
+// True if [p, p + bytes) shares a byte with any device buffer the handle
+// binds (counts, src_index, slot_index, status, scratch), which dispatch
+// writes and combine reads.
+bool overlaps_handle(const moe_handle *h, const void *p, size_t bytes) {
+    return overlaps(p, bytes, h->counts, (size_t)h->ep_size * 4) ||
+           overlaps(p, bytes, h->src_index, (size_t)h->ep_size * h->max_tokens_per_rank * 4) ||
+           overlaps(p, bytes, h->slot_index, (size_t)h->max_tokens * h->top_k * 4) ||
+           overlaps(p, bytes, h->status, 4) ||
+           overlaps(p, bytes, h->scratch, h->scratch_bytes);
 }
 
 }  // namespace
@@ -173,6 +188,26 @@ static size_t token_bytes(const moe_handle *h, int32_t num_tokens) {
 static size_t ws_bytes(const moe_handle *h, size_t elem) {
     return (size_t)h->ep_size * h->max_tokens_per_rank * h->hidden * elem;
 }
+// Bytes of the gates [T, k] fp32 of the last dispatch.
+static size_t weight_bytes(const moe_handle *h) {
+    return (size_t)h->num_tokens * h->top_k * sizeof(float);
+}
+
+// The inputs and outputs of a dispatch against each other and the handle's
+// buffers: the workspace (and fp8 scales) may not overlap x, the ids or
+// each other, and the handle's buffers, which the dispatch writes, may not
+// overlap any of them.  (x and the ids are only read: they may overlap.)
+static bool dispatch_overlaps(const moe_handle *h, const void *x, const void *ids,
+                              int32_t num_tokens, const void *ws, size_t ws_bytes,
+                              const void *scales, size_t scale_bytes) {
+    const size_t xb = (size_t)num_tokens * h->hidden * sizeof(uint16_t);
+    const size_t ib = (size_t)num_tokens * h->top_k * sizeof(int32_t);
+    return overlaps(ws, ws_bytes, x, xb) || overlaps(ws, ws_bytes, ids, ib) ||
+           overlaps(scales, scale_bytes, x, xb) || overlaps(scales, scale_bytes, ids, ib) ||
+           overlaps(scales, scale_bytes, ws, ws_bytes) || overlaps_handle(h, x, xb) ||
+           overlaps_handle(h, ids, ib) || overlaps_handle(h, ws, ws_bytes) ||
+           overlaps_handle(h, scales, scale_bytes);
+}
 
 static int dispatch_launch(moe_handle *h, moe::DispatchArgs da, const int32_t *topk_ids,
                            int32_t num_tokens, int32_t R, hipStream_t s) {
@@ -197,7 +232,8 @@ int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
     const int32_t R = runtime_max_tokens_per_rank;
     int rc = dispatch_checks(h, x, topk_ids, num_tokens, R, workspace);
     if (rc != MOE_OK) return rc;
-    if (overlaps(workspace, ws_bytes(h, sizeof(uint16_t)), x, token_bytes(h, num_tokens)))
+    if (dispatch_overlaps(h, x, topk_ids, num_tokens, workspace, ws_bytes(h, sizeof(uint16_t)),
+                          nullptr, 0))
         return MOE_ERR_ARG;
     const moe::DispatchArgs da = dispatch_args(h, x, topk_ids, num_tokens, workspace,
                                                moe::plan_route(num_tokens), 0);
@@ -212,9 +248,8 @@ int moe_dispatch_fp8(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
     if (rc != MOE_OK) return rc;
     if (!dev_ok(scales, 4) || h->hidden > MOE_MAX_FUSED_HIDDEN) return MOE_ERR_ARG;
     const size_t scale_bytes = (size_t)h->ep_size * h->max_tokens_per_rank * sizeof(float);
-    if (overlaps(workspace, ws_bytes(h, 1), x, token_bytes(h, num_tokens)) ||
-        overlaps(scales, scale_bytes, x, token_bytes(h, num_tokens)) ||
-        overlaps(scales, scale_bytes, workspace, ws_bytes(h, 1)))
+    if (dispatch_overlaps(h, x, topk_ids, num_tokens, workspace, ws_bytes(h, 1), scales,
+                          scale_bytes))
         return MOE_ERR_ARG;
     moe::DispatchArgs da = dispatch_args(h, x, topk_ids, num_tokens, nullptr,
                                          moe::plan_route(num_tokens), 0);
@@ -229,6 +264,8 @@ int moe_route_counts(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens,
     if (h->phase != 0) return MOE_ERR_PHASE;
     if (num_tokens < 0 || num_tokens > h->max_tokens) return MOE_ERR_ARG;
     if (num_tokens > 0 && !dev_ok(topk_ids, 4)) return MOE_ERR_ARG;
+    if (overlaps_handle(h, topk_ids, (size_t)num_tokens * h->top_k * sizeof(int32_t)))
+        return MOE_ERR_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     moe::RoutePlan plan;
     int rc = route(h, topk_ids, num_tokens, s, &plan);
@@ -271,7 +308,9 @@ int moe_combine(moe_handle *h, const uint16_t *expert_out, const float *topk_wei
     int rc = combine_common(h, expert_out, topk_weights, weighted);
     if (rc != MOE_OK) return rc;
     if (h->num_tokens > 0 && !dev_ok(out, 16)) return MOE_ERR_ARG;
-    if (overlaps(out, token_bytes(h, h->num_tokens), expert_out, ws_bytes(h, sizeof(uint16_t))))
+    const size_t ob = token_bytes(h, h->num_tokens);
+    if (overlaps(out, ob, expert_out, ws_bytes(h, sizeof(uint16_t))) ||
+        (weighted && overlaps(out, ob, topk_weights, weight_bytes(h))) || overlaps_handle(h, out, ob))
         return MOE_ERR_ARG;
     moe::CombineArgs ca = combine_args(h, expert_out, topk_weights, weighted);
     ca.out = out;
@@ -293,9 +332,12 @@ int moe_combine_residual_rmsnorm(moe_handle *h, const uint16_t *expert_out,
     if (h->num_tokens > 0 && (!dev_ok(residual, 16) || !dev_ok(residual_out, 16) ||
                               !dev_ok(gamma, 16) || !dev_ok(normed, 16)))
         return MOE_ERR_ARG;
+    const size_t ob = token_bytes(h, h->num_tokens);
     if (fused_outputs_overlap(expert_out, ws_bytes(h, sizeof(uint16_t)), residual, residual_out,
-                              gamma, normed, token_bytes(h, h->num_tokens),
-                              (size_t)h->hidden * sizeof(uint16_t)))
+                              gamma, normed, ob, (size_t)h->hidden * sizeof(uint16_t)) ||
+        (weighted && (overlaps(residual_out, ob, topk_weights, weight_bytes(h)) ||
+                      overlaps(normed, ob, topk_weights, weight_bytes(h)))) ||
+        overlaps_handle(h, residual_out, ob) || overlaps_handle(h, normed, ob))
         return MOE_ERR_ARG;
     moe::CombineArgs ca = combine_args(h, expert_out, topk_weights, weighted);
     ca.residual = residual;
@@ -340,8 +382,8 @@ int moe_partials_reduce(const uint16_t *partials, int32_t num_partials, int32_t 
     if (overlaps(out, row_bytes, partials, row_bytes * num_partials)) return MOE_ERR_ARG;
     moe::CombineArgs ca = partials_args(partials, num_partials, num_tokens, hidden);
     ca.out = out;
-    return moe::launch_combine(ca, false, static_cast<hipStream_t>(stream)) == hipSuccess
-               ? MOE_OK : MOE_ERR_HIP;
+    const hipError_t e = moe::launch_combine(ca, false, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(nullptr, e);
 }
 
 int moe_partials_reduce_residual_rmsnorm(const uint16_t *partials, int32_t num_partials,
@@ -365,8 +407,8 @@ int moe_partials_reduce_residual_rmsnorm(const uint16_t *partials, int32_t num_p
     ca.gamma = gamma;
     ca.normed = normed;
     ca.eps = eps;
-    return moe::launch_combine(ca, true, static_cast<hipStream_t>(stream)) == hipSuccess
-               ? MOE_OK : MOE_ERR_HIP;
+    const hipError_t e = moe::launch_combine(ca, true, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(nullptr, e);
 }
 
 int moe_sync_status(moe_handle *h, void *stream, int32_t *bits) {
@@ -394,6 +436,8 @@ int moe_reset(moe_handle *h) {
 }
 
 int moe_output_is_reduced(void) { return 1; }
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
 
 const char *moe_strerror(int code) {
     switch (code) {

@@ -901,21 +901,10 @@ void launch_combine_vpt(const CombineArgs &a, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
-RoutePlan plan_route(int32_t num_tokens) {
-    RoutePlan p;
-    p.tokens_per_chunk = num_tokens > 0 ? (num_tokens + kMaxChunks - 1) / kMaxChunks : 1;
-    p.n_chunks = num_tokens > 0 ? (num_tokens + p.tokens_per_chunk - 1) / p.tokens_per_chunk : 0;
-    return p;
-}
-
 hipError_t launch_route(const RouteArgs &a, int32_t n_chunks, hipStream_t s) {
     if (n_chunks > 0)
         hipLaunchKernelGGL(route_rank_kernel, dim3(n_chunks), dim3(kThreads), 0, s, a);
     return hipGetLastError();
-}
-
-bool dispatch_is_small(int32_t num_tokens, int32_t top_k) {
-    return (int64_t)num_tokens * top_k <= kSmallItems;
 }
 
 hipError_t launch_dispatch_copy(const DispatchArgs &args, hipStream_t s) {

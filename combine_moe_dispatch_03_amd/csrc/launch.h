@@ -1,5 +1,8 @@
 // Internal interface between the C ABI (api.hip) and the gfx950 kernels
 // (kernels.hip).  Not installed; the public surface is include/moe_a2a.h.
+// The planning functions are inline so that every user of this header (the
+// library, and the host-only sanitizer driver that stands in for the
+// kernels) computes the same plan.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,14 +21,22 @@ constexpr int kMaxChunks = 64;
 constexpr int kSmallItems = 2048;
 
 // True when dispatch uses the single-launch path.
-bool dispatch_is_small(int32_t num_tokens, int32_t top_k);
+inline bool dispatch_is_small(int32_t num_tokens, int32_t top_k) {
+    return (int64_t)num_tokens * top_k <= kSmallItems;
+}
 
 struct RoutePlan {
     int32_t tokens_per_chunk;
     int32_t n_chunks;
 };
 
-RoutePlan plan_route(int32_t num_tokens);
+// Chunks of whole tokens for the routing kernel: at most kMaxChunks.
+inline RoutePlan plan_route(int32_t num_tokens) {
+    RoutePlan p;
+    p.tokens_per_chunk = num_tokens > 0 ? (num_tokens + kMaxChunks - 1) / kMaxChunks : 1;
+    p.n_chunks = num_tokens > 0 ? (num_tokens + p.tokens_per_chunk - 1) / p.tokens_per_chunk : 0;
+    return p;
+}
 
 // Scratch layout: rank[max_tokens * k] then hist[kMaxChunks * ep].
 inline int32_t *scratch_rank(void *scratch) { return static_cast<int32_t *>(scratch); }

@@ -60,7 +60,8 @@ extern "C" {
 #define MOE_ERR_PHASE     (-2)  /* dispatch twice, or combine without dispatch */
 #define MOE_ERR_OVERFLOW  (-3)  /* a region received more than cap copies    */
 #define MOE_ERR_EXPERT_ID (-4)  /* an expert id outside [-1, E)              */
-#define MOE_ERR_HIP       (-5)  /* a HIP runtime call failed (see hip_error) */
+#define MOE_ERR_HIP       (-5)  /* a HIP runtime call failed (see hip_error, */
+                                /* moe_last_hip_error)                     */
 
 /* workspace layouts (moe_init) */
 #define MOE_LAYOUT_PER_COPY   0     /* one row per routed copy (t, j)          */
@@ -109,11 +110,15 @@ typedef struct moe_handle {
     int32_t hip_error;           /* hipError_t behind the last MOE_ERR_HIP     */
 } moe_handle;
 
-/* Bytes of the padded workspace [ep, cap, H] bf16. */
+/* Bytes of the padded workspace [ep, cap, H] bf16: the receive buffer
+ * [A2A] "The adapter" sizes once from the ladder maximum ([ep_size,
+ * max_tokens_per_rank, hidden]).  Returns 0 for a non-positive argument. */
 size_t moe_workspace_bytes(int32_t ep_size, int32_t max_tokens_per_rank, int32_t hidden);
 
 /* Bytes of routing scratch a handle needs (per-copy ranks and per-chunk
- * region histograms); returns 0 for arguments outside the limits. */
+ * region histograms of the routing kernel); returns 0 for arguments outside
+ * the limits.  Any contents are accepted: the routing kernel writes what the
+ * copy kernel reads. */
 size_t moe_scratch_bytes(int32_t max_tokens, int32_t top_k, int32_t ep_size);
 
 /*
@@ -139,7 +144,9 @@ size_t moe_scratch_bytes(int32_t max_tokens, int32_t top_k, int32_t ep_size);
  *                        so cap = max_tokens always suffices.
  *   counts, src_index, slot_index, status, scratch: device, 4-byte aligned,
  *                        sized as in moe_handle; *status must be 0 before
- *                        the first dispatch (zero-filled memory)
+ *                        the first dispatch (zero-filled memory); the scratch
+ *                        belongs to this handle (two handles in flight at
+ *                        once must not share it)
  *   scratch_bytes        >= moe_scratch_bytes(max_tokens, top_k, ep_size)
  * Returns MOE_OK or MOE_ERR_ARG.  No HIP call is made.
  */
@@ -168,7 +175,10 @@ int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
  * Copies past cap are dropped (slot_index -1) and set MOE_STATUS_OVERFLOW;
  * ids outside [-1, E) are dropped and set MOE_STATUS_EXPERT_ID; both are
  * reported by moe_sync_status.
- * A workspace overlapping x is MOE_ERR_ARG.
+ * Batches of at most 2048 routed copies (T * k) run as one kernel launch;
+ * larger ones run the routing kernel, then the copy kernel.
+ * The workspace must not overlap x or topk_ids, and none of the three may
+ * overlap the handle's device buffers (MOE_ERR_ARG).
  * Returns MOE_OK, MOE_ERR_ARG, MOE_ERR_PHASE (already dispatched) or
  * MOE_ERR_HIP (launch failed).  On success the handle is "dispatched".
  */
@@ -192,7 +202,8 @@ int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
  *              the scale of row (r, s), written for valid rows only
  * Other arguments, outputs (counts, slot_index, src_index), errors and the
  * phase as moe_dispatch; requires H <= MOE_MAX_FUSED_HIDDEN; workspace,
- * scales and x must not overlap (MOE_ERR_ARG).  The combine
+ * scales, x and topk_ids must not overlap each other (x and topk_ids
+ * excepted) or the handle's device buffers (MOE_ERR_ARG).  The combine
  * that follows reads bf16 expert outputs from a buffer of the same
  * [ep, cap, H] layout (the experts dequantise and write it).
  */
@@ -209,7 +220,8 @@ int moe_dispatch_fp8(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
  *   topk_weights device [T, k] fp32 gates; read only when weighted != 0
  *   weighted     0: out = bf16(sum_j y_j); else out = bf16(sum_j w_j * y_j)
  *   out          device [T, H] bf16, 16-byte aligned; overwritten; overlapping
- *                expert_out is MOE_ERR_ARG
+ *                expert_out, topk_weights (when weighted) or the handle's
+ *                device buffers is MOE_ERR_ARG
  * Sum over j = 0..k-1 in order in fp32 (weighted terms as fused
  * multiply-adds), skipping copies with slot_index -1; padding rows are never
  * read.  A token with no valid copy gets +0.
@@ -236,9 +248,10 @@ int moe_combine(moe_handle *h, const uint16_t *expert_out, const float *topk_wei
  *   gamma        device [H] bf16, 16-byte aligned
  *   eps          finite, >= 0
  *   normed       device [T, H] bf16, 16-byte aligned
- * The outputs may not overlap expert_out, gamma or each other, nor (normed)
- * the residual, and residual_out overlaps the residual only by being the
- * same buffer; otherwise MOE_ERR_ARG.
+ * The outputs may not overlap expert_out, gamma, topk_weights (when
+ * weighted), the handle's device buffers or each other, nor (normed) the
+ * residual, and residual_out overlaps the residual only by being the same
+ * buffer; otherwise MOE_ERR_ARG.
  * Other arguments as moe_combine.  Requires H <= MOE_MAX_FUSED_HIDDEN.
  */
 int moe_combine_residual_rmsnorm(moe_handle *h, const uint16_t *expert_out,
@@ -263,8 +276,8 @@ int moe_combine_residual_rmsnorm(moe_handle *h, const uint16_t *expert_out,
  *   out          device [T, H] bf16, 16-byte aligned; overwritten; overlapping
  *                partials is MOE_ERR_ARG
  * Asynchronous on `stream`.  Returns MOE_OK, MOE_ERR_ARG (checked before
- * anything is enqueued) or MOE_ERR_HIP (the launch failed; no handle keeps
- * the HIP code, hipGetLastError has already been read).
+ * anything is enqueued) or MOE_ERR_HIP (the launch failed; the hipError_t is
+ * kept for moe_last_hip_error, as no handle holds it).
  */
 int moe_partials_reduce(const uint16_t *partials, int32_t num_partials, int32_t num_tokens,
                         int32_t hidden, uint16_t *out, void *stream);
@@ -293,7 +306,9 @@ int moe_partials_reduce_residual_rmsnorm(const uint16_t *partials, int32_t num_p
 
 /*
  * moe_route_counts -- only the per-region copy counts of a routing, so a
- * caller can size max_tokens_per_rank before allocating the workspace.
+ * caller can size max_tokens_per_rank before allocating the workspace
+ * ([A2A] "The adapter": the receive is sized once, from the largest batch;
+ * the counts are the dispatch's own, computed by its routing kernel).
  * Writes counts (and routing scratch); leaves the phase idle.
  *   topk_ids   device [T, k] int32;  0 <= num_tokens <= max_tokens
  * Returns MOE_OK, MOE_ERR_ARG, MOE_ERR_PHASE (a dispatch is pending) or
@@ -304,6 +319,9 @@ int moe_route_counts(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens,
 
 /*
  * moe_sync_status -- wait for `stream`, read and clear the device status.
+ * The device-side checks stand in for the host asserts of [A2A] "The
+ * adapter" (ids outside the experts, a receive region past its capacity),
+ * which a one-sided kernel cannot raise itself.
  *   bits  host, optional: receives the MOE_STATUS_* bits that were set
  * Returns MOE_ERR_EXPERT_ID or MOE_ERR_OVERFLOW if a kernel flagged one since
  * the last call (expert id first), MOE_OK otherwise, MOE_ERR_HIP on a
@@ -311,7 +329,10 @@ int moe_route_counts(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens,
  */
 int moe_sync_status(moe_handle *h, void *stream, int32_t *bits);
 
-/* moe_reset -- return a dispatched handle to idle without combining. */
+/* moe_reset -- return a dispatched handle to idle without combining: the
+ * way out of the dispatch -> combine phase contract of [A2A] "The adapter"
+ * when a dispatch is abandoned (e.g. after a device-detected error).
+ * Returns MOE_OK, or MOE_ERR_ARG for a null handle. */
 int moe_reset(moe_handle *h);
 
 /* moe_output_is_reduced -- always 1: the combine output is final and must not
@@ -320,6 +341,12 @@ int moe_output_is_reduced(void);
 
 /* moe_strerror -- static text for a return code. */
 const char *moe_strerror(int code);
+
+/* moe_last_hip_error -- the hipError_t behind the most recent MOE_ERR_HIP
+ * returned to the calling thread by any call of this library (0 if none);
+ * the handle-free calls (moe_partials_reduce*) have no other place to keep
+ * it.  Per thread; not cleared by later successful calls. */
+int moe_last_hip_error(void);
 
 #ifdef __cplusplus
 }

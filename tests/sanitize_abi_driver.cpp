@@ -20,15 +20,8 @@ static bool in_scratch(const int32_t *p, int64_t n) {
 
 namespace moe {
 static int launches = 0;
-RoutePlan plan_route(int32_t num_tokens) {
-    RoutePlan p;
-    p.tokens_per_chunk = num_tokens > 0 ? (num_tokens + kMaxChunks - 1) / kMaxChunks : 1;
-    p.n_chunks = num_tokens > 0 ? (num_tokens + p.tokens_per_chunk - 1) / p.tokens_per_chunk : 0;
-    return p;
-}
-bool dispatch_is_small(int32_t num_tokens, int32_t top_k) {
-    return (int64_t)num_tokens * top_k <= kSmallItems;
-}
+static int fail_partials = 0;     // a partials launch of this many rows reports a HIP error
+// plan_route and dispatch_is_small are the library's own (inline in launch.h)
 hipError_t launch_route(const RouteArgs &a, int32_t n_chunks, hipStream_t) {
     if (n_chunks < 1 || n_chunks > kMaxChunks || a.n_items < 1) std::abort();
     if (!in_scratch(a.rank, a.n_items) || !in_scratch(a.hist, (int64_t)n_chunks * a.ep)) std::abort();
@@ -51,6 +44,7 @@ hipError_t launch_combine(const CombineArgs &a, bool fused, hipStream_t) {
                        (int64_t)a.k * a.T > INT32_MAX || (a.T > 0 && (!a.y || (!fused && !a.out)))))
         std::abort();
     if (!a.partials && !a.slot_index) std::abort();
+    if (a.partials && a.k == fail_partials) return hipErrorInvalidValue;
     ++launches;
     return hipSuccess;
 }
@@ -128,8 +122,30 @@ int main() {
         CHECK(moe_dispatch(&o, ws + 8 * H, ids, 16, 16, ws, nullptr) == MOE_ERR_ARG);  // x inside ws
         CHECK(moe_dispatch_fp8(&o, x, ids, 16, 16, ws8, reinterpret_cast<float *>(ws8 + 64),
                                nullptr) == MOE_ERR_ARG);                            // scales inside ws8
+        CHECK(moe_dispatch(&o, x, reinterpret_cast<const int32_t *>(ws), 16, 16, ws, nullptr) ==
+              MOE_ERR_ARG);                                                         // ids inside ws
+        CHECK(moe_dispatch(&o, reinterpret_cast<const uint16_t *>(scratch.data()), ids, 16, 16, ws,
+                           nullptr) == MOE_ERR_ARG);                                // x over scratch
+        CHECK(moe_dispatch(&o, x, slot.data(), 16, 16, ws, nullptr) == MOE_ERR_ARG);  // ids = slot_index
+        CHECK(moe_dispatch(&o, x, ids, 16, 16, reinterpret_cast<uint16_t *>(src.data()), nullptr) ==
+              MOE_ERR_ARG);                                                         // ws over src_index
+        CHECK(moe_dispatch_fp8(&o, x, ids, 16, 16, ws8, reinterpret_cast<float *>(counts.data()),
+                               nullptr) == MOE_ERR_ARG);                            // scales = counts
+        CHECK(moe_route_counts(&o, counts.data(), 1, nullptr) == MOE_ERR_ARG);     // ids = counts
+        CHECK(o.phase == 0);
         LAUNCHES(moe_dispatch(&o, x, ids, 16, 16, ws, nullptr), 1);
         CHECK(moe_combine(&o, ws, nullptr, 0, ws + 16 * H, nullptr) == MOE_ERR_ARG);  // out inside ws
+        CHECK(moe_combine(&o, ws, reinterpret_cast<const float *>(out), 1, out, nullptr) ==
+              MOE_ERR_ARG);                                                         // out over weights
+        CHECK(moe_combine(&o, ws, nullptr, 0, reinterpret_cast<uint16_t *>(slot.data()), nullptr) ==
+              MOE_ERR_ARG);                                                         // out over slot_index
+        CHECK(moe_combine(&o, ws, nullptr, 0, reinterpret_cast<uint16_t *>(status.data()), nullptr) ==
+              MOE_ERR_ARG);                                                         // out over status
+        CHECK(moe_combine_residual_rmsnorm(&o, ws, reinterpret_cast<const float *>(nrm), 1, res, res,
+                                           gam, 1e-6f, nrm, nullptr) == MOE_ERR_ARG);  // normed over weights
+        CHECK(moe_combine_residual_rmsnorm(&o, ws, nullptr, 0, res,
+                                           reinterpret_cast<uint16_t *>(scratch.data()), gam, 1e-6f,
+                                           nrm, nullptr) == MOE_ERR_ARG);         // residual_out over scratch
         CHECK(moe_combine_residual_rmsnorm(&o, ws, nullptr, 0, res, res, gam, 1e-6f, res + 8 * H,
                                            nullptr) == MOE_ERR_ARG);              // normed over residual
         CHECK(moe_combine_residual_rmsnorm(&o, ws, nullptr, 0, res, res, gam, 1e-6f, ws + H,
@@ -170,6 +186,14 @@ int main() {
         CHECK(moe_partials_reduce_residual_rmsnorm(parts, P, Tn, Hn, res, res, nrm, 1e-6f, nrm,
                                                    nullptr) == MOE_ERR_ARG);
     }
+    // a failed partials launch keeps its hipError_t for moe_last_hip_error
+    moe::fail_partials = 5;
+    CHECK(moe_partials_reduce(ws, 5, 4, H, out, nullptr) == MOE_ERR_HIP);
+    CHECK(moe_last_hip_error() == (int)hipErrorInvalidValue);
+    CHECK(moe_partials_reduce_residual_rmsnorm(ws, 5, 4, H, out, out, out + 1024, 1e-6f, out + 2048,
+                                               nullptr) == MOE_ERR_HIP);
+    CHECK(moe_last_hip_error() == (int)hipErrorInvalidValue);
+    moe::fail_partials = 0;
     std::printf("sanitized ABI driver: ok (%d launches, sync_status rc %d)\n", moe::launches, rc);
     return 0;
 }
