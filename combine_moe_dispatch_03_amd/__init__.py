@@ -41,6 +41,8 @@ MOE_ERR_PHASE = -2
 MOE_ERR_OVERFLOW = -3
 MOE_ERR_EXPERT_ID = -4
 MOE_ERR_HIP = -5
+MOE_ERR_NOALLOC_SIZE = -6
+MOE_NOALLOC_MAX_ITEMS = 1048576
 MOE_LAYOUT_PER_COPY = 0
 MOE_LAYOUT_PER_REGION = 1
 LAYOUTS = {"copy": MOE_LAYOUT_PER_COPY, "region": MOE_LAYOUT_PER_REGION}
@@ -58,7 +60,7 @@ EXPORTED = (
     "moe_combine",
     "moe_combine_residual_rmsnorm", "moe_route_counts", "moe_sync_status", "moe_reset",
     "moe_output_is_reduced", "moe_strerror", "moe_partials_reduce",
-    "moe_partials_reduce_residual_rmsnorm", "moe_last_hip_error",
+    "moe_partials_reduce_residual_rmsnorm", "moe_last_hip_error", "moe_dispatch_noalloc",
 )
 
 
@@ -102,6 +104,7 @@ def library() -> ctypes.CDLL:
             "moe_init": (ctypes.c_int, [H, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, SZ]),
             "moe_dispatch": (ctypes.c_int, [H, P, P, I32, I32, P, P]),
             "moe_dispatch_fp8": (ctypes.c_int, [H, P, P, I32, I32, P, P, P]),
+            "moe_dispatch_noalloc": (ctypes.c_int, [H, P, P, I32, I32, P, P]),
             "moe_combine": (ctypes.c_int, [H, P, P, I32, P, P]),
             "moe_combine_residual_rmsnorm": (ctypes.c_int,
                                              [H, P, P, I32, P, P, P, ctypes.c_float, P, P]),
@@ -220,7 +223,8 @@ class MoeA2A:
     copy) or "region" (one row per token and destination region)."""
 
     def __init__(self, max_tokens: int, hidden: int, top_k: int, num_experts: int,
-                 ep_size: int, max_tokens_per_rank: int, device=None, layout: str = "copy"):
+                 ep_size: int, max_tokens_per_rank: int, device=None, layout: str = "copy",
+                 scratch: bool = True):
         dev = torch.device(device if device is not None else "cuda")
         if dev.type != "cuda":          # the handle's index buffers are written by kernels
             raise ValueError(f"MoeA2A needs a GPU device, got {dev}")
@@ -234,14 +238,15 @@ class MoeA2A:
         self.src_index = torch.full((ep_size * max_tokens_per_rank,), -1, **i32)
         self.slot_index = torch.full((max_tokens * top_k,), -1, **i32)
         self.status = torch.zeros(1, **i32)
-        self.scratch = torch.zeros((nbytes + 3) // 4, **i32)
+        # scratch=False binds none: the handle then serves moe_dispatch_noalloc only
+        self.scratch = torch.zeros((nbytes + 3) // 4, **i32) if scratch else None
         if layout not in LAYOUTS:
             raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
         _check(lib.moe_init(ctypes.byref(self.handle), max_tokens, hidden, top_k, num_experts,
                             ep_size, max_tokens_per_rank, LAYOUTS[layout],
                             _ptr(self.counts), _ptr(self.src_index),
                             _ptr(self.slot_index), _ptr(self.status), _ptr(self.scratch),
-                            self.scratch.numel() * 4), "moe_init")
+                            self.scratch.numel() * 4 if scratch else 0), "moe_init")
         self.device = dev
         self.device_index = dev.index if dev.index is not None else torch.cuda.current_device()
         self.ref = ctypes.byref(self.handle)     # built once, passed on ctypes calls
@@ -298,6 +303,20 @@ def moe_dispatch(h: MoeA2A, x: torch.Tensor, topk_ids: torch.Tensor,
     _need(workspace, "workspace", torch.bfloat16, h.device_index, numel=h.workspace_numel)
     _check(_fast().dispatch(h.addr, _ptr(x), _ptr(topk_ids), T, runtime_max_tokens_per_rank,
                             _ptr(workspace), _stream(stream, h.device_index)), "moe_dispatch")
+
+
+def moe_dispatch_noalloc(h: MoeA2A, x: torch.Tensor, topk_ids: torch.Tensor,
+                         runtime_max_tokens_per_rank: int, workspace: torch.Tensor,
+                         stream=None) -> None:
+    """moe_dispatch with the routing scratch taken from the library's static
+    per-GPU array (no allocation anywhere in the call)."""
+    T = x.shape[0] if x.dim() == 2 else 0
+    _need(x, "x", torch.bfloat16, h.device_index, shape=(T, h.hidden))
+    _need(topk_ids, "topk_ids", torch.int32, h.device_index, shape=(T, h.top_k))
+    _need(workspace, "workspace", torch.bfloat16, h.device_index, numel=h.workspace_numel)
+    _check(library().moe_dispatch_noalloc(h.ref, _ptr(x), _ptr(topk_ids), T,
+                                          runtime_max_tokens_per_rank, _ptr(workspace),
+                                          _stream(stream, h.device_index)), "moe_dispatch_noalloc")
 
 
 def moe_dispatch_fp8(h: MoeA2A, x: torch.Tensor, topk_ids: torch.Tensor,
@@ -433,7 +452,8 @@ def moe_partials_reduce_residual_rmsnorm(partials: torch.Tensor, residual: torch
 
 
 __all__ = [
-    "MoeA2A", "MoeError", "MoeHandle", "library", "moe_dispatch", "moe_dispatch_fp8", "moe_combine",
+    "MoeA2A", "MoeError", "MoeHandle", "library", "moe_dispatch", "moe_dispatch_noalloc",
+    "moe_dispatch_fp8", "moe_combine",
     "moe_combine_residual_rmsnorm", "moe_route_counts", "moe_sync_status", "moe_reset",
     "moe_output_is_reduced", "moe_strerror", "moe_workspace_bytes", "moe_scratch_bytes",
     "moe_partials_reduce", "moe_partials_reduce_residual_rmsnorm", "moe_last_hip_error",

@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "launch.h"
 #include "moe_a2a.h"
 
@@ -59,6 +61,38 @@ bool overlaps_handle(const moe_handle *h, const void *p, size_t bytes) {
            overlaps(p, bytes, h->scratch, h->scratch_bytes);
 }
 
+// Routing scratch of moe_dispatch_noalloc: one array per GPU, in the
+// library's device code (no allocation).  Holds the per-copy ranks of up to
+// MOE_NOALLOC_MAX_ITEMS routed copies, then the per-chunk region histograms
+// (kMaxChunks x MOE_MAX_EP int32).
+constexpr size_t kStaticRankBytes = (size_t)MOE_NOALLOC_MAX_ITEMS * sizeof(int32_t);
+constexpr size_t kStaticScratchBytes =
+    kStaticRankBytes + (size_t)moe::kMaxChunks * MOE_MAX_EP * sizeof(int32_t);
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// Device addresses of `scratch`, one per GPU, looked up on the first
+// moe_dispatch_noalloc call with that GPU current.  In host code `scratch`
+// names a host-side stand-in, so kernels get these addresses instead.
+constexpr int kMaxDevices = 64;
+void *g_scratch_dev[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t static_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,10 +129,13 @@ int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
     if ((int64_t)ep_size * max_tokens_per_rank > INT32_MAX) return MOE_ERR_ARG;
     if ((int64_t)max_tokens * top_k > INT32_MAX) return MOE_ERR_ARG;
     if (!dev_ok(counts, 4) || !dev_ok(src_index, 4) || !dev_ok(slot_index, 4) ||
-        !dev_ok(status, 4) || !dev_ok(scratch, 4))
+        !dev_ok(status, 4))
         return MOE_ERR_ARG;
     const size_t need = moe_scratch_bytes(max_tokens, top_k, ep_size);
-    if (need == 0 || scratch_bytes < need) return MOE_ERR_ARG;
+    if (need == 0) return MOE_ERR_ARG;
+    // no scratch (NULL, 0): a handle for moe_dispatch_noalloc only
+    if (!(scratch == nullptr && scratch_bytes == 0) && (!dev_ok(scratch, 4) || scratch_bytes < need))
+        return MOE_ERR_ARG;
 
     memset(h, 0, sizeof *h);
     h->max_tokens = max_tokens;
@@ -118,13 +155,25 @@ int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
     return MOE_OK;
 }
 
-static int route(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens, hipStream_t s,
-                 moe::RoutePlan *plan_out) {
+// The routing scratch of a call: the handle's, laid out for its largest
+// batch, or the library's static array (moe_dispatch_noalloc), laid out for
+// MOE_NOALLOC_MAX_ITEMS copies.
+struct Scratch {
+    void *base;
+    int64_t max_items;
+};
+
+static Scratch handle_scratch(const moe_handle *h) {
+    return Scratch{h->scratch, (int64_t)h->max_tokens * h->top_k};
+}
+
+static int route(moe_handle *h, const Scratch &sc, const int32_t *topk_ids, int32_t num_tokens,
+                 hipStream_t s, moe::RoutePlan *plan_out) {
     const moe::RoutePlan plan = moe::plan_route(num_tokens);
     moe::RouteArgs ra;
     ra.ids = topk_ids;
-    ra.rank = moe::scratch_rank(h->scratch);
-    ra.hist = moe::scratch_hist(h->scratch, (int64_t)h->max_tokens * h->top_k);
+    ra.rank = moe::scratch_rank(sc.base);
+    ra.hist = moe::scratch_hist(sc.base, sc.max_items);
     ra.status = h->status;
     ra.n_items = (int64_t)num_tokens * h->top_k;
     ra.items_per_chunk = plan.tokens_per_chunk * h->top_k;
@@ -139,14 +188,14 @@ static int route(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens, hip
     return MOE_OK;
 }
 
-static moe::DispatchArgs dispatch_args(moe_handle *h, const uint16_t *x, const int32_t *ids,
-                                       int32_t T, uint16_t *ws, const moe::RoutePlan &plan,
-                                       int32_t count_only) {
+static moe::DispatchArgs dispatch_args(moe_handle *h, const Scratch &sc, const uint16_t *x,
+                                       const int32_t *ids, int32_t T, uint16_t *ws,
+                                       const moe::RoutePlan &plan, int32_t count_only) {
     moe::DispatchArgs da;
     da.x = x;
     da.ids = ids;
-    da.rank = moe::scratch_rank(h->scratch);
-    da.hist = moe::scratch_hist(h->scratch, (int64_t)h->max_tokens * h->top_k);
+    da.rank = moe::scratch_rank(sc.base);
+    da.hist = moe::scratch_hist(sc.base, sc.max_items);
     da.ws = ws;
     da.counts = h->counts;
     da.slot_index = h->slot_index;
@@ -209,11 +258,11 @@ static bool dispatch_overlaps(const moe_handle *h, const void *x, const void *id
            overlaps_handle(h, scales, scale_bytes);
 }
 
-static int dispatch_launch(moe_handle *h, moe::DispatchArgs da, const int32_t *topk_ids,
-                           int32_t num_tokens, int32_t R, hipStream_t s) {
+static int dispatch_launch(moe_handle *h, const Scratch &sc, moe::DispatchArgs da,
+                           const int32_t *topk_ids, int32_t num_tokens, int32_t R, hipStream_t s) {
     moe::RoutePlan plan = moe::plan_route(num_tokens);
     if (!moe::dispatch_is_small(num_tokens, h->top_k)) {   // small batches need no routing kernel
-        int rc = route(h, topk_ids, num_tokens, s, &plan);
+        int rc = route(h, sc, topk_ids, num_tokens, s, &plan);
         if (rc != MOE_OK) return rc;
     }
     da.tokens_per_chunk = plan.tokens_per_chunk;
@@ -232,12 +281,32 @@ int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
     const int32_t R = runtime_max_tokens_per_rank;
     int rc = dispatch_checks(h, x, topk_ids, num_tokens, R, workspace);
     if (rc != MOE_OK) return rc;
+    if (h->scratch == nullptr) return MOE_ERR_ARG;         // a handle for moe_dispatch_noalloc
     if (dispatch_overlaps(h, x, topk_ids, num_tokens, workspace, ws_bytes(h, sizeof(uint16_t)),
                           nullptr, 0))
         return MOE_ERR_ARG;
-    const moe::DispatchArgs da = dispatch_args(h, x, topk_ids, num_tokens, workspace,
+    const Scratch sc = handle_scratch(h);
+    const moe::DispatchArgs da = dispatch_args(h, sc, x, topk_ids, num_tokens, workspace,
                                                moe::plan_route(num_tokens), 0);
-    return dispatch_launch(h, da, topk_ids, num_tokens, R, static_cast<hipStream_t>(stream));
+    return dispatch_launch(h, sc, da, topk_ids, num_tokens, R, static_cast<hipStream_t>(stream));
+}
+
+int moe_dispatch_noalloc(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
+                         int32_t num_tokens, int32_t runtime_max_tokens_per_rank,
+                         uint16_t *workspace, void *stream) {
+    const int32_t R = runtime_max_tokens_per_rank;
+    int rc = dispatch_checks(h, x, topk_ids, num_tokens, R, workspace);
+    if (rc != MOE_OK) return rc;
+    if ((int64_t)num_tokens * h->top_k > MOE_NOALLOC_MAX_ITEMS) return MOE_ERR_NOALLOC_SIZE;
+    if (dispatch_overlaps(h, x, topk_ids, num_tokens, workspace, ws_bytes(h, sizeof(uint16_t)),
+                          nullptr, 0))
+        return MOE_ERR_ARG;
+    Scratch sc{nullptr, MOE_NOALLOC_MAX_ITEMS};
+    const hipError_t e = static_scratch(&sc.base);
+    if (e != hipSuccess) return hip_fail(h, e);
+    const moe::DispatchArgs da = dispatch_args(h, sc, x, topk_ids, num_tokens, workspace,
+                                               moe::plan_route(num_tokens), 0);
+    return dispatch_launch(h, sc, da, topk_ids, num_tokens, R, static_cast<hipStream_t>(stream));
 }
 
 int moe_dispatch_fp8(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
@@ -247,16 +316,18 @@ int moe_dispatch_fp8(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
     int rc = dispatch_checks(h, x, topk_ids, num_tokens, R, workspace);
     if (rc != MOE_OK) return rc;
     if (!dev_ok(scales, 4) || h->hidden > MOE_MAX_FUSED_HIDDEN) return MOE_ERR_ARG;
+    if (h->scratch == nullptr) return MOE_ERR_ARG;         // a handle for moe_dispatch_noalloc
     const size_t scale_bytes = (size_t)h->ep_size * h->max_tokens_per_rank * sizeof(float);
     if (dispatch_overlaps(h, x, topk_ids, num_tokens, workspace, ws_bytes(h, 1), scales,
                           scale_bytes))
         return MOE_ERR_ARG;
-    moe::DispatchArgs da = dispatch_args(h, x, topk_ids, num_tokens, nullptr,
+    const Scratch sc = handle_scratch(h);
+    moe::DispatchArgs da = dispatch_args(h, sc, x, topk_ids, num_tokens, nullptr,
                                          moe::plan_route(num_tokens), 0);
     da.fp8 = 1;
     da.ws8 = workspace;
     da.scales = scales;
-    return dispatch_launch(h, da, topk_ids, num_tokens, R, static_cast<hipStream_t>(stream));
+    return dispatch_launch(h, sc, da, topk_ids, num_tokens, R, static_cast<hipStream_t>(stream));
 }
 
 int moe_route_counts(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens, void *stream) {
@@ -264,13 +335,15 @@ int moe_route_counts(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens,
     if (h->phase != 0) return MOE_ERR_PHASE;
     if (num_tokens < 0 || num_tokens > h->max_tokens) return MOE_ERR_ARG;
     if (num_tokens > 0 && !dev_ok(topk_ids, 4)) return MOE_ERR_ARG;
+    if (h->scratch == nullptr) return MOE_ERR_ARG;         // a handle for moe_dispatch_noalloc
     if (overlaps_handle(h, topk_ids, (size_t)num_tokens * h->top_k * sizeof(int32_t)))
         return MOE_ERR_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     moe::RoutePlan plan;
-    int rc = route(h, topk_ids, num_tokens, s, &plan);
+    const Scratch sc = handle_scratch(h);
+    int rc = route(h, sc, topk_ids, num_tokens, s, &plan);
     if (rc != MOE_OK) return rc;
-    const moe::DispatchArgs da = dispatch_args(h, nullptr, topk_ids, num_tokens, nullptr, plan, 1);
+    const moe::DispatchArgs da = dispatch_args(h, sc, nullptr, topk_ids, num_tokens, nullptr, plan, 1);
     hipError_t e = moe::launch_dispatch_copy(da, s);
     if (e != hipSuccess) return hip_fail(h, e);
     return MOE_OK;
@@ -447,6 +520,9 @@ const char *moe_strerror(int code) {
         case MOE_ERR_OVERFLOW: return "a destination region received more copies than max_tokens_per_rank";
         case MOE_ERR_EXPERT_ID: return "expert id outside [-1, num_experts)";
         case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_NOALLOC_SIZE:
+            return "batch too large for the library's static routing scratch "
+                   "(moe_dispatch_noalloc: num_tokens * top_k <= MOE_NOALLOC_MAX_ITEMS)";
         default: return "unknown error code";
     }
 }

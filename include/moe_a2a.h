@@ -62,6 +62,8 @@ extern "C" {
 #define MOE_ERR_EXPERT_ID (-4)  /* an expert id outside [-1, E)              */
 #define MOE_ERR_HIP       (-5)  /* a HIP runtime call failed (see hip_error, */
                                 /* moe_last_hip_error)                     */
+#define MOE_ERR_NOALLOC_SIZE (-6) /* a batch beyond the static scratch of  */
+                                /* moe_dispatch_noalloc                    */
 
 /* workspace layouts (moe_init) */
 #define MOE_LAYOUT_PER_COPY   0     /* one row per routed copy (t, j)          */
@@ -77,6 +79,7 @@ extern "C" {
 #define MOE_MAX_FUSED_HIDDEN 16384  /* hidden size of the fused epilogue       */
 #define MOE_MAX_HIDDEN     1048576  /* hidden size (a row stays under 2^31 B)  */
 #define MOE_MAX_PARTIALS     64     /* partials summed by moe_partials_reduce* */
+#define MOE_NOALLOC_MAX_ITEMS 1048576 /* routed copies (T * k) per moe_dispatch_noalloc */
 #define MOE_MAX_TOKENS     8388608  /* tokens per handle: the combine runs one */
                                     /* 256-lane block per token, and a launch */
                                     /* holds fewer than 2^32 lanes            */
@@ -147,6 +150,10 @@ size_t moe_scratch_bytes(int32_t max_tokens, int32_t top_k, int32_t ep_size);
  *                        the first dispatch (zero-filled memory); the scratch
  *                        belongs to this handle (two handles in flight at
  *                        once must not share it)
+ *   scratch, scratch_bytes  may instead be NULL and 0: the handle then serves
+ *                        moe_dispatch_noalloc only (moe_dispatch,
+ *                        moe_dispatch_fp8 and moe_route_counts return
+ *                        MOE_ERR_ARG)
  *   scratch_bytes        >= moe_scratch_bytes(max_tokens, top_k, ep_size)
  * Returns MOE_OK or MOE_ERR_ARG.  No HIP call is made.
  */
@@ -185,6 +192,28 @@ int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
 int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
                  int32_t num_tokens, int32_t runtime_max_tokens_per_rank,
                  uint16_t *workspace, void *stream);
+
+/*
+ * moe_dispatch_noalloc -- moe_dispatch for callers that cannot allocate
+ * device memory at all (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the routing scratch (per-copy ranks
+ * and per-chunk region histograms) comes from a static array in the
+ * library's device code, 4 MiB + 64 KiB on each GPU the library runs on,
+ * held until the process ends, instead of the handle's scratch (which may
+ * be NULL).  The caller still passes x, topk_ids and the workspace, and the
+ * handle still binds the output buffers.  Arguments, outputs, errors and the
+ * phase as moe_dispatch, plus:
+ *   num_tokens * top_k <= MOE_NOALLOC_MAX_ITEMS, else MOE_ERR_NOALLOC_SIZE
+ * (checked before anything is enqueued).  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (on different streams,
+ * or from different threads without ordering) race and give wrong results.
+ * Nothing in the array needs clearing: each call's routing kernel writes
+ * what its copy kernel reads.  Makes no allocating call; the first call on
+ * a GPU looks up the array's device address (hipGetSymbolAddress).
+ */
+int moe_dispatch_noalloc(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
+                         int32_t num_tokens, int32_t runtime_max_tokens_per_rank,
+                         uint16_t *workspace, void *stream);
 
 /*
  * moe_dispatch_fp8 -- moe_dispatch with an FP8 payload: each token row is

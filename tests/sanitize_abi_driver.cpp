@@ -186,6 +186,29 @@ int main() {
         CHECK(moe_partials_reduce_residual_rmsnorm(parts, P, Tn, Hn, res, res, nrm, 1e-6f, nrm,
                                                    nullptr) == MOE_ERR_ARG);
     }
+    // a handle without scratch serves moe_dispatch_noalloc only; that call
+    // rejects batches beyond its static scratch before anything else
+    {
+        moe_handle n;
+        CHECK(moe_init(&n, T, H, k, E, ep, T, MOE_LAYOUT_PER_COPY, counts.data(), src.data(),
+                       slot.data(), status.data(), nullptr, 0) == MOE_OK);
+        CHECK(moe_init(&n, T, H, k, E, ep, T, MOE_LAYOUT_PER_COPY, counts.data(), src.data(),
+                       slot.data(), status.data(), nullptr, 4) == MOE_ERR_ARG);
+        CHECK(moe_init(&n, T, H, k, E, ep, T, MOE_LAYOUT_PER_COPY, counts.data(), src.data(),
+                       slot.data(), status.data(), nullptr, 0) == MOE_OK);
+        const int before = moe::launches;
+        CHECK(moe_dispatch(&n, x, ids, T, T, ws, nullptr) == MOE_ERR_ARG);
+        CHECK(moe_dispatch_fp8(&n, x, ids, T, T, ws8, scales, nullptr) == MOE_ERR_ARG);
+        CHECK(moe_route_counts(&n, ids, T, nullptr) == MOE_ERR_ARG);
+        CHECK(moe::launches == before && n.phase == 0);
+        moe_handle big;
+        const int32_t Tb = MOE_NOALLOC_MAX_ITEMS / k + 1;
+        CHECK(moe_init(&big, Tb, H, k, E, ep, 1, MOE_LAYOUT_PER_COPY, counts.data(), src.data(),
+                       slot.data(), status.data(), nullptr, 0) == MOE_OK);
+        CHECK(moe_dispatch_noalloc(&big, x, ids, Tb, Tb, ws, nullptr) == MOE_ERR_NOALLOC_SIZE);
+        CHECK(moe::launches == before && big.phase == 0);
+    }
+
     // a failed partials launch keeps its hipError_t for moe_last_hip_error
     moe::fail_partials = 5;
     CHECK(moe_partials_reduce(ws, 5, 4, H, out, nullptr) == MOE_ERR_HIP);

@@ -52,7 +52,7 @@ def test_handle_layout_and_constants_match_header(tmp_path):
             "int main(void){", 'printf("%zu\\n", sizeof(moe_handle));']
     prog += [f'printf("%zu\\n", offsetof(moe_handle, {f}));' for f in fields]
     consts = ["MOE_OK", "MOE_ERR_ARG", "MOE_ERR_PHASE", "MOE_ERR_OVERFLOW", "MOE_ERR_EXPERT_ID",
-              "MOE_ERR_HIP", "MOE_STATUS_OVERFLOW", "MOE_STATUS_EXPERT_ID", "MOE_MAX_EP",
+              "MOE_ERR_HIP", "MOE_ERR_NOALLOC_SIZE", "MOE_NOALLOC_MAX_ITEMS", "MOE_STATUS_OVERFLOW", "MOE_STATUS_EXPERT_ID", "MOE_MAX_EP",
               "MOE_MAX_TOP_K", "MOE_MAX_FUSED_HIDDEN", "MOE_MAX_HIDDEN", "MOE_MAX_TOKENS", "MOE_MAX_PARTIALS", "MOE_LAYOUT_PER_COPY",
               "MOE_LAYOUT_PER_REGION"]
     prog += [f'printf("%d\\n", (int){c});' for c in consts]
@@ -121,6 +121,25 @@ def test_init_rejects_pointers_and_scratch(lib):
     assert lib.moe_init(None, *args, FAKE, FAKE, FAKE, FAKE, FAKE, sb) == moe.MOE_ERR_ARG
     assert lib.moe_init(ctypes.byref(h), *args, FAKE, FAKE, FAKE, FAKE, FAKE, sb) == moe.MOE_OK
     assert h.experts_per_rank == 2 and h.phase == 0
+
+
+def test_scratch_free_handle_and_noalloc_size_limit(lib):
+    h = moe.MoeHandle()
+    args = [1 << 20, 128, 2, 8, 4, 128, 0]
+    # no scratch (NULL, 0): a handle for moe_dispatch_noalloc only
+    assert lib.moe_init(ctypes.byref(h), *args, FAKE, FAKE, FAKE, FAKE, None, 0) == moe.MOE_OK
+    assert lib.moe_init(ctypes.byref(h), *args, FAKE, FAKE, FAKE, FAKE, None, 64) == moe.MOE_ERR_ARG
+    assert lib.moe_init(ctypes.byref(h), *args, FAKE, FAKE, FAKE, FAKE, None, 0) == moe.MOE_OK
+    assert lib.moe_dispatch(ctypes.byref(h), FAKE, FAKE, 8, 8, FAKE, None) == moe.MOE_ERR_ARG
+    assert lib.moe_dispatch_fp8(ctypes.byref(h), FAKE, FAKE, 8, 8, FAKE, FAKE, None) == moe.MOE_ERR_ARG
+    assert lib.moe_route_counts(ctypes.byref(h), FAKE, 8, None) == moe.MOE_ERR_ARG
+    # the static scratch holds MOE_NOALLOC_MAX_ITEMS routed copies (top-2 here)
+    T = moe.MOE_NOALLOC_MAX_ITEMS // 2 + 1
+    rc = lib.moe_dispatch_noalloc(ctypes.byref(h), FAKE, FAKE, T, T, FAKE, None)
+    assert rc == moe.MOE_ERR_NOALLOC_SIZE and h.phase == 0
+    assert "static routing scratch" in moe.moe_strerror(rc)
+    assert lib.moe_dispatch_noalloc(ctypes.byref(h), FAKE + 8, FAKE, 8, 8, FAKE, None) == moe.MOE_ERR_ARG
+    assert isinstance(lib.moe_last_hip_error(), int)
 
 
 def test_dispatch_argument_checks(lib):
