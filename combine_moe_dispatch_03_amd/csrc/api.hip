@@ -163,6 +163,14 @@ struct Scratch {
     int64_t max_items;
 };
 
+// log2 of experts_per_rank when it is a power of two (the kernels then map
+// an expert to its region with a shift), else -1.
+static int32_t epr_shift(const moe_handle *h) {
+    for (int32_t s = 0; s < 31; ++s)
+        if ((int32_t(1) << s) == h->experts_per_rank) return s;
+    return -1;
+}
+
 static Scratch handle_scratch(const moe_handle *h) {
     return Scratch{h->scratch, (int64_t)h->max_tokens * h->top_k};
 }
@@ -180,6 +188,7 @@ static int route(moe_handle *h, const Scratch &sc, const int32_t *topk_ids, int3
     ra.ep = h->ep_size;
     ra.epr = h->experts_per_rank;
     ra.n_experts = h->num_experts;
+    ra.epr_shift = epr_shift(h);
     ra.k = h->top_k;
     ra.per_region = h->layout == MOE_LAYOUT_PER_REGION;
     hipError_t e = moe::launch_route(ra, plan.n_chunks, s);
@@ -207,6 +216,7 @@ static moe::DispatchArgs dispatch_args(moe_handle *h, const Scratch &sc, const u
     da.ep = h->ep_size;
     da.epr = h->experts_per_rank;
     da.n_experts = h->num_experts;
+    da.epr_shift = epr_shift(h);
     da.cap = h->max_tokens_per_rank;
     da.tokens_per_chunk = plan.tokens_per_chunk;
     da.n_chunks = plan.n_chunks;

@@ -155,6 +155,13 @@ __device__ __forceinline__ void add_copy_sums(int32_t *cbase, const int32_t *des
     if (sum != 0) atomicAdd(&cbase[j], sum);
 }
 
+// Region of expert e (0 <= e < E): a shift when experts_per_rank is a power
+// of two (epr_shift >= 0), else a division.
+template <typename Args>
+__device__ __forceinline__ int region_of(const Args &a, int e) {
+    return a.epr_shift >= 0 ? e >> a.epr_shift : e / a.epr;
+}
+
 // Lanes of this wave bound for the same region as this lane (d >= 0), found
 // by intersecting one ballot per bit of the region number.  Every lane must
 // call this (ballots).
@@ -257,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
             if (i < end) {
                 const int e = ids[g];
                 if (e >= 0 && e < a.n_experts)
-                    d = e / a.epr;
+                    d = region_of(a, e);
                 else if (e != -1)
                     bad = true;
             }
@@ -482,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
     if (tid < a.k) {
         const int e = a.ids[f];
         rank = a.rank[f];                       // meaningful only for a ranked copy
-        if (e >= 0 && e < a.n_experts) d = e / a.epr;
+        if (e >= 0 && e < a.n_experts) d = region_of(a, e);
         dests[tid] = d;
     }
 
@@ -538,47 +545,23 @@ __device__ __forceinline__ void accumulate(float (&acc)[VPT][8], const u32x4 (&r
 }
 
 // ---------------------------------------------------------------------------
-// dispatch_small_kernel<VPT, NT, FP8>: the whole dispatch in one launch, for
-// batches of at most kSmallItems routed copies (decode).  Each block counts,
-// per region, the copies of all earlier tokens itself (at most kSmallItems
-// ids, read from L2), adds the rank among its own token's earlier copies,
-// and copies its row like dispatch_copy_kernel.  Block (0, 0) also counts
-// every copy for `counts` and flags bad ids.  Same stable slot order as the
-// two-kernel path: copies fill a region in increasing flat index.
-// Within a wave, lanes bound for the same region are grouped with ballots
-// (rank_group, as in route_rank_kernel) so each group adds its size to the
-// LDS counter with one atomic.
+// dispatch_small_kernel<VPT, NT, FP8, C>: the whole dispatch in one launch,
+// for batches of at most kSmallItems routed copies (decode).  Grid and block
+// order as dispatch_copy_kernel: blocks of C copies of one token, a token's
+// blocks 8 indices apart so they share an XCD, x column blocks.  In place of
+// the routing kernel's chunk histograms each block counts, per region, the
+// copies of all earlier tokens itself: at most kSmallItems ids from L2,
+// loaded together with the source row, one LDS add per copy (under the
+// per-region layout one per ballot group of first copies, as in
+// route_rank_kernel).  A copy's rank among its own token's earlier copies to
+// the same region comes from the token's ids, so the slots follow the stable
+// order of the routed path.  Each token's first block flags the token's bad
+// ids; the last token's first block writes counts (the earlier tokens' copies
+// plus its own).
 static_assert(kSmallItems % kThreads == 0, "small-batch ids are split evenly over a block");
-__device__ __forceinline__ void count_regions(int32_t *cnt, const DispatchArgs &a, int64_t n,
-                                              int region_bits, int tid, bool *bad) {
-    // n <= kSmallItems: every id this thread needs is loaded up front
-    constexpr int kPer = kSmallItems / kThreads;
-    const int lane = tid & 63;
-    int ids[kPer];
-#pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-        const int64_t i = (int64_t)p * kThreads + tid;
-        ids[p] = i < n ? a.ids[i] : -1;
-    }
-#pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-        if ((int64_t)p * kThreads >= n) break;         // uniform
-        const int64_t i = (int64_t)p * kThreads + tid;
-        const int e = ids[p];
-        int d = -1;
-        if (i < n) {
-            if (e >= 0 && e < a.n_experts)
-                d = e / a.epr;
-            else if (e != -1)
-                *bad = true;
-        }
-        const uint64_t same = a.per_region ? rank_group(a, d, i, i < n, region_bits)
-                                           : region_group(d, region_bits);
-        if (d >= 0 && (same >> lane) == 1ull) atomicAdd(&cnt[d], __popcll(same));
-    }
-}
+constexpr int kSmallPer = kSmallItems / kThreads;
 
-template <int VPT, bool NT, bool FP8>
+template <int VPT, bool NT, bool FP8, int C>
 __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a) {
     __shared__ int32_t cnt[MOE_MAX_EP];
     __shared__ int32_t dests[MOE_MAX_TOP_K];
@@ -587,24 +570,17 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
     __shared__ float red[kWaves];
 
     const int tid = threadIdx.x;
-    const int t = blockIdx.x;
+    const int lane = tid & 63;
     const int cb = blockIdx.y;
     const int ep = a.ep;
-    int region_bits = 0;
-    while ((1 << region_bits) < ep) ++region_bits;
+    const int n = (a.k + C - 1) / C;            // copy groups per token
+    const int b = blockIdx.x;
+    const int grp = (b >> 3) % n;
+    const int t = ((b >> 3) / n) * 8 + (b & 7);
+    if (t >= a.T) return;                       // past the batch in the last group of 8 tokens
+    const bool first_block = (grp | cb) == 0;   // writes the token's index maps
 
-    if (t == 0 && cb == 0) {                    // totals and the bad-id flag
-        for (int r = tid; r < ep; r += kThreads) cnt[r] = 0;
-        __syncthreads();
-        bool bad = false;
-        count_regions(cnt, a, (int64_t)a.T * a.k, region_bits, tid, &bad);
-        if (bad) atomicOr(a.status, MOE_STATUS_EXPERT_ID);
-        __syncthreads();
-        for (int r = tid; r < ep; r += kThreads) a.counts[r] = cnt[r];
-        __syncthreads();
-    }
-    if (t >= a.T) return;
-
+    // loads: the source row, this token's ids, the ids of every earlier token
     const int vpr = a.H >> 3;
     const uint16_t *src = a.x + (int64_t)t * a.H;
     u32x4 v[VPT];
@@ -616,27 +592,64 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
         off[q] = (int64_t)min(col[q], vpr - 1) * 8;
         v[q] = load16(src + off[q]);
     }
-
-    const int64_t f = (int64_t)t * a.k + tid;
+    const int64_t mine = (int64_t)t * a.k;      // this token's first copy
+    const int own_id = tid < a.k ? a.ids[mine + tid] : -1;
+    int eid[kSmallPer];
+#pragma unroll
+    for (int p = 0; p < kSmallPer; ++p) {
+        const int64_t i = (int64_t)p * kThreads + tid;
+        eid[p] = i < mine ? a.ids[i] : -1;
+    }
     for (int r = tid; r < ep; r += kThreads) cnt[r] = 0;
     int d = -1;
     if (tid < a.k) {
-        const int e = a.ids[f];
-        d = (e >= 0 && e < a.n_experts) ? e / a.epr : -1;
+        if (own_id >= 0 && own_id < a.n_experts)
+            d = region_of(a, own_id);
+        else if (own_id != -1 && first_block)
+            atomicOr(a.status, MOE_STATUS_EXPERT_ID);
         dests[tid] = d;
     }
     __syncthreads();
-    bool unused = false;
-    count_regions(cnt, a, (int64_t)t * a.k, region_bits, tid, &unused);
-    int rank = 0;                               // earlier copies of this token to d
+
+    // copies of the earlier tokens, per region
+    if (a.per_region) {
+        int region_bits = 0;
+        while ((1 << region_bits) < ep) ++region_bits;
+#pragma unroll
+        for (int p = 0; p < kSmallPer; ++p) {
+            if ((int64_t)p * kThreads >= mine) break;     // uniform
+            const int64_t i = (int64_t)p * kThreads + tid;
+            int de = -1;
+            if (i < mine && eid[p] >= 0 && eid[p] < a.n_experts) de = region_of(a, eid[p]);
+            const uint64_t same = rank_group(a, de, i, i < mine, region_bits);
+            if (de >= 0 && (same >> lane) == 1ull) atomicAdd(&cnt[de], __popcll(same));
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < kSmallPer; ++p)
+            if (eid[p] >= 0 && eid[p] < a.n_experts) atomicAdd(&cnt[region_of(a, eid[p])], 1);
+    }
+    // rank among the token's earlier copies to the same region (under the
+    // per-region layout a first copy's rank is 0 and the later ones share its
+    // row in assign_rows)
+    int rank = 0;
     if (tid < a.k && d >= 0)
         for (int j = 0; j < tid; ++j) rank += (dests[j] == d);
     __syncthreads();
-    assign_rows(a, d, tid, cb, f, d < 0 ? 0 : cnt[d], rank, dests, rows, copy_rows);
+
+    if (first_block && t == a.T - 1) {          // totals: the earlier tokens' copies plus this one's
+        for (int r = tid; r < ep; r += kThreads) {
+            int own = 0;
+            for (int j = 0; j < a.k; ++j) own += (dests[j] == r);
+            a.counts[r] = cnt[r] + (a.per_region ? (own > 0) : own);
+        }
+    }
+    assign_rows(a, d, tid, cb | grp, mine + tid, d < 0 ? 0 : cnt[d], rank, dests, rows, copy_rows);
+    const int j0 = grp * C, j1 = min(a.k, j0 + C);
     if constexpr (FP8)
-        store_rows_fp8<VPT, NT>(a, v, col, off, vpr, copy_rows, red, tid, 0, a.k);
+        store_rows_fp8<VPT, NT>(a, v, col, off, vpr, copy_rows, red, tid, j0, j1);
     else
-        store_rows_bf16<VPT, NT>(a, v, col, off, vpr, copy_rows, 0, a.k);
+        store_rows_bf16<VPT, NT>(a, v, col, off, vpr, copy_rows, j0, j1);
 }
 
 // G rows starting at compacted copy j0: all G x VPT loads, then the adds in
@@ -853,17 +866,23 @@ int combine_group(int vpt, bool fused, const CombineArgs &a) {
     return (fused || vpt >= 8 || a.k <= 4 || a.per_region) ? 4 : 8;
 }
 
+template <int VPT, bool FP8, int C>
+void launch_copy_c(const DispatchArgs &a, dim3 grid, hipStream_t s, bool small) {
+    if (small)
+        hipLaunchKernelGGL((dispatch_small_kernel<VPT, kCopyNT, FP8, C>), grid, dim3(kThreads), 0, s,
+                           a);
+    else
+        hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT, FP8, C>), grid, dim3(kThreads), 0, s,
+                           a);
+}
+
 template <int VPT, bool FP8>
 void launch_copy_vpt(const DispatchArgs &a, dim3 grid, hipStream_t s, bool small, int c) {
     constexpr int kSplit = FP8 ? kCopiesPerBlockFp8 : kCopiesPerBlock;
-    if (small)
-        hipLaunchKernelGGL((dispatch_small_kernel<VPT, kCopyNT, FP8>), grid, dim3(kThreads), 0, s, a);
-    else if (c == kSplit)
-        hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT, FP8, kSplit>), grid,
-                           dim3(kThreads), 0, s, a);
+    if (c == kSplit)
+        launch_copy_c<VPT, FP8, kSplit>(a, grid, s, small);
     else
-        hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT, FP8, MOE_MAX_TOP_K>), grid,
-                           dim3(kThreads), 0, s, a);
+        launch_copy_c<VPT, FP8, MOE_MAX_TOP_K>(a, grid, s, small);
 }
 
 // c: copies per dispatch_copy_kernel block (kCopiesPerBlock[Fp8], or
@@ -910,26 +929,32 @@ hipError_t launch_route(const RouteArgs &a, int32_t n_chunks, hipStream_t s) {
 hipError_t launch_dispatch_copy(const DispatchArgs &args, hipStream_t s) {
     DispatchArgs a = args;
     a.t_base = 0;
-    const bool small = !a.count_only && dispatch_is_small(a.T, a.k);
-    if (small || a.count_only || a.T == 0) {    // one block per token, or the totals only
-        const int vpt = a.fp8 ? full_row_vpt(a.H) : streaming_vpt(a.T, a.H);
-        const dim3 grid(a.T > 0 && !a.count_only ? a.T : 1,
-                        a.T > 0 && !a.count_only ? column_blocks(a.H, vpt) : 1);
+    if (a.count_only || a.T == 0) {             // the totals only (an empty batch: zeros)
+        const dim3 grid(1, 1);
         if (a.fp8)
-            launch_copy<true>(a, vpt, grid, s, small, MOE_MAX_TOP_K);
+            launch_copy<true>(a, full_row_vpt(a.H), grid, s, false, MOE_MAX_TOP_K);
         else
-            launch_copy<false>(a, vpt, grid, s, small, MOE_MAX_TOP_K);
+            launch_copy<false>(a, 1, grid, s, false, MOE_MAX_TOP_K);
         return hipGetLastError();
     }
-    // Blocks of c copies in XCD order (dispatch_copy_kernel), over tokens
-    // padded to a multiple of 8, in launches of at most kMaxBlocksX blocks
-    // along x.  Rows under kSplitMinHidden stay one block per token.  The
-    // fp8 payload needs the whole row in a block for its scale.
+    // Blocks of c copies in XCD order (both copy kernels), over tokens
+    // padded to a multiple of 8.  Rows under kSplitMinHidden stay one block
+    // per token.  The fp8 payload needs the whole row in a block for its
+    // scale.
     const int c = a.H < kSplitMinHidden ? MOE_MAX_TOP_K
                                         : a.fp8 ? kCopiesPerBlockFp8 : kCopiesPerBlock;
     const int n = (a.k + c - 1) / c;
     const int64_t t_pad = ((int64_t)a.T + 7) / 8 * 8;
     const int vpt = a.fp8 ? full_row_vpt(a.H) : streaming_vpt(t_pad * n, a.H);
+    if (dispatch_is_small(a.T, a.k)) {          // one launch, no routing kernel before it
+        const dim3 grid((uint32_t)(t_pad * n), column_blocks(a.H, vpt));
+        if (a.fp8)
+            launch_copy<true>(a, vpt, grid, s, true, c);
+        else
+            launch_copy<false>(a, vpt, grid, s, true, c);
+        return hipGetLastError();
+    }
+    // Routed: launches of at most kMaxBlocksX blocks along x.
     const int64_t slab = std::max<int64_t>(8, kMaxBlocksX / n / 8 * 8);    // tokens per launch
     for (int64_t t0 = 0; t0 < a.T; t0 += slab) {
         a.t_base = (int32_t)t0;

@@ -52,6 +52,7 @@ struct RouteArgs {
     int64_t n_items;         // T*k
     int32_t items_per_chunk;
     int32_t ep, epr, n_experts;
+    int32_t epr_shift;       // log2(epr) when epr is a power of two, else -1
     int32_t k;
     int32_t per_region;      // 1: only a token's first copy to a region takes a row
 };
@@ -67,6 +68,7 @@ struct DispatchArgs {
     int32_t *src_index;      // [ep*cap]
     int32_t *status;
     int32_t T, H, k, ep, epr, n_experts, cap;
+    int32_t epr_shift;       // log2(epr) when epr is a power of two, else -1
     int32_t tokens_per_chunk, n_chunks;
     int32_t count_only;      // 1: only write counts
     int32_t per_region;      // 1: one row per (token, region), duplicates share it
