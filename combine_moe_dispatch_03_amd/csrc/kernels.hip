@@ -81,6 +81,24 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// fp64 -> fp32 rounded to odd: the truncation toward zero, with its last bit
+// set when the conversion is inexact.  fp32 carries 16 more bits than bf16
+// (also among subnormals), so a nearest-even narrowing of this value to bf16
+// equals the direct nearest-even rounding of the fp64 value: Boldo and
+// Melquiond, "When double rounding is odd" (2005).  NaN and infinities pass
+// through; a finite value beyond fp32's range becomes the largest finite
+// fp32 (odd), which still narrows to the bf16 infinity.
+__device__ __forceinline__ float f64_to_f32_odd(double d) {
+    float f = (float)d;                          // nearest-even
+    const double back = (double)f;
+    if (back != d && d == d) {                   // inexact (and not NaN)
+        uint32_t b = __float_as_uint(f);
+        if (__builtin_fabs(back) > __builtin_fabs(d)) b -= 1;   // back to the truncation
+        f = __uint_as_float(b | 1u);
+    }
+    return f;
+}
+
 __device__ __forceinline__ void unpack8(const u32x4 &r, float (&f)[8]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -764,8 +782,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
         // in fp32, s^2 summed over a row overflows once the elements pass
         // ~2e17 (bf16 reaches 3e38) and, with eps = 0, underflows for tiny
         // rows, where fp64 covers the whole bf16 range.  The fp64 product
-        // is rounded to fp32, then to bf16 (both nearest-even).  The fp64
-        // work is a few dozen operations per thread in a memory-bound kernel.
+        // is rounded to fp32 with round-to-odd, then to bf16 nearest-even,
+        // which together round it to bf16 nearest-even exactly once.  The
+        // fp64 work is a few dozen operations per thread in a memory-bound
+        // kernel.
         double ss = 0.0;
         u32x4 rv[VPT];
 #pragma unroll
@@ -801,7 +821,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
             unpack8(gv[q], g);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                acc[q][e] = (float)(((double)acc[q][e] * inv) * (double)g[e]);
+                acc[q][e] = f64_to_f32_odd(((double)acc[q][e] * inv) * (double)g[e]);
             store_out16(row_rsrc(a.normed + row_off, a.H), off[q], pack8(acc[q]), cached);
         }
     }

@@ -3,8 +3,11 @@
 Dispatch (counts, slot_index, src_index, every valid row) must match
 bit-exactly; padding rows keep their NaN canary (never written) and, because
 a read canary would poison the sum, the combine result also shows padding is
-never read.  Combine and the fused epilogue must be within 1 bf16 ulp of the
-oracle everywhere, and the normalised output within 1e-2 relative error
+never read.  Combine and the fused epilogue must equal the oracle bit for bit
+everywhere (the kernels take the oracle's fp32 operations in its order and
+round once; the normalised output rounds its fp64 value through fp32 with
+round-to-odd, so it too is rounded once), and the normalised output is also
+checked against 1e-2 relative error
 (0.02 magnitude floor).  All five workloads run at their full sizes, in the
 same launch configuration the benchmark times.
 """
@@ -71,7 +74,7 @@ def test_combine_within_one_ulp(name):
         got = to_u16(out)
         want = orc.combine(ref.ws, ref.slot_index, inp.weights, weighted, wl.H)
         inexact = assert_bf16_close(got, want, f"{name} combine")
-        say(f"{name}: {inexact} of {got.size} elements differ by 1 ulp")
+        say(f"{name}: {inexact} of {got.size} elements differ from the oracle")
         assert run.h.handle.phase == 0
 
 
@@ -93,7 +96,7 @@ def test_fused_epilogue_within_one_ulp():
         assert_bf16_close(got_r, want_r, "residual_out")
         inexact = assert_bf16_close(got_n, want_n, "normed")
         assert compare.rel_err(got_n, want_n) <= 1e-2
-        say(f"fused: {inexact} normed elements differ by 1 ulp, "
+        say(f"fused: {inexact} normed elements differ from the oracle, "
             f"rel err {compare.rel_err(got_n, want_n):.2e}")
 
 

@@ -13,7 +13,7 @@ oracle, and a seed sweep against it.
   unweighted combine gives 2^k - 1 exactly (255 for top-8); a copy counted
   twice or missed changes the sum.
 * Seeds 1-4 on the small workloads: dispatch bit-exact and combine (and the
-  fused epilogue) within 1 ulp of the oracle.
+  fused epilogue) bit for bit against the oracle.
 * The combine reads expert outputs from a buffer other than the dispatch
   workspace and leaves the workspace as dispatched.
 * Two handles driven on two streams at once give the same bytes as each

@@ -6,7 +6,7 @@ top-12, 1 to 16 regions of 1 to 8 experts, both layouts, unrouted copies and
 repeated experts, and now and then a capacity too small for the routing (an
 overflow: reported, the copies past capacity dropped).  Dispatch must match
 bit for bit and the combine (weighted for the per-copy layout, the
-per-region rank-sum otherwise) within 1 bf16 ulp.  Twenty more cases run
+per-region rank-sum otherwise) bit for bit.  Twenty more cases run
 the fused residual + RMSNorm epilogue and twenty the FP8 payload (codes and
 scales bit-exact).
 """
