@@ -15,15 +15,22 @@ cost).  One JSON line is printed.
 ``value`` is tokens/s of the headline workload (prefill: 4096 tokens,
 hidden 7168, top-8 of 256 experts over 8 regions, unweighted combine).  The
 line also carries:
-  roofline      the dominant kernel (the combine kernel: one launch per
-                moe_combine call, timed with HIP events on the launch stream
-                in the instrumented steps) against MI355X's 8 TB/s HBM peak,
-                algorithmic bytes per launch / mean launch time; ``traffic``
-                is the measured HBM bytes per launch from the committed
-                rocprofv3 counter summary, or null if the kernel source has
-                changed since those counters were taken
-  cpu_baseline  the CPU oracle (plain scalar C, one thread) timed on the
-                same workload, repeated for about 10 s
+  roofline      the phase that takes longer of the two: the dispatch call
+                (route_rank_kernel + dispatch_copy_kernel, one C call,
+                timed as one) or the combine (combine_kernel), with HIP
+                events on the launch stream in the instrumented steps,
+                against MI355X's 8 TB/s HBM peak: algorithmic bytes per call
+                / mean call time; ``traffic`` is the measured HBM bytes per
+                call from the committed rocprofv3 counter summary, or null
+                if the kernel source has changed since those counters were
+                taken
+  cpu_baseline  the CPU oracle (plain scalar C, its -O3 -march=native build
+                compiled on this host) on the headline workload, one thread:
+                dispatch + combine, each the median of 5 runs; with the
+                per-workload medians (prefill, skewed, fused; dispatch,
+                combine, fused epilogue) behind it, and the headline
+                workload on every core this process may use (at most 16:
+                cpu_baseline_all_cores)
   cold          per-kernel p50 / mean over --cold-iters launches, each after
                 an untimed 1 GiB read that evicts the 256 MB Infinity Cache
   workloads     the same step on the skewed, decode and fused workloads (decode
@@ -32,7 +39,10 @@ line also carries:
                 token and destination region, the form the FlashInfer pages
                 measure; unweighted combine of per-region messages), and with
                 the fp8 dispatch payload (e4m3 codes + one scale per row; the
-                combine reads the experts' bf16 outputs)
+                combine reads the experts' bf16 outputs); decode and the
+                ladder run at least 100 timed steps whatever --steps is
+  summary       last in the line: tokens/s and % of the HBM peak of every
+                workload, warm and cold, and of each phase
 """
 from __future__ import annotations
 
@@ -50,6 +60,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 GRAPH_STEPS = 10               # decode steps per captured graph
+SMALL_STEPS = 100              # timed steps of the launch-bound workloads (decode, ladder), at least
 PROFILES = {"combine": os.path.join(ROOT, "profiles", "combine_prefill_counters.txt"),
             "dispatch": os.path.join(ROOT, "profiles", "dispatch_prefill_counters.txt")}
 KERNEL_SOURCE = os.path.join(ROOT, "combine_moe_dispatch_03_amd", "csrc", "kernels.hip")
@@ -477,6 +488,34 @@ def measure_ladder(iters: int, warmup: int, rungs=LADDER_RUNGS, seed: int = 0) -
     return res
 
 
+def summary(main_res: dict, main_name: str, extras: dict) -> dict:
+    """A compact view of every workload: tokens/s and % of the HBM peak for the
+    warm step, the step after a cache-evicting read (cold), and each phase."""
+    def pct(v):
+        return None if v is None else round(100.0 * v, 1)
+
+    def one(r):
+        if "rungs" in r:                             # the ladder
+            return {t: {"roundtrip_us_p50": round(x["roundtrip_us_p50"], 2),
+                        "hbm_pct": pct(x["gbs_p50"] / HBM_PEAK_GBS)} for t, x in r["rungs"].items()}
+        if "fused_bytes" in r:                       # the partials reduction
+            c = r.get("cold") or {}
+            return {"tokens_per_s": round(r["tokens_per_s"]), "hbm_pct": pct(r["step_hbm_frac"]),
+                    "cold_hbm_pct": pct(c.get("hbm_frac_p50"))}
+        c = r.get("cold") or {}
+        d = {"tokens_per_s": round(r["tokens_per_s"]), "ms_per_step": round(r["ms_per_step"], 4),
+             "hbm_pct": pct(r["step_hbm_frac"]), "cold_hbm_pct": pct(c.get("hbm_frac_p50")),
+             "dispatch_pct": pct(r["dispatch_gbs"] / HBM_PEAK_GBS),
+             "combine_pct": pct(r["combine_gbs"] / HBM_PEAK_GBS)}
+        if "graph_ms_per_step" in r:
+            d["graph_ms_per_step"] = round(r["graph_ms_per_step"], 4)
+        return d
+
+    out = {main_name: one(main_res)}
+    out.update({k: one(v) for k, v in extras.items()})
+    return out
+
+
 def region_bytes(wl, rows: int) -> dict:
     """Algorithmic bytes under the per-region layout with ``rows`` rows sent:
     dispatch reads x and ids, writes the rows, slot_index and src_index;
@@ -505,85 +544,126 @@ def cold_stats(cd_ms, cc_ms, iters, T, disp_bytes, comb_bytes) -> dict:
     }
 
 
-def cpu_baseline(wl, seconds: float = 10.0, seed: int = 0) -> dict:
-    """The CPU oracle (dispatch + identity stage + combine) on the same
-    workload, repeated until about ``seconds`` of CPU work."""
-    import oracle
-    import synth
-
+def _cpu_ops(orc, wl, seed: int = 0):
+    """One batch of ``wl`` on the CPU oracle: callables running dispatch, and
+    on its result the combine (and, for the fused workload, the fused
+    epilogue).  The workspace is kept across runs, so a timed run does not
+    pay for first-touch page faults."""
     import numpy as np
 
-    orc = oracle.load()
+    import synth
+
     inp = synth.make_inputs(wl, seed)
     weighted = wl.combine in ("weighted", "both", "fused")
     cap = wl.cap
     if cap is None:
         cap = int(orc.dispatch(np.zeros((wl.T, 1), np.uint16), inp.ids, wl.ep, wl.epr,
                                wl.T * wl.k).counts.max())
-    reps, t_total = 0, 0.0
-    while t_total < seconds:
-        t0 = time.perf_counter()
-        d = orc.dispatch(inp.x, inp.ids, wl.ep, wl.epr, cap)
-        orc.combine(d.ws, d.slot_index, inp.weights, weighted, wl.H)
-        t_total += time.perf_counter() - t0
-        reps += 1
-        del d
-    return {"value": wl.T * reps / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"the full {wl.name} workload ({wl.T} tokens, dispatch + combine), "
-                      f"{reps} repetition(s), {t_total:.1f} s, single-threaded scalar C",
-            "cpu_model": _cpu_model(), "host_cpus_visible": os.cpu_count()}
+    x, ids, w = inp.x.copy(), inp.ids.copy(), inp.weights.copy()
+    state = {}
+
+    def dispatch():
+        state["d"] = orc.dispatch(x, ids, wl.ep, wl.epr, cap, ws=state.get("ws"))
+        state["ws"] = state["d"].ws
+
+    def combine():
+        d = state["d"]
+        orc.combine(d.ws, d.slot_index, w, weighted, wl.H)
+
+    ops = {"dispatch": dispatch, "combine": combine}
+    if wl.combine == "fused":
+        res, gamma = inp.residual.copy(), inp.gamma.copy()
+
+        def fused():
+            d = state["d"]
+            orc.combine_residual_rmsnorm(d.ws, d.slot_index, w, True, res, gamma, wl.eps)
+
+        ops["fused"] = fused
+    return ops
 
 
-def cpu_baseline_all_cores(wl, threads: int, seconds: float = 10.0, seed: int = 0) -> dict:
-    """The same oracle on every host core it may use: ``threads`` threads each
-    run dispatch + combine over their own copy of the batch, back to back,
-    for about ``seconds`` of wall time (the oracle's C calls release the
-    interpreter lock, so the threads run in parallel).  Independent batches
-    in parallel, not a parallel oracle: the oracle's code is unchanged."""
+def cpu_baseline_suite(names=("prefill", "skewed", "fused"), runs: int = 5,
+                       threads: int = 1, seed: int = 0) -> dict:
+    """The CPU oracle (its -O3 -march=native build, compiled here for this
+    host) timed per workload and op: one untimed run, then the median of
+    ``runs`` timed runs of each op.  With ``threads`` > 1, each thread runs
+    the op on its own copy of the batch at the same time (independent batches
+    in parallel: the oracle's code is unchanged and single-threaded), and a
+    run's time is the wall time until every thread is done."""
     import threading
 
+    import numpy as np
+
     import oracle
     import synth
 
-    import numpy as np
+    orc = oracle.load_timing(rebuild=True)
+    out = {}
+    for name in names:
+        wl = synth.BY_NAME[name]
+        workers = [_cpu_ops(orc, wl, seed) for _ in range(threads)]
+        times = {op: [] for op in workers[0]}
+        for op in workers[0]:
+            if threads == 1:
+                fn = workers[0][op]
+                fn()                                       # untimed: first touch
+                for _ in range(runs):
+                    t0 = time.perf_counter()
+                    fn()
+                    times[op].append(time.perf_counter() - t0)
+                continue
+            start, done = threading.Barrier(threads + 1), threading.Barrier(threads + 1)
 
-    orc = oracle.load()
-    inp = synth.make_inputs(wl, seed)
-    weighted = wl.combine in ("weighted", "both", "fused")
-    cap = wl.cap
-    if cap is None:
-        cap = int(orc.dispatch(np.zeros((wl.T, 1), np.uint16), inp.ids, wl.ep, wl.epr,
-                               wl.T * wl.k).counts.max())
-    reps = [0] * threads
-    start = threading.Barrier(threads + 1)
-    deadline = [0.0]
+            def work(ops, op=op):
+                for _ in range(runs + 1):
+                    start.wait()
+                    ops[op]()
+                    done.wait()
 
-    def worker(i):
-        x, ids, w = inp.x.copy(), inp.ids.copy(), inp.weights.copy()
-        start.wait()
-        while True:
-            d = orc.dispatch(x, ids, wl.ep, wl.epr, cap)
-            orc.combine(d.ws, d.slot_index, w, weighted, wl.H)
-            del d
-            reps[i] += 1
-            if time.perf_counter() >= deadline[0]:
-                return
+            pool = [threading.Thread(target=work, args=(ops,)) for ops in workers]
+            for th in pool:
+                th.start()
+            for r in range(runs + 1):
+                start.wait()
+                t0 = time.perf_counter()
+                done.wait()
+                if r > 0:                                  # run 0: first touch, untimed
+                    times[op].append(time.perf_counter() - t0)
+            for th in pool:
+                th.join()
+        med = {op: float(np.median(v)) for op, v in times.items()}
+        second = "fused" if "fused" in med else "combine"
+        step = med["dispatch"] + med[second]
+        out[name] = {"tokens": wl.T, "threads": threads,
+                     **{f"{op}_ms_p50": v * 1e3 for op, v in med.items()},
+                     "step": f"dispatch + {second}",
+                     "tokens_per_s": threads * wl.T / step}
+        del workers
+    return out
 
-    pool = [threading.Thread(target=worker, args=(i,)) for i in range(threads)]
-    for th in pool:
-        th.start()
-    t0 = time.perf_counter()
-    deadline[0] = t0 + seconds
-    start.wait()
-    for th in pool:
-        th.join()
-    wall = time.perf_counter() - t0
-    return {"value": wl.T * sum(reps) / wall, "unit": "tokens/s", "cores": threads,
+
+def cpu_baseline_lines(threads: int, runs: int = 5) -> tuple:
+    """The bench line's cpu_baseline (one core, the headline workload) and
+    cpu_baseline_all_cores, with the per-workload medians behind them."""
+    build = "gcc " + " ".join(__import__("oracle").TIMING_CFLAGS[:2]) + " -ffp-contract=off"
+    one = cpu_baseline_suite(threads=1, runs=runs)
+    line = {"value": one["prefill"]["tokens_per_s"], "unit": "tokens/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"the full {wl.name} workload ({wl.T} tokens, dispatch + combine) on "
-                      f"{threads} threads, each running its own copy of the batch; "
-                      f"{sum(reps)} batches in {wall:.1f} s of wall time, scalar C",
-            "cpu_model": _cpu_model()}
+            "sample": f"the full prefill workload (4096 tokens): dispatch + combine, each the "
+                      f"median of {runs} runs after one untimed run, single-threaded scalar C "
+                      f"({build})",
+            "cpu_model": _cpu_model(), "host_cpus_visible": os.cpu_count(),
+            "per_workload": one}
+    all_cores = None
+    if threads > 1:
+        many = cpu_baseline_suite(names=("prefill",), threads=threads, runs=runs)
+        all_cores = {"value": many["prefill"]["tokens_per_s"], "unit": "tokens/s",
+                     "cores": threads, "kind": "oracle",
+                     "sample": f"the full prefill workload on {threads} threads at once, each "
+                               f"running its own copy of the batch; per op the median of {runs} "
+                               f"runs of the wall time until every thread is done ({build})",
+                     "cpu_model": _cpu_model(), "per_workload": many}
+    return line, all_cores
 
 
 def host_cores() -> int:
@@ -656,7 +736,8 @@ def main() -> int:
     ap.add_argument("--cold-iters", type=int, default=100,
                     help="launches timed after an untimed 1 GiB cache-evicting read, per kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-runs", type=int, default=5,
+                    help="timed runs per op of the CPU baseline (the median is reported)")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="threads of the all-cores CPU baseline (0: every core this process "
                          "may use, at most 16; 1 skips it)")
@@ -694,16 +775,20 @@ def main() -> int:
     names = re.split(r",(?=(?:tiny|decode|prefill|skewed|fused|partials|ladder|shape:))",
                      args.extras)
     for name in [n for n in names if n and n != args.workload]:
-        if name == "ladder":
-            extras[name] = measure_ladder(max(args.steps // 2, 5), max(args.warmup // 2, 2))
+        if name == "ladder":                 # launch-bound: never fewer than 100 timed steps
+            extras[name] = measure_ladder(max(args.steps, SMALL_STEPS), max(args.warmup, 10))
             continue
         if name == "partials":
             extras[name] = measure_partials(synth.PARTIALS, max(args.steps // 2, 5),
                                             max(args.warmup // 2, 2), args.cold_iters)
             continue
         ewl, eopts = variant(name)
-        extras[name] = measure(ewl, max(args.steps // 2, 5), max(args.warmup // 2, 2),
-                               args.cold_iters, graph=ewl.name == "decode", **eopts)
+        if ewl.name in ("decode", "tiny"):   # launch-bound: never fewer than 100 timed steps
+            steps, warm = max(args.steps, SMALL_STEPS), max(args.warmup, 10)
+        else:
+            steps, warm = max(args.steps // 2, 5), max(args.warmup // 2, 2)
+        extras[name] = measure(ewl, steps, warm, args.cold_iters, graph=ewl.name == "decode",
+                               **eopts)
 
     # the roofline describes the phase that takes longer: the dispatch call
     # (routing + copy kernels, one C call, timed as one) or the combine
@@ -750,10 +835,12 @@ def main() -> int:
         "workloads": extras,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-        threads = args.cpu_threads or host_cores()
-        if threads > 1:
-            line["cpu_baseline_all_cores"] = cpu_baseline_all_cores(wl, threads, args.cpu_seconds)
+        one, many = cpu_baseline_lines(args.cpu_threads or host_cores(), args.cpu_runs)
+        line["cpu_baseline"] = one
+        if many is not None:
+            line["cpu_baseline_all_cores"] = many
+    # last, so that a reader of the line's tail sees every workload
+    line["summary"] = summary(main_res, wl.name, extras)
     print(json.dumps(line), flush=True)
     return 0
 

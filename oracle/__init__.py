@@ -22,17 +22,35 @@ SOURCE = os.path.join(HERE, "moe_oracle.c")
 LIBRARY = os.path.join(HERE, "libmoe_oracle.so")
 # -ffp-contract=off: every fused multiply-add in the oracle is an explicit fmaf.
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math"]
+# The same source built for timing only (the CPU baseline): -O3 for the host
+# it runs on.  The arithmetic flags are the same, so the results are too.
+TIMING_LIBRARY = os.path.join(HERE, "libmoe_oracle_timing.so")
+TIMING_CFLAGS = ["-O3", "-march=native", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                 "-fno-fast-math"]
 
 STATUS_OVERFLOW = 1
 STATUS_BAD_ID = 2
 
 
-def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+def build(source: str = SOURCE, output: str = LIBRARY, flags=CFLAGS) -> str:
     """Compile the oracle with gcc; returns the path of the shared library."""
     tmp = output + ".tmp"
-    subprocess.run(["gcc", *CFLAGS, "-o", tmp, source, "-lm"], check=True)
+    subprocess.run(["gcc", *flags, "-o", tmp, source, "-lm"], check=True)
     os.replace(tmp, output)
     return output
+
+
+def build_timing(output: str = TIMING_LIBRARY) -> str:
+    """The timing build (-O3 -march=native).  Build it on the host that times
+    it: -march=native targets the CPU doing the compiling."""
+    return build(SOURCE, output, TIMING_CFLAGS)
+
+
+def load_timing(rebuild: bool = True) -> "Oracle":
+    """The timing build of the oracle, compiled here first unless told not to."""
+    if rebuild or not os.path.exists(TIMING_LIBRARY):
+        build_timing()
+    return Oracle(TIMING_LIBRARY)
 
 
 _P = ctypes.c_void_p

@@ -54,17 +54,27 @@ def test_shape_workloads_parse():
         raise AssertionError(f"{bad} accepted")
 
 
-def test_cpu_baselines_on_the_tiny_workload():
-    # both CPU legs run the oracle on the same batch; the all-cores one
-    # counts every thread's batches over the wall time
-    import synth
-    wl = synth.BY_NAME["tiny"]
-    one = bench.cpu_baseline(wl, seconds=0.2)
-    many = bench.cpu_baseline_all_cores(wl, threads=2, seconds=0.2)
-    assert one["cores"] == 1 and many["cores"] == 2
-    for res in (one, many):
-        assert res["kind"] == "oracle" and res["unit"] == "tokens/s" and res["value"] > 0
+def test_cpu_baseline_suite_on_small_workloads():
+    # one thread and two threads, median of 3 runs per op; the fused
+    # workload also times its fused epilogue, and its step is dispatch + fused
+    one = bench.cpu_baseline_suite(names=("tiny", "decode"), runs=3, threads=1)
+    many = bench.cpu_baseline_suite(names=("tiny",), runs=3, threads=2)
+    for res, threads in ((one, 1), (many, 2)):
+        for name, r in res.items():
+            assert r["threads"] == threads and r["tokens_per_s"] > 0
+            assert r["dispatch_ms_p50"] > 0 and r["combine_ms_p50"] > 0
+            assert r["step"] == "dispatch + combine"
     assert 1 <= bench.host_cores() <= 16
+
+
+def test_summary_lists_every_workload():
+    res = {"tokens_per_s": 1e6, "ms_per_step": 0.1, "step_hbm_frac": 0.7, "dispatch_gbs": 5000.0,
+           "combine_gbs": 6000.0, "cold": {"hbm_frac_p50": 0.65}, "graph_ms_per_step": 0.01}
+    ladder = {"rungs": {"1": {"roundtrip_us_p50": 7.5, "gbs_p50": 40.0}}}
+    s = bench.summary(res, "prefill", {"decode": res, "ladder": ladder})
+    assert list(s) == ["prefill", "decode", "ladder"]
+    assert s["prefill"]["hbm_pct"] == 70.0 and s["prefill"]["cold_hbm_pct"] == 65.0
+    assert s["decode"]["graph_ms_per_step"] == 0.01 and s["ladder"]["1"]["hbm_pct"] == 0.5
 
 
 def test_unknown_workload_exits_with_a_message():
