@@ -686,6 +686,89 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+PROBE_KINDS = {"read": 0, "copy": 1, "write": 2, "rows": 3, "oneshot_write": 4, "oneshot_copy": 5}
+
+
+def _probe_library():
+    from combine_moe_dispatch_03_amd import build as pkg_build
+    if not os.path.exists(pkg_build.PROBE_LIBRARY):
+        raise SystemExit(f"{pkg_build.PROBE_LIBRARY} is not built (python -m combine_moe_dispatch_03_amd.build)")
+    lib = ctypes.CDLL(pkg_build.PROBE_LIBRARY)
+    lib.moe_probe_stream.restype = ctypes.c_int
+    lib.moe_probe_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_void_p]
+    return lib
+
+
+def ceilings(nbytes: int = 1 << 30, reps: int = 20) -> dict:
+    """Reference bandwidths on this GPU, for comparing the path's kernels
+    with what plain streaming reaches on the same device: the reference
+    kernels of libmoe_stream_probe.so (grid-stride read, copy and write, plain
+    and non-temporal, over a grid sweep; rows written whole by one workgroup,
+    one or eight per workgroup) and torch's fill, max reduction and copy, all
+    over ``nbytes``.  Mean of ``reps`` launches after 3 warm-up launches, timed
+    with HIP events; GB/s counts the bytes read plus written."""
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    hev = HipEvents()
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    lib = _probe_library()
+
+    def probe(kind, nt, grid=0, row_bytes=0, rpb=0):
+        def run():
+            rc = lib.moe_probe_stream(PROBE_KINDS[kind], nt, ctypes.c_void_p(b.data_ptr()),
+                                      ctypes.c_void_p(a.data_ptr()), nbytes, grid, row_bytes, rpb,
+                                      ctypes.c_void_p(sh))
+            if rc != 0:
+                raise RuntimeError(f"moe_probe_stream({kind}) returned {rc}")
+        return run
+
+    ops = {"torch fill": (lambda: b.fill_(2), nbytes),
+           "torch max": (lambda: a.max(), nbytes),
+           "torch copy": (lambda: b.copy_(a), 2 * nbytes)}
+    for kind, moved in (("read", nbytes), ("copy", 2 * nbytes), ("write", nbytes)):
+        for nt in (0, 1):
+            for grid in (1024, 2048, 4096, 8192, 16384):
+                ops[f"{kind} {'nt' if nt else 'plain'} grid={grid}"] = (probe(kind, nt, grid=grid), moved)
+    for kind, moved in (("oneshot_write", nbytes), ("oneshot_copy", 2 * nbytes)):
+        for nt in (0, 1):
+            for v in (1, 2, 4, 8):
+                ops[f"{kind} {'nt' if nt else 'plain'} {v} vec/lane"] = (probe(kind, nt, rpb=v), moved)
+    for row_bytes, rpb in ((16384, 1), (65536, 1), (262144, 1), (14336, 1), (14336, 8)):
+        for nt in (0, 1):
+            written = nbytes // (row_bytes * rpb) * row_bytes * rpb
+            ops[f"rows {'nt' if nt else 'plain'} {row_bytes} B x{rpb}/workgroup"] = (
+                probe("rows", nt, row_bytes=row_bytes, rpb=rpb), written)
+    out = {}
+    for name, (fn, moved) in ops.items():
+        for _ in range(3):
+            fn()
+        evs = [(hev.create(), hev.create()) for _ in range(reps)]
+        for e0, e1 in evs:
+            hev.record(e0, sh)
+            fn()
+            hev.record(e1, sh)
+        torch.cuda.synchronize(dev)
+        ms = sum(hev.elapsed_ms(e0, e1) for e0, e1 in evs) / reps
+        for e0, e1 in evs:
+            hev.destroy(e0)
+            hev.destroy(e1)
+        gbs = moved / (ms / 1e3) / 1e9
+        out[name] = {"bytes": moved, "us_mean": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                     "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1)}
+        print(f"# {name:40s} {ms * 1e3:9.1f} us {gbs:8.1f} GB/s", file=sys.stderr, flush=True)
+    best = {}
+    for name, rec in out.items():
+        family = name.split(" grid=")[0].split(" vec/lane")[0].rsplit(" ", 1)[0] \
+            if name.startswith("oneshot") else name.split(" grid=")[0]
+        if family not in best or rec["gbs"] > best[family]["gbs"]:
+            best[family] = {"variant": name, "gbs": rec["gbs"], "pct_of_peak": rec["pct_of_peak"]}
+    return {"ceilings": out, "best": best, "nbytes": nbytes, "reps": reps}
+
+
 def calibrate_copy(nbytes: int, reps: int) -> None:
     """A plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -743,6 +826,8 @@ def main() -> int:
                          "may use, at most 16; 1 skips it)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter calibration)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only time plain 1 GiB fill / read / copy (reference bandwidths)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -752,6 +837,9 @@ def main() -> int:
         return 2
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, max(args.steps, 1))
+        return 0
+    if args.ceilings:
+        print(json.dumps(ceilings()), flush=True)
         return 0
 
     import synth

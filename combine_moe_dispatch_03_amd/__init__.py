@@ -146,12 +146,22 @@ def _fast():
 
 # ---------------------------------------------------------------- helpers
 
+def _current_stream_slow(device_index: int) -> int:
+    return torch.cuda.current_stream(device_index).cuda_stream
+
+
+# The current stream's raw handle without building a torch Stream object
+# (that costs a few microseconds per call and would dominate a decode step).
+# The fast query is torch-internal; if a torch version lacks it, the public
+# (slower) one is used.
+_current_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", _current_stream_slow)
+
+
 def _stream(stream, device_index: int) -> int:
     """Raw HIP stream handle: the given stream, else the current stream of the
-    handle's device (read without building a torch Stream object, which costs
-    a few microseconds per call and would dominate a decode step)."""
+    handle's device."""
     if stream is None:
-        return torch._C._cuda_getCurrentRawStream(device_index)
+        return _current_raw_stream(device_index)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 

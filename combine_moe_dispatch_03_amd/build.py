@@ -24,6 +24,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libmoe_a2a.so")
 SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.hip")]
 ARCH = "gfx950"
+# Reference streaming kernels (plain read / copy / write), loaded only by
+# the benchmark's ceilings mode; no part of the dispatch/combine path.
+PROBE_LIBRARY = os.path.join(PKG, "libmoe_stream_probe.so")
+PROBE_SOURCE = os.path.join(CSRC, "stream_probe.hip")
 FAST_SOURCE = os.path.join(CSRC, "pyfast.c")
 FAST_MODULE = os.path.join(PKG, "_moe_fast" + sysconfig.get_config_var("EXT_SUFFIX"))
 
@@ -64,10 +68,9 @@ def check_device_feature() -> None:
             raise RuntimeError("the gfx950 device pass does not accept -packed-fp32-ops:\n" + out)
 
 
-def build(output: str = LIBRARY, verbose: bool = False) -> str:
-    check_device_feature()
+def _hipcc_shared(output: str, sources: list, verbose: bool) -> None:
     tmp = output + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *SOURCES]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -78,8 +81,14 @@ def build(output: str = LIBRARY, verbose: bool = False) -> str:
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(tmp, output)
+
+
+def build(output: str = LIBRARY, verbose: bool = False) -> str:
+    check_device_feature()
+    _hipcc_shared(output, SOURCES, verbose)
     if output == LIBRARY:
         build_fast(verbose)
+        _hipcc_shared(PROBE_LIBRARY, [PROBE_SOURCE], verbose)
     return output
 
 

@@ -283,3 +283,36 @@ def test_dispatch_and_combine_reject_overlapping_buffers(lib):
     assert f(far, far, far + 4 * rows, far + 16) == moe.MOE_ERR_ARG          # normed over residual
     assert f(far, far + 16, far + 4 * rows, far + 2 * rows) == moe.MOE_ERR_ARG  # residual_out shifted
     assert h.phase == 1
+
+
+def test_stream_probe_library_rejects_bad_arguments_before_any_launch():
+    """The reference streaming kernels' library (the benchmark's ceilings
+    mode) exports its one entry point, and every malformed call returns -1
+    without a HIP call (the fake addresses are never used)."""
+    from combine_moe_dispatch_03_amd import build
+    if not os.path.exists(build.PROBE_LIBRARY):
+        build.build()
+    out = subprocess.run(["nm", "-D", "--defined-only", build.PROBE_LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    assert set(re.findall(r" T (moe_\w+)", out)) == {"moe_probe_stream"}
+    probe = ctypes.CDLL(build.PROBE_LIBRARY).moe_probe_stream
+    probe.restype = ctypes.c_int
+    probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                      ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    dst, src = 0x7F0000000000, 0x7F1000000000
+    bad = [
+        (0, 0, dst, src, 0, 1024, 0, 0),            # no bytes
+        (0, 0, dst, src, 1000, 1024, 0, 0),         # not a multiple of 16
+        (0, 0, dst + 8, src, 1 << 20, 1024, 0, 0),  # misaligned dst
+        (1, 0, dst, src + 4, 1 << 20, 1024, 0, 0),  # misaligned src
+        (1, 0, dst, None, 1 << 20, 1024, 0, 0),     # copy without a source
+        (2, 0, dst, None, 1 << 20, 0, 0, 0),        # grid 0
+        (2, 0, dst, None, 1 << 20, (1 << 20) + 1, 0, 0),
+        (0, 0, dst, src, 4096, 2048, 0, 0),         # read sink larger than dst
+        (3, 0, dst, None, 1 << 20, 0, 100, 1),      # row not a multiple of 16
+        (3, 0, dst, None, 1 << 20, 0, 16384, 0),    # no rows per workgroup
+        (3, 0, dst, None, 1 << 13, 0, 16384, 1),    # not one whole row
+        (7, 0, dst, src, 1 << 20, 1024, 0, 0),      # unknown kind
+    ]
+    for args in bad:
+        assert probe(*args, None) == -1, args
