@@ -432,7 +432,7 @@ __device__ __forceinline__ void store_rows_fp8(const DispatchArgs &a, const u32x
     }
 }
 
-// dispatch_copy_kernel<VPT, NT, FP8, C>: grid = (blocks of C copies, column
+// dispatch_copy_kernel<VPT, NT, FP8, C, ROW_FIRST>: grid = (blocks of C copies, column
 // blocks), a launch covering tokens t_base ... ; each thread moves VPT 16-byte
 // vectors of the token's row, vector v of block cb at (cb*VPT + v)*256 + tid,
 // so every vector step is one coalesced 4 KB stripe.
@@ -455,12 +455,34 @@ __device__ __forceinline__ void store_rows_fp8(const DispatchArgs &a, const u32x
 // row's scale and converts the whole row) C = 4.
 // Every block computes the slots of all its token's copies (a few hundred
 // bytes from L2); only group 0, column block 0 writes the index maps.
-// The source loads are issued first (they do not depend on the slots) and
-// unconditionally (lanes past the row end re-read the row's last vector and
-// store nothing), so they are all in flight while the slots are computed.
+// Load order: vector memory loads complete in the order they are issued, so a
+// wait for one load also waits for every load issued before it.  With
+// ROW_FIRST the source row's loads go first, then the token's ids and
+// in-chunk ranks; the earlier chunks' histogram entries are read after the
+// first barrier.  Without it the slot computation's loads (ids, ranks and the
+// histogram entries, at most kPreLoads per thread) are issued first and the
+// row's last, so the slots are computed while the row is still in flight and
+// only the stores wait for it.  When the prefix is summed per copy its
+// histogram entries depend on the copies' regions, so there the ids' round
+// trip comes before them.  Dispatch us, warm / after a 1 GiB cache-evicting
+// read, row first -> row last: prefill 92.5 / 96.1 -> 93.1 / 99.9, fused
+// 50.2 / 52.7 -> 49.8 / 53.7, skewed 180.3 / 187.4 -> 180.6 / 186.5,
+// per-region prefill 61.6 / 72.9 -> 63.2 / 69.3, per-region skewed
+// 90.8 / 118.1 -> 86.4 / 106.2, fp8 prefill 51.2 / 59.5 -> 50.6 / 57.4,
+// per-region fp8 prefill 42.2 / 47.0 -> 40.3 / 45.6.  A block that writes
+// few rows per row it reads (the per-region layout, ~5.3 rows per token at
+// top-8 of 8 regions; the fp8 payload, a quarter of the bytes per row) gains
+// from overlapping the row's latency with its slot computation; the
+// per-copy bf16 copy writes 8 rows per row read and is faster cold with the
+// row requested first.  Issuing its histogram loads together with the ids
+// (one round trip fewer) made the skewed dispatch faster warm (180 -> 172)
+// but slower cold (188 -> 202) and prefill 6 us slower cold, so that case
+// keeps the order above.  Loads of the row are unconditional (lanes past the
+// row end re-read the row's last vector and store nothing).
 // NT marks the workspace stores non-temporal; FP8 writes e4m3 codes and a
 // row scale instead of the bf16 row (each block finds the row's scale).
-template <int VPT, bool NT, bool FP8, int C>
+constexpr int kPreLoads = 4;                   // prefix loads per thread issued with the slots' own
+template <int VPT, bool NT, bool FP8, int C, bool ROW_FIRST>
 __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a) {
     __shared__ int32_t base[MOE_MAX_EP];
     __shared__ int32_t cbase[MOE_MAX_TOP_K];
@@ -487,8 +509,6 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
     }
     if (a.count_only || t >= a.T) return;
 
-    // The source row does not depend on the slots: start its loads first so
-    // they overlap the slot computation below.
     const int vpr = a.H >> 3;                   // 16-byte vectors per row
     const uint16_t *src = a.x + (int64_t)t * a.H;
     u32x4 v[VPT];
@@ -498,17 +518,19 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
     for (int q = 0; q < VPT; ++q) {
         col[q] = (cb * VPT + q) * kThreads + tid;
         off[q] = (int64_t)min(col[q], vpr - 1) * 8;
-        v[q] = load16(src + off[q]);
+    }
+    if constexpr (ROW_FIRST) {
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) v[q] = load16(src + off[q]);
     }
 
-    // This token's ids and in-chunk ranks (independent of the prefix too).
-    int d = -1, rank = 0;
-    const int64_t f = (int64_t)t * a.k + tid;
+    // This token's ids and in-chunk ranks.
+    const int64_t f0 = (int64_t)t * a.k;
+    const int64_t f = f0 + tid;
+    int e = -1, rank = 0;
     if (tid < a.k) {
-        const int e = a.ids[f];
+        e = a.ids[f];
         rank = a.rank[f];                       // meaningful only for a ranked copy
-        if (e >= 0 && e < a.n_experts) d = region_of(a, e);
-        dests[tid] = d;
     }
 
     // Slots of this token's copies: copies of earlier chunks come first,
@@ -522,17 +544,83 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
     int kp = 1;
     while (kp < a.k) kp <<= 1;
     const bool by_copy = a.per_region ? 2 * kp < ep : kp < ep;
+    const int chunk = t / a.tokens_per_chunk;
+    // Per region: entries i = tid + q*256 of the chunk * ep entries before
+    // this chunk.  Per copy: copy j = tid / lanes sums chunks sub, sub +
+    // lanes, ... of its own region (lanes = 256 / kp threads per copy).
+    const int lanes = kThreads / kp;
+    const int pj = tid / lanes, sub = tid % lanes;
+    int pd = -1;                                // per copy: region of copy pj
+    int pre[kPreLoads];
+    if constexpr (ROW_FIRST) {
+        // the histogram entries are read after the first barrier
+    } else if (by_copy) {
+        if (pj < a.k) {
+            const int ej = a.ids[f0 + pj];
+            if (ej >= 0 && ej < a.n_experts) pd = region_of(a, ej);
+        }
+#pragma unroll
+        for (int q = 0; q < kPreLoads; ++q) {
+            const int c = sub + q * lanes;
+            pre[q] = (pd >= 0 && c < chunk) ? a.hist[(int64_t)c * ep + pd] : 0;
+        }
+    } else {
+        const int n_pre = chunk * ep;
+#pragma unroll
+        for (int q = 0; q < kPreLoads; ++q) {
+            const int i = tid + q * kThreads;
+            pre[q] = i < n_pre ? a.hist[i] : 0;
+        }
+    }
+
+    if constexpr (!ROW_FIRST) {                 // the source row, after every load the slots need
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) v[q] = load16(src + off[q]);
+    }
+
+    int d = -1;
+    if (tid < a.k) {
+        if (e >= 0 && e < a.n_experts) d = region_of(a, e);
+        dests[tid] = d;
+    }
     if (by_copy) {
         if (tid < a.k) cbase[tid] = 0;
     } else {
         for (int r = tid; r < ep; r += kThreads) base[r] = 0;
     }
     __syncthreads();
-    const int chunk = t / a.tokens_per_chunk;
-    if (by_copy)
-        add_copy_sums(cbase, dests, a.hist, chunk, ep, a.k, tid);
-    else
-        add_region_sums(base, a.hist, chunk * ep, ep, tid);
+    if constexpr (ROW_FIRST) {
+        if (by_copy)
+            add_copy_sums(cbase, dests, a.hist, chunk, ep, a.k, tid);
+        else
+            add_region_sums(base, a.hist, chunk * ep, ep, tid);
+    } else if (by_copy) {
+        if (pj < a.k && pd >= 0) {
+            int sum = 0;
+#pragma unroll
+            for (int q = 0; q < kPreLoads; ++q) sum += pre[q];
+            for (int c = sub + kPreLoads * lanes; c < chunk; c += lanes)   // k > 16 only
+                sum += a.hist[(int64_t)c * ep + pd];
+            if (sum != 0) atomicAdd(&cbase[pj], sum);
+        }
+    } else {
+        const int n_pre = chunk * ep;
+        if (kThreads % ep == 0) {               // every entry of this thread is region tid % ep
+            int sum = 0;
+#pragma unroll
+            for (int q = 0; q < kPreLoads; ++q) sum += pre[q];
+            for (int i = tid + kPreLoads * kThreads; i < n_pre; i += kThreads) sum += a.hist[i];
+            if (sum != 0) atomicAdd(&base[tid % ep], sum);
+        } else {
+#pragma unroll
+            for (int q = 0; q < kPreLoads; ++q) {
+                const int i = tid + q * kThreads;
+                if (i < n_pre) atomicAdd(&base[i % ep], pre[q]);
+            }
+            for (int i = tid + kPreLoads * kThreads; i < n_pre; i += kThreads)
+                atomicAdd(&base[i % ep], a.hist[i]);
+        }
+    }
     __syncthreads();
     const int before = d < 0 ? 0 : by_copy ? cbase[tid] : base[d];
     assign_rows(a, d, tid, cb | grp, f, before, rank, dests, rows, copy_rows);
@@ -598,7 +686,17 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
     if (t >= a.T) return;                       // past the batch in the last group of 8 tokens
     const bool first_block = (grp | cb) == 0;   // writes the token's index maps
 
-    // loads: the source row, this token's ids, the ids of every earlier token
+    // loads: this token's ids and the ids of every earlier token, then the
+    // source row (loads complete in issue order: the count below waits only
+    // for the ids, the stores for the row)
+    const int64_t mine = (int64_t)t * a.k;      // this token's first copy
+    const int own_id = tid < a.k ? a.ids[mine + tid] : -1;
+    int eid[kSmallPer];
+#pragma unroll
+    for (int p = 0; p < kSmallPer; ++p) {
+        const int64_t i = (int64_t)p * kThreads + tid;
+        eid[p] = i < mine ? a.ids[i] : -1;
+    }
     const int vpr = a.H >> 3;
     const uint16_t *src = a.x + (int64_t)t * a.H;
     u32x4 v[VPT];
@@ -609,14 +707,6 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
         col[q] = (cb * VPT + q) * kThreads + tid;
         off[q] = (int64_t)min(col[q], vpr - 1) * 8;
         v[q] = load16(src + off[q]);
-    }
-    const int64_t mine = (int64_t)t * a.k;      // this token's first copy
-    const int own_id = tid < a.k ? a.ids[mine + tid] : -1;
-    int eid[kSmallPer];
-#pragma unroll
-    for (int p = 0; p < kSmallPer; ++p) {
-        const int64_t i = (int64_t)p * kThreads + tid;
-        eid[p] = i < mine ? a.ids[i] : -1;
     }
     for (int r = tid; r < ep; r += kThreads) cnt[r] = 0;
     int d = -1;
@@ -888,12 +978,21 @@ int combine_group(int vpt, bool fused, const CombineArgs &a) {
 
 template <int VPT, bool FP8, int C>
 void launch_copy_c(const DispatchArgs &a, dim3 grid, hipStream_t s, bool small) {
-    if (small)
+    if (small) {
         hipLaunchKernelGGL((dispatch_small_kernel<VPT, kCopyNT, FP8, C>), grid, dim3(kThreads), 0, s,
                            a);
-    else
-        hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT, FP8, C>), grid, dim3(kThreads), 0, s,
-                           a);
+        return;
+    }
+    // the source row first only for the per-copy bf16 copy (see dispatch_copy_kernel)
+    if constexpr (!FP8) {
+        if (!a.per_region) {
+            hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT, FP8, C, true>), grid, dim3(kThreads),
+                               0, s, a);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT, FP8, C, false>), grid, dim3(kThreads), 0, s,
+                       a);
 }
 
 template <int VPT, bool FP8>
