@@ -355,23 +355,20 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Payload writers: the token's row (VPT vectors of 8 bf16 per thread, lanes
 // with col >= vpr hold a duplicate vector and store nothing) goes to the rows
-// copy_rows[j0 .. j1-1] (-1 = nothing to write).
-template <int VPT, bool NT>
+// copy_rows[j0 .. j1-1] (-1 = nothing to write), with buffer stores of cache
+// policy POLICY (a uniform row base; offsets stay inside the row).
+template <int VPT, int POLICY>
 __device__ __forceinline__ void store_rows_bf16(const DispatchArgs &a, const u32x4 (&v)[VPT],
                                                 const int (&col)[VPT], const int64_t (&off)[VPT],
                                                 int vpr, const int32_t *copy_rows, int j0, int j1) {
     for (int j = j0; j < j1; ++j) {
         const int row = uniform(copy_rows[j]);
         if (row < 0) continue;
-        uint16_t *dst = a.ws + (int64_t)row * a.H;
+        const __amdgpu_buffer_rsrc_t dst = row_rsrc(a.ws + (int64_t)row * a.H, a.H);
 #pragma unroll
         for (int q = 0; q < VPT; ++q) {
             if (col[q] >= vpr) continue;
-            u32x4 *p = reinterpret_cast<u32x4 *>(dst + off[q]);
-            if (NT)
-                __builtin_nontemporal_store(v[q], p);
-            else
-                *p = v[q];
+            __builtin_amdgcn_raw_buffer_store_b128(v[q], dst, (int)(off[q] * sizeof(uint16_t)), 0, POLICY);
         }
     }
 }
@@ -381,7 +378,7 @@ __device__ __forceinline__ void store_rows_bf16(const DispatchArgs &a, const u32
 // q = e4m3(x * (448/amax)) with gfx950's nearest-even conversion
 // (v_cvt_pk_fp8_f32), 8 codes per 8-byte store; an all-zero row gets scale 0
 // and zero codes.  The whole row must be in the block (one column block).
-template <int VPT, bool NT>
+template <int VPT, int POLICY>
 __device__ __forceinline__ void store_rows_fp8(const DispatchArgs &a, const u32x4 (&v)[VPT],
                                                const int (&col)[VPT], const int64_t (&off)[VPT],
                                                int vpr, const int32_t *copy_rows, float *red,
@@ -418,21 +415,18 @@ __device__ __forceinline__ void store_rows_fp8(const DispatchArgs &a, const u32x
     for (int j = j0; j < j1; ++j) {
         const int row = uniform(copy_rows[j]);
         if (row < 0) continue;
-        uint8_t *dst = a.ws8 + (int64_t)row * a.H;
+        const __amdgpu_buffer_rsrc_t dst =
+            __builtin_amdgcn_make_buffer_rsrc(a.ws8 + (int64_t)row * a.H, 0, a.H, 0x00020000);
 #pragma unroll
         for (int q = 0; q < VPT; ++q) {
             if (col[q] >= vpr) continue;
-            u32x2 *p = reinterpret_cast<u32x2 *>(dst + off[q]);
-            if (NT)
-                __builtin_nontemporal_store(qv[q], p);
-            else
-                *p = qv[q];
+            __builtin_amdgcn_raw_buffer_store_b64(qv[q], dst, (int)off[q], 0, POLICY);
         }
         if (tid == 0) a.scales[row] = scale;
     }
 }
 
-// dispatch_copy_kernel<VPT, NT, FP8, C, ROW_FIRST>: grid = (blocks of C copies, column
+// dispatch_copy_kernel<VPT, POLICY, FP8, C, ROW_FIRST>: grid = (blocks of C copies, column
 // blocks), a launch covering tokens t_base ... ; each thread moves VPT 16-byte
 // vectors of the token's row, vector v of block cb at (cb*VPT + v)*256 + tid,
 // so every vector step is one coalesced 4 KB stripe.
@@ -479,10 +473,10 @@ __device__ __forceinline__ void store_rows_fp8(const DispatchArgs &a, const u32x
 // but slower cold (188 -> 202) and prefill 6 us slower cold, so that case
 // keeps the order above.  Loads of the row are unconditional (lanes past the
 // row end re-read the row's last vector and store nothing).
-// NT marks the workspace stores non-temporal; FP8 writes e4m3 codes and a
-// row scale instead of the bf16 row (each block finds the row's scale).
+// POLICY is the cache policy of the workspace stores; FP8 writes e4m3 codes
+// and a row scale instead of the bf16 row (each block finds the row's scale).
 constexpr int kPreLoads = 4;                   // prefix loads per thread issued with the slots' own
-template <int VPT, bool NT, bool FP8, int C, bool ROW_FIRST>
+template <int VPT, int POLICY, bool FP8, int C, bool ROW_FIRST>
 __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a) {
     __shared__ int32_t base[MOE_MAX_EP];
     __shared__ int32_t cbase[MOE_MAX_TOP_K];
@@ -626,9 +620,9 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
     assign_rows(a, d, tid, cb | grp, f, before, rank, dests, rows, copy_rows);
     const int j0 = grp * C, j1 = min(a.k, j0 + C);
     if constexpr (FP8)
-        store_rows_fp8<VPT, NT>(a, v, col, off, vpr, copy_rows, red, tid, j0, j1);
+        store_rows_fp8<VPT, POLICY>(a, v, col, off, vpr, copy_rows, red, tid, j0, j1);
     else
-        store_rows_bf16<VPT, NT>(a, v, col, off, vpr, copy_rows, j0, j1);
+        store_rows_bf16<VPT, POLICY>(a, v, col, off, vpr, copy_rows, j0, j1);
 }
 
 template <bool NT>
@@ -651,7 +645,7 @@ __device__ __forceinline__ void accumulate(float (&acc)[VPT][8], const u32x4 (&r
 }
 
 // ---------------------------------------------------------------------------
-// dispatch_small_kernel<VPT, NT, FP8, C>: the whole dispatch in one launch,
+// dispatch_small_kernel<VPT, POLICY, FP8, C>: the whole dispatch in one launch,
 // for batches of at most kSmallItems routed copies (decode).  Grid and block
 // order as dispatch_copy_kernel: blocks of C copies of one token, a token's
 // blocks 8 indices apart so they share an XCD, x column blocks.  In place of
@@ -667,7 +661,7 @@ __device__ __forceinline__ void accumulate(float (&acc)[VPT][8], const u32x4 (&r
 static_assert(kSmallItems % kThreads == 0, "small-batch ids are split evenly over a block");
 constexpr int kSmallPer = kSmallItems / kThreads;
 
-template <int VPT, bool NT, bool FP8, int C>
+template <int VPT, int POLICY, bool FP8, int C>
 __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a) {
     __shared__ int32_t cnt[MOE_MAX_EP];
     __shared__ int32_t dests[MOE_MAX_TOP_K];
@@ -755,9 +749,9 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
     assign_rows(a, d, tid, cb | grp, mine + tid, d < 0 ? 0 : cnt[d], rank, dests, rows, copy_rows);
     const int j0 = grp * C, j1 = min(a.k, j0 + C);
     if constexpr (FP8)
-        store_rows_fp8<VPT, NT>(a, v, col, off, vpr, copy_rows, red, tid, j0, j1);
+        store_rows_fp8<VPT, POLICY>(a, v, col, off, vpr, copy_rows, red, tid, j0, j1);
     else
-        store_rows_bf16<VPT, NT>(a, v, col, off, vpr, copy_rows, j0, j1);
+        store_rows_bf16<VPT, POLICY>(a, v, col, off, vpr, copy_rows, j0, j1);
 }
 
 // G rows starting at compacted copy j0: all G x VPT loads, then the adds in
@@ -951,7 +945,26 @@ int column_blocks(int32_t H, int vpt) {
 // 8 rows x 4 vectors (32 loads in flight per thread) is the best plain
 // combine shape.  Wider rows (8 vectors per thread) use groups of 4 rows to
 // keep the register count near 200.
-constexpr bool kCopyNT = true;
+// Workspace store policy.  The routed copy stores non-temporal with sc1 set.
+// Step us, back-to-back dispatch -> combine, nt -> nt + sc1 (two runs each):
+// prefill 175.0, 174.5 -> 174.0, 173.0; fused 99.8, 99.6 -> 98.6, 98.9;
+// skewed 344.6, 345.3 -> 339.3, 342.4; per-region prefill 122.8, 122.9 ->
+// 119.9, 119.3; per-region skewed 172.4, 172.5 -> 173.1, 172.3 (its
+// dispatch 87.0 -> 83.7).  nt + sc0 + sc1 measured the same as nt + sc1, and
+// nt + sc0 the same as nt.  Plain stores made the prefill dispatch 84 us but
+// its combine 84 -> 90 us and the skewed step 345 -> 366 us: the dirty rows'
+// write-back moves into the next kernel.  The single-launch decode dispatch
+// stays plain non-temporal: with sc1 its combine, which then reads the rows
+// from HBM rather than the caches, took 5.8 instead of 4.4 us (decode step
+// 8.9 -> 11.1 us).  The same holds while a routed copy's rows fit the caches
+// (T = 512, 59 MB: step 26.4 -> 28.9 us with sc1), so sc1 is set only above
+// kCopyWriteThroughBytes of rows (T = 1024, 117 MB: 49.0 either way;
+// T = 1536: 69.8 -> 69.0; T = 2048: 91.0 -> 89.3), and only for the per-copy
+// bf16 layout (the per-region skewed step lost 5 us with it, the fp8 payload
+// measured the same).
+constexpr int kCopyPolicy = kPolicyNT | kPolicySC1;
+constexpr int kSmallPolicy = kPolicyNT;
+constexpr int64_t kCopyWriteThroughBytes = int64_t(128) << 20;
 // Copies per dispatch_copy_kernel block (bf16 and fp8 payloads), and the
 // most blocks along x in one launch (a launch must hold fewer than 2^32
 // lanes).
@@ -979,19 +992,25 @@ int combine_group(int vpt, bool fused, const CombineArgs &a) {
 template <int VPT, bool FP8, int C>
 void launch_copy_c(const DispatchArgs &a, dim3 grid, hipStream_t s, bool small) {
     if (small) {
-        hipLaunchKernelGGL((dispatch_small_kernel<VPT, kCopyNT, FP8, C>), grid, dim3(kThreads), 0, s,
+        hipLaunchKernelGGL((dispatch_small_kernel<VPT, kSmallPolicy, FP8, C>), grid, dim3(kThreads), 0, s,
                            a);
         return;
     }
-    // the source row first only for the per-copy bf16 copy (see dispatch_copy_kernel)
+    // the source row first only for the per-copy bf16 copy (see dispatch_copy_kernel),
+    // which also stores with sc1 once its rows outgrow kCopyWriteThroughBytes
     if constexpr (!FP8) {
         if (!a.per_region) {
-            hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT, FP8, C, true>), grid, dim3(kThreads),
-                               0, s, a);
+            const int64_t written = (int64_t)a.T * a.k * a.H * (int64_t)sizeof(uint16_t);
+            if (written > kCopyWriteThroughBytes)
+                hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyPolicy, FP8, C, true>), grid,
+                                   dim3(kThreads), 0, s, a);
+            else
+                hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kPolicyNT, FP8, C, true>), grid,
+                                   dim3(kThreads), 0, s, a);
             return;
         }
     }
-    hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kCopyNT, FP8, C, false>), grid, dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((dispatch_copy_kernel<VPT, kPolicyNT, FP8, C, false>), grid, dim3(kThreads), 0, s,
                        a);
 }
 
