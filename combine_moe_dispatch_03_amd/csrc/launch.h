@@ -17,8 +17,10 @@ constexpr int kMaxChunks = 64;
 
 // Batches of at most this many routed copies dispatch in one launch: each
 // block counts the regions of all earlier copies itself (see
-// dispatch_small_kernel), so no separate routing kernel runs.
-constexpr int kSmallItems = 2048;
+// dispatch_small_kernel), so no separate routing kernel runs.  Up to
+// kSmallItemsShort copies each lane holds 8 of the ids, above that 16.
+constexpr int kSmallItems = 4096;
+constexpr int kSmallItemsShort = 2048;
 
 // True when dispatch uses the single-launch path.
 inline bool dispatch_is_small(int32_t num_tokens, int32_t top_k) {

@@ -182,7 +182,7 @@ int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
  * Copies past cap are dropped (slot_index -1) and set MOE_STATUS_OVERFLOW;
  * ids outside [-1, E) are dropped and set MOE_STATUS_EXPERT_ID; both are
  * reported by moe_sync_status.
- * Batches of at most 2048 routed copies (T * k) run as one kernel launch;
+ * Batches of at most 4096 routed copies (T * k) run as one kernel launch;
  * larger ones run the routing kernel, then the copy kernel.
  * The workspace must not overlap x or topk_ids, and none of the three may
  * overlap the handle's device buffers (MOE_ERR_ARG).

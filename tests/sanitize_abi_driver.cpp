@@ -55,7 +55,7 @@ hipError_t launch_combine(const CombineArgs &a, bool fused, hipStream_t) {
 #define LAUNCHES(call, n) do { int before_ = moe::launches; CHECK((call) == MOE_OK); CHECK(moe::launches - before_ == (n)); } while (0)
 
 int main() {
-    const int32_t T = 512, H = 128, k = 8, E = 64, ep = 8;
+    const int32_t T = 640, H = 128, k = 8, E = 64, ep = 8;
     // aligned host buffers stand in for device memory: the stubs never dereference them
     std::vector<int32_t> counts(ep), src(ep * T), slot(T * k), status(4);
     // stand-ins sized as the handle declares them (cap = T), so the overlap
@@ -87,7 +87,11 @@ int main() {
     CHECK(h.phase == 0);
     LAUNCHES(moe_dispatch(&h, x, ids, 256, 256, ws, nullptr), 1);      // 2048 copies: single launch
     LAUNCHES(moe_combine_residual_rmsnorm(&h, ws, w, 1, res, res, gam, 1e-6f, nrm, nullptr), 1);
-    LAUNCHES(moe_dispatch(&h, x, ids, 257, 300, ws, nullptr), 2);      // first routed size
+    LAUNCHES(moe_dispatch(&h, x, ids, 257, 300, ws, nullptr), 1);      // 2056 copies: single launch
+    CHECK(moe_reset(&h) == MOE_OK && h.phase == 0);
+    LAUNCHES(moe_dispatch(&h, x, ids, 512, 512, ws, nullptr), 1);      // 4096 copies: the last single launch
+    CHECK(moe_reset(&h) == MOE_OK && h.phase == 0);
+    LAUNCHES(moe_dispatch(&h, x, ids, 513, 600, ws, nullptr), 2);      // first routed size
     CHECK(moe_reset(&h) == MOE_OK && h.phase == 0);
     LAUNCHES(moe_dispatch_fp8(&h, x, ids, T, T, ws8, scales, nullptr), 2);
     CHECK(moe_reset(&h) == MOE_OK);

@@ -78,8 +78,10 @@ ROUNDTRIP_CASES = [
     ("odd_hidden", 7, 9000, 5, 40, 5),
     ("max_regions_max_topk", 24, 64, 64, 512, 256),
     ("many_chunks_ragged", 4099, 24, 6, 36, 6),
-    ("single_launch_limit", 256, 128, 8, 64, 8),     # 2048 copies: one-launch dispatch
-    ("two_kernel_threshold", 257, 128, 8, 64, 8),    # 2056 copies: routing kernel + copy
+    ("single_launch_short_ids", 256, 128, 8, 64, 8), # 2048 copies: one launch, 8 ids per lane
+    ("single_launch_long_ids", 257, 128, 8, 64, 8),  # 2056 copies: one launch, 16 ids per lane
+    ("single_launch_limit", 512, 128, 8, 64, 8),     # 4096 copies: the last one-launch size
+    ("two_kernel_threshold", 513, 128, 8, 64, 8),    # 4104 copies: routing kernel + copy
     # the routing kernel loads its chunk's ids 4 tiles of 256 at a time:
     ("full_and_partial_tile_group", 9000, 16, 8, 64, 8),   # 1128 copies per chunk: 4 + 1 tiles
     ("five_tile_groups", 40000, 8, 8, 64, 8),              # 5000 copies per chunk: 20 tiles

@@ -1,7 +1,8 @@
 """Dispatch sequences and shapes on one handle, each compared with the oracle.
 
 * many dispatches in a row on one handle, of sizes on both sides of the
-  single-launch limit (2048 routed copies) and both layouts, each followed by
+  single-launch limit (4096 routed copies, 8 ids per lane up to 2048) and
+  both layouts, each followed by
   a combine or by moe_reset: nothing a call leaves in the handle's scratch or
   index buffers leaks into the next (bit-exact every time);
 * top-k from 1 to 64 with one to 256 regions and ragged routing chunks, on
@@ -32,7 +33,7 @@ def routing(rng, T, k, E, p_missing=0.05):
 def test_consecutive_dispatches_of_varying_size():
     orc = oracle.load()
     H, k, E, ep = 64, 8, 64, 8
-    sizes = [1, 7, 33, 4099, 128, 32, 31, 5000, 0, 257, 4099]
+    sizes = [1, 7, 33, 4099, 128, 32, 31, 5000, 0, 257, 512, 513, 256, 4099]
     for layout in ("copy", "region"):
         cap = 5000 * k if layout == "copy" else 5000
         h = moe.MoeA2A(5000, H, k, E, ep, cap, layout=layout)
