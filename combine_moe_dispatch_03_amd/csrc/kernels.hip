@@ -1086,8 +1086,15 @@ hipError_t launch_dispatch_copy(const DispatchArgs &args, hipStream_t s) {
     // padded to a multiple of 8.  Rows under kSplitMinHidden stay one block
     // per token.  The fp8 payload needs the whole row in a block for its
     // scale.
-    const int c = a.H < kSplitMinHidden ? MOE_MAX_TOP_K
-                                        : a.fp8 ? kCopiesPerBlockFp8 : kCopiesPerBlock;
+    // The single-launch kernel above kSmallItemsShort copies counts up to
+    // 4096 earlier ids in every block, so it takes a whole token per block
+    // there (one count per token instead of one per pair of copies): ladder
+    // T = 512 roundtrip 25.9 -> 25.0 us, T = 384 step 20.6 -> 19.7 us, other
+    // sizes unchanged; 4 copies per block measured the same at T = 512 but
+    // 0.8 us slower at T = 448.
+    const bool small_long = dispatch_is_small(a.T, a.k) && (int64_t)a.T * a.k > kSmallItemsShort;
+    const int c = (a.H < kSplitMinHidden || small_long) ? MOE_MAX_TOP_K
+                                                        : a.fp8 ? kCopiesPerBlockFp8 : kCopiesPerBlock;
     const int n = (a.k + c - 1) / c;
     const int64_t t_pad = ((int64_t)a.T + 7) / 8 * 8;
     const int vpt = a.fp8 ? full_row_vpt(a.H) : streaming_vpt(t_pad * n, a.H);
