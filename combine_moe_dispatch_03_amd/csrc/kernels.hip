@@ -874,9 +874,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
         // fp64 work is a few dozen operations per thread in a memory-bound
         // kernel.
         double ss = 0.0;
-        u32x4 rv[VPT];
+        // the residual and gamma in one round trip (gamma overlaps neither
+        // output, so its loads may come before the residual_out stores)
+        u32x4 rv[VPT], gv[VPT];
 #pragma unroll
         for (int q = 0; q < VPT; ++q) rv[q] = load16(a.residual + row_off + off[q]);
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) gv[q] = load16(a.gamma + off[q]);
 #pragma unroll
         for (int q = 0; q < VPT; ++q) {
             float r[8];
@@ -893,9 +897,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
         if ((tid & 63) == 0) partial[tid >> 6] = ss;
-        u32x4 gv[VPT];
-#pragma unroll
-        for (int q = 0; q < VPT; ++q) gv[q] = load16(a.gamma + off[q]);
         __syncthreads();
         double total = 0.0;
 #pragma unroll
