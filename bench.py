@@ -16,8 +16,10 @@ cost).  One JSON line is printed.
 hidden 7168, top-8 of 256 experts over 8 regions, unweighted combine).  The
 line also carries:
   roofline      the phase that takes longer of the two: the dispatch call
-                (route_rank_kernel + dispatch_copy_kernel, one C call,
-                timed as one) or the combine (combine_kernel), with HIP
+                (one C call, timed as one, whichever kernels it launches:
+                dispatch_small_kernel, dispatch_onepass_kernel, or
+                route_rank_kernel + dispatch_copy_kernel) or the combine
+                (combine_kernel), with HIP
                 events on the launch stream in the instrumented steps,
                 against MI355X's 8 TB/s HBM peak: algorithmic bytes per call
                 / mean call time; ``traffic`` is the measured HBM bytes per
@@ -138,6 +140,17 @@ class HipEvents:
 
     def destroy(self, ev) -> None:
         self.lib.hipEventDestroy(ev)
+
+
+def dispatch_kernels(items: int, layout: str, payload: str) -> str:
+    """The kernels one dispatch call launches for `items` routed copies
+    (the library's size thresholds: single launch up to 4096 copies; the
+    single-pass kernel for the per-copy bf16 layout up to 32768)."""
+    if items <= 4096:
+        return "dispatch_small_kernel"
+    if layout == "copy" and payload == "bf16" and items <= 32768:
+        return "dispatch_onepass_kernel (routing blocks + copy blocks, one launch)"
+    return "route_rank_kernel + dispatch_copy_kernel"
 
 
 def describe(wl, cap) -> str:
@@ -884,7 +897,7 @@ def main() -> int:
     phase_ms = main_res[f"{phase}_ms_mean"]
     phase_bytes = main_res[f"{phase}_bytes"]
     achieved = phase_bytes / (phase_ms / 1e3) / 1e9
-    phase_kernels = {"dispatch": "route_rank_kernel + dispatch_copy_kernel",
+    phase_kernels = {"dispatch": dispatch_kernels(wl.T * wl.k, opts["layout"], opts["payload"]),
                      "combine": "combine_kernel"}[phase]
     line = {
         "metric": "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), H=7168 top-8",

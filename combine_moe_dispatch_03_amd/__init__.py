@@ -42,12 +42,14 @@ MOE_ERR_OVERFLOW = -3
 MOE_ERR_EXPERT_ID = -4
 MOE_ERR_HIP = -5
 MOE_ERR_NOALLOC_SIZE = -6
+MOE_ERR_GAVE_UP = -7
 MOE_NOALLOC_MAX_ITEMS = 1048576
 MOE_LAYOUT_PER_COPY = 0
 MOE_LAYOUT_PER_REGION = 1
 LAYOUTS = {"copy": MOE_LAYOUT_PER_COPY, "region": MOE_LAYOUT_PER_REGION}
 MOE_STATUS_OVERFLOW = 1
 MOE_STATUS_EXPERT_ID = 2
+MOE_STATUS_GAVE_UP = 4
 MOE_MAX_EP = 256
 MOE_MAX_TOP_K = 64
 MOE_MAX_FUSED_HIDDEN = 16384
@@ -76,6 +78,7 @@ class MoeHandle(ctypes.Structure):
         ("scratch", ctypes.c_void_p), ("scratch_bytes", ctypes.c_size_t),
         ("phase", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
         ("runtime_max_tokens_per_rank", ctypes.c_int32), ("hip_error", ctypes.c_int32),
+        ("onepass_epoch", ctypes.c_uint32), ("onepass_spin_limit", ctypes.c_int32),
     ]
 
 

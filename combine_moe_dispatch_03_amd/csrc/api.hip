@@ -108,7 +108,8 @@ size_t moe_scratch_bytes(int32_t max_tokens, int32_t top_k, int32_t ep_size) {
         return 0;
     const int64_t items = (int64_t)max_tokens * top_k;
     if (items > INT32_MAX) return 0;
-    const size_t bytes = (size_t)(items + (int64_t)moe::kMaxChunks * ep_size) * sizeof(int32_t);
+    const size_t bytes = (size_t)moe::scratch_words_offset(items, ep_size) +
+                         (size_t)moe::scratch_words_count(items, ep_size) * sizeof(uint64_t);
     return (bytes + 255) & ~(size_t)255;
 }
 
@@ -175,9 +176,8 @@ static Scratch handle_scratch(const moe_handle *h) {
     return Scratch{h->scratch, (int64_t)h->max_tokens * h->top_k};
 }
 
-static int route(moe_handle *h, const Scratch &sc, const int32_t *topk_ids, int32_t num_tokens,
-                 hipStream_t s, moe::RoutePlan *plan_out) {
-    const moe::RoutePlan plan = moe::plan_route(num_tokens);
+static moe::RouteArgs route_args(moe_handle *h, const Scratch &sc, const int32_t *topk_ids,
+                                 int32_t num_tokens, const moe::RoutePlan &plan) {
     moe::RouteArgs ra;
     ra.ids = topk_ids;
     ra.rank = moe::scratch_rank(sc.base);
@@ -191,6 +191,13 @@ static int route(moe_handle *h, const Scratch &sc, const int32_t *topk_ids, int3
     ra.epr_shift = epr_shift(h);
     ra.k = h->top_k;
     ra.per_region = h->layout == MOE_LAYOUT_PER_REGION;
+    return ra;
+}
+
+static int route(moe_handle *h, const Scratch &sc, const int32_t *topk_ids, int32_t num_tokens,
+                 hipStream_t s, moe::RoutePlan *plan_out) {
+    const moe::RoutePlan plan = moe::plan_route(num_tokens);
+    const moe::RouteArgs ra = route_args(h, sc, topk_ids, num_tokens, plan);
     hipError_t e = moe::launch_route(ra, plan.n_chunks, s);
     if (e != hipSuccess) return hip_fail(h, e);
     *plan_out = plan;
@@ -226,7 +233,19 @@ static moe::DispatchArgs dispatch_args(moe_handle *h, const Scratch &sc, const u
     da.ws8 = nullptr;
     da.scales = nullptr;
     da.t_base = 0;
+    da.onepass = 0;
+    da.route_blocks = 0;
+    da.epoch = 0;
+    da.spin_limit = 0;
+    da.rank_w = nullptr;
+    da.hist_w = nullptr;
     return da;
+}
+
+
+static bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone;
 }
 
 static int dispatch_checks(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
@@ -269,8 +288,37 @@ static bool dispatch_overlaps(const moe_handle *h, const void *x, const void *id
 }
 
 static int dispatch_launch(moe_handle *h, const Scratch &sc, moe::DispatchArgs da,
-                           const int32_t *topk_ids, int32_t num_tokens, int32_t R, hipStream_t s) {
+                           const int32_t *topk_ids, int32_t num_tokens, int32_t R, hipStream_t s,
+                           bool words = false) {
     moe::RoutePlan plan = moe::plan_route(num_tokens);
+    if (words && !da.fp8 && moe::dispatch_is_onepass(num_tokens, h->top_k, da.per_region) &&
+        !capturing(s)) {
+        uint64_t *rw = moe::scratch_rank_words(sc.base, sc.max_items, h->ep_size);
+        // The handle's words are cleared on its first single-pass dispatch
+        // (moe_init zeroes onepass_epoch; epoch 0 is never used) and whenever
+        // the epoch would wrap; each dispatch then takes the next epoch.
+        if (h->onepass_epoch == 0 || h->onepass_epoch >= 0x7FFFFFFFu) {
+            const hipError_t me = hipMemsetAsync(
+                rw, 0, moe::scratch_words_count(sc.max_items, h->ep_size) * sizeof(uint64_t), s);
+            if (me != hipSuccess) return hip_fail(h, me);
+            h->onepass_epoch = 0;
+        }
+        const uint32_t epoch = ++h->onepass_epoch;
+        da.tokens_per_chunk = plan.tokens_per_chunk;
+        da.n_chunks = plan.n_chunks;
+        da.onepass = 1;
+        da.epoch = epoch;
+        da.spin_limit = h->onepass_spin_limit != 0 ? h->onepass_spin_limit : moe::kOnePassSpinLimit;
+        da.rank_w = rw;
+        da.hist_w = moe::scratch_hist_words(sc.base, sc.max_items, h->ep_size);
+        const moe::RouteArgs ra = route_args(h, sc, topk_ids, num_tokens, plan);
+        hipError_t e = moe::launch_dispatch_onepass(da, ra, s);
+        if (e != hipSuccess) return hip_fail(h, e);
+        h->phase = 1;
+        h->num_tokens = num_tokens;
+        h->runtime_max_tokens_per_rank = R;
+        return MOE_OK;
+    }
     if (!moe::dispatch_is_small(num_tokens, h->top_k)) {   // small batches need no routing kernel
         int rc = route(h, sc, topk_ids, num_tokens, s, &plan);
         if (rc != MOE_OK) return rc;
@@ -298,7 +346,7 @@ int moe_dispatch(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
     const Scratch sc = handle_scratch(h);
     const moe::DispatchArgs da = dispatch_args(h, sc, x, topk_ids, num_tokens, workspace,
                                                moe::plan_route(num_tokens), 0);
-    return dispatch_launch(h, sc, da, topk_ids, num_tokens, R, static_cast<hipStream_t>(stream));
+    return dispatch_launch(h, sc, da, topk_ids, num_tokens, R, static_cast<hipStream_t>(stream), true);
 }
 
 int moe_dispatch_noalloc(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
@@ -509,6 +557,7 @@ int moe_sync_status(moe_handle *h, void *stream, int32_t *bits) {
     if (bits) *bits = host;
     if (host & MOE_STATUS_EXPERT_ID) return MOE_ERR_EXPERT_ID;
     if (host & MOE_STATUS_OVERFLOW) return MOE_ERR_OVERFLOW;
+    if (host & MOE_STATUS_GAVE_UP) return MOE_ERR_GAVE_UP;
     return MOE_OK;
 }
 
@@ -530,6 +579,9 @@ const char *moe_strerror(int code) {
         case MOE_ERR_OVERFLOW: return "a destination region received more copies than max_tokens_per_rank";
         case MOE_ERR_EXPERT_ID: return "expert id outside [-1, num_experts)";
         case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_GAVE_UP:
+            return "a single-pass dispatch block gave up waiting for the routing words "
+                   "(its tokens were not dispatched)";
         case MOE_ERR_NOALLOC_SIZE:
             return "batch too large for the library's static routing scratch "
                    "(moe_dispatch_noalloc: num_tokens * top_k <= MOE_NOALLOC_MAX_ITEMS)";

@@ -247,15 +247,44 @@ __device__ __forceinline__ uint64_t rank_group(const Args &a, int &d, int64_t i,
 // (clamped to the chunk, so the loads are unconditional and all in flight),
 // instead of one dependent load per tile after the previous tile's barriers.
 constexpr int kTileGroup = 4;
-__global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
-    __shared__ int32_t wave_cnt[kWaves * MOE_MAX_EP];
-    __shared__ int32_t carry[MOE_MAX_EP];
 
+// Words of the single-pass dispatch: a 32-bit value under the 32-bit epoch of
+// the dispatch that wrote it, stored and loaded whole at device scope (vector
+// memory instructions with sc1), so a reader that sees its own epoch in a
+// word has that word's value; no other memory is ordered by it.
+__device__ __forceinline__ uint64_t load_word(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_word(uint64_t *p, uint32_t epoch, int32_t v) {
+    __hip_atomic_store(p, ((uint64_t)epoch << 32) | (uint32_t)v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+// The value of word p once it carries `epoch`; false after `limit` further
+// polls (each after a short sleep) without it, or at once when limit < 0.
+__device__ __forceinline__ bool wait_word(const uint64_t *p, uint32_t epoch, int limit, int &v) {
+    if (limit < 0) return false;                // a forced give-up
+    uint64_t w = load_word(p);
+    for (int n = 0; (uint32_t)(w >> 32) != epoch; ++n) {
+        if (n >= limit) return false;
+        __builtin_amdgcn_s_sleep(2);
+        w = load_word(p);
+    }
+    v = (int)(uint32_t)w;
+    return true;
+}
+
+// The body of route_rank_kernel for one chunk.  WORDS: ranks and the chunk
+// histogram go to rank_w / hist_w as words of `epoch` (the single-pass
+// dispatch) instead of a.rank / a.hist.
+template <bool WORDS>
+__device__ __forceinline__ void rank_chunk(const RouteArgs &a, int chunk, int32_t *wave_cnt,
+                                           int32_t *carry, uint64_t *rank_w, uint64_t *hist_w,
+                                           uint32_t epoch) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int ep = a.ep;
-    const int64_t begin = (int64_t)blockIdx.x * a.items_per_chunk;
+    const int64_t begin = (int64_t)chunk * a.items_per_chunk;
     const int64_t end = min(begin + (int64_t)a.items_per_chunk, a.n_items);
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
@@ -296,7 +325,10 @@ __global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
             if (d >= 0) {
                 int off = carry[d];
                 for (int w = 0; w < wave; ++w) off += wave_cnt[w * ep + d];
-                a.rank[i] = off + lane_rank;
+                if constexpr (WORDS)
+                    store_word(&rank_w[i], epoch, off + lane_rank);
+                else
+                    a.rank[i] = off + lane_rank;
             }
             __syncthreads();
             for (int r = tid; r < ep; r += kThreads) {
@@ -309,8 +341,18 @@ __global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
     }
 
     if (bad) atomicOr(a.status, MOE_STATUS_EXPERT_ID);
-    for (int r = tid; r < ep; r += kThreads)
-        a.hist[(int64_t)blockIdx.x * ep + r] = carry[r];
+    for (int r = tid; r < ep; r += kThreads) {
+        if constexpr (WORDS)
+            store_word(&hist_w[(int64_t)chunk * ep + r], epoch, carry[r]);
+        else
+            a.hist[(int64_t)chunk * ep + r] = carry[r];
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
+    __shared__ int32_t wave_cnt[kWaves * MOE_MAX_EP];
+    __shared__ int32_t carry[MOE_MAX_EP];
+    rank_chunk<false>(a, blockIdx.x, wave_cnt, carry, nullptr, nullptr, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -623,6 +665,152 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
         store_rows_fp8<VPT, POLICY>(a, v, col, off, vpr, copy_rows, red, tid, j0, j1);
     else
         store_rows_bf16<VPT, POLICY>(a, v, col, off, vpr, copy_rows, j0, j1);
+}
+
+// dispatch_onepass_kernel<VPT, POLICY, C, ROW_FIRST>: routing and copy in
+// one launch for mid-size batches (bf16 payload).  Blocks 0 .. route_blocks-1
+// (a multiple of 8, so the copy blocks keep the copy kernel's XCD grouping)
+// rank one chunk each, exactly as route_rank_kernel, into words of this
+// dispatch's epoch (ranks, and the chunk's per-region histogram).  They have
+// the lowest block indices, so they are placed on the GPU before any copy
+// block.  Every other block is a copy kernel block: it issues its source
+// loads, then its lanes read their rank and histogram words, each polled
+// until it carries the epoch (a block of an early chunk needs only the
+// chunks before its own).  A block that has polled a word spin_limit times
+// without the epoch gives up: it sets MOE_STATUS_GAVE_UP, its token's index
+// maps read -1 and it writes no row, so every block ends.  Copy block 0,
+// column block 0 also sums every chunk's histogram into counts.
+template <int VPT, int POLICY, int C, bool ROW_FIRST>
+__global__ __launch_bounds__(kThreads) void dispatch_onepass_kernel(DispatchArgs a, RouteArgs ra) {
+    __shared__ int32_t wave_cnt[kWaves * MOE_MAX_EP];
+    __shared__ int32_t carry[MOE_MAX_EP];
+    __shared__ int32_t base[MOE_MAX_EP];
+    __shared__ int32_t cbase[MOE_MAX_TOP_K];
+    __shared__ int32_t dests[MOE_MAX_TOP_K];
+    __shared__ int32_t rows[MOE_MAX_TOP_K];
+    __shared__ int32_t copy_rows[MOE_MAX_TOP_K];
+    __shared__ int32_t gave_up;
+
+    const int tid = threadIdx.x;
+    if ((int)blockIdx.x < a.route_blocks) {
+        if (blockIdx.y == 0 && (int)blockIdx.x < a.n_chunks) {
+            rank_chunk<true>(ra, blockIdx.x, wave_cnt, carry, a.rank_w, a.hist_w, a.epoch);
+        }
+        return;
+    }
+    const int cb = blockIdx.y;
+    const int ep = a.ep;
+    const int n = (a.k + C - 1) / C;
+    const int b = blockIdx.x - a.route_blocks;
+    const int grp = (b >> 3) % n;
+    const int t = ((b >> 3) / n) * 8 + (b & 7);
+    const bool totals = b == 0 && cb == 0;
+    if (!totals && t >= a.T) return;
+
+    const int vpr = a.H >> 3;
+    const uint16_t *src = a.x + (int64_t)min(t, a.T - 1) * a.H;
+    u32x4 v[VPT];
+    int col[VPT];
+    int64_t off[VPT];
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+        col[q] = (cb * VPT + q) * kThreads + tid;
+        off[q] = (int64_t)min(col[q], vpr - 1) * 8;
+    }
+    if constexpr (ROW_FIRST) {
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) v[q] = load16(src + off[q]);
+    }
+    const int64_t f0 = (int64_t)t * a.k;
+    const int64_t f = f0 + tid;
+    int e = -1;
+    if (tid < a.k && t < a.T) e = a.ids[f];
+    if constexpr (!ROW_FIRST) {
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) v[q] = load16(src + off[q]);
+    }
+    int d = -1;
+    if (tid < a.k) {
+        if (e >= 0 && e < a.n_experts) d = region_of(a, e);
+        dests[tid] = d;
+    }
+    int kp = 1;
+    while (kp < a.k) kp <<= 1;
+    const bool by_copy = a.per_region ? 2 * kp < ep : kp < ep;
+    const int chunk = t / a.tokens_per_chunk;
+    if (by_copy) {
+        if (tid < a.k) cbase[tid] = 0;
+    } else {
+        for (int r = tid; r < ep; r += kThreads) base[r] = 0;
+    }
+    if (tid == 0) gave_up = 0;
+    __syncthreads();
+    bool ok = true;
+    if (totals && ok) {                         // region totals over all chunks (in carry)
+        for (int r = tid; r < ep; r += kThreads) carry[r] = 0;
+        __syncthreads();
+        for (int i = tid; i < a.n_chunks * ep; i += kThreads) {
+            int w = 0;
+            if (!wait_word(a.hist_w + i, a.epoch, a.spin_limit, w)) ok = false;
+            if (w != 0) atomicAdd(&carry[i % ep], w);
+        }
+        __syncthreads();
+        for (int r = tid; r < ep; r += kThreads) a.counts[r] = carry[r];
+    }
+    if (t >= a.T) {                             // the totals block past the batch
+        if (!ok) atomicOr(a.status, MOE_STATUS_GAVE_UP);
+        return;
+    }
+    // this token's ranks (a rank word exists only for a ranked copy: one with
+    // a region, and under the per-region layout its token's first to it)
+    int rank = 0;
+    if (ok && tid < a.k && d >= 0) {
+        bool ranked = true;
+        if (a.per_region)
+            for (int j = 0; j < tid; ++j)
+                if (dests[j] == d) { ranked = false; break; }
+        if (ranked && !wait_word(a.rank_w + f, a.epoch, a.spin_limit, rank)) ok = false;
+    }
+    if (ok) {
+        if (by_copy) {
+            const int lanes = kThreads / kp;
+            const int j = tid / lanes, sub = tid % lanes;
+            if (j < a.k && dests[j] >= 0) {
+                int sum = 0;
+                for (int c = sub; c < chunk; c += lanes) {
+                    int w = 0;
+                    if (!wait_word(a.hist_w + (int64_t)c * ep + dests[j], a.epoch, a.spin_limit, w)) ok = false;
+                    sum += w;
+                }
+                if (sum != 0) atomicAdd(&cbase[j], sum);
+            }
+        } else {
+            int sum = 0;
+            const bool same_region = kThreads % ep == 0;
+            for (int i = tid; i < chunk * ep; i += kThreads) {
+                int w = 0;
+                if (!wait_word(a.hist_w + i, a.epoch, a.spin_limit, w)) ok = false;
+                if (same_region)
+                    sum += w;
+                else if (w != 0)
+                    atomicAdd(&base[i % ep], w);
+            }
+            if (same_region && sum != 0) atomicAdd(&base[tid % ep], sum);
+        }
+    }
+    if (!ok) gave_up = 1;
+    __syncthreads();
+    if (gave_up) {                              // uniform: nothing written for this token
+        if ((cb | grp) == 0) {
+            if (tid < a.k) a.slot_index[f] = -1;
+            if (tid == 0) atomicOr(a.status, MOE_STATUS_GAVE_UP);
+        }
+        return;
+    }
+    const int before = d < 0 ? 0 : by_copy ? cbase[tid] : base[d];
+    assign_rows(a, d, tid, cb | grp, f, before, rank, dests, rows, copy_rows);
+    const int j0 = grp * C, j1 = min(a.k, j0 + C);
+    store_rows_bf16<VPT, POLICY>(a, v, col, off, vpr, copy_rows, j0, j1);
 }
 
 template <bool NT>
@@ -1069,6 +1257,50 @@ void launch_combine_vpt(const CombineArgs &a, dim3 grid, hipStream_t s) {
 hipError_t launch_route(const RouteArgs &a, int32_t n_chunks, hipStream_t s) {
     if (n_chunks > 0)
         hipLaunchKernelGGL(route_rank_kernel, dim3(n_chunks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+namespace {
+template <int VPT, int C>
+void launch_onepass_c(const DispatchArgs &a, const RouteArgs &ra, dim3 grid, hipStream_t s) {
+    if (!a.per_region) {
+        const int64_t written = (int64_t)a.T * a.k * a.H * (int64_t)sizeof(uint16_t);
+        if (written > kCopyWriteThroughBytes)
+            hipLaunchKernelGGL((dispatch_onepass_kernel<VPT, kCopyPolicy, C, true>), grid, dim3(kThreads), 0,
+                               s, a, ra);
+        else
+            hipLaunchKernelGGL((dispatch_onepass_kernel<VPT, kPolicyNT, C, true>), grid, dim3(kThreads), 0, s,
+                               a, ra);
+        return;
+    }
+    hipLaunchKernelGGL((dispatch_onepass_kernel<VPT, kPolicyNT, C, false>), grid, dim3(kThreads), 0, s, a,
+                       ra);
+}
+
+template <int VPT>
+void launch_onepass_vpt(const DispatchArgs &a, const RouteArgs &ra, dim3 grid, hipStream_t s, int c) {
+    if (c == kCopiesPerBlock)
+        launch_onepass_c<VPT, kCopiesPerBlock>(a, ra, grid, s);
+    else
+        launch_onepass_c<VPT, MOE_MAX_TOP_K>(a, ra, grid, s);
+}
+}  // namespace
+
+hipError_t launch_dispatch_onepass(const DispatchArgs &args, const RouteArgs &ra, hipStream_t s) {
+    DispatchArgs a = args;
+    a.t_base = 0;
+    const int c = a.H < kSplitMinHidden ? MOE_MAX_TOP_K : kCopiesPerBlock;
+    const int n = (a.k + c - 1) / c;
+    const int64_t t_pad = ((int64_t)a.T + 7) / 8 * 8;
+    const int vpt = streaming_vpt(t_pad * n, a.H);
+    a.route_blocks = (a.n_chunks + 7) / 8 * 8;   // keeps the copy blocks' XCD grouping
+    const dim3 grid((uint32_t)(a.route_blocks + t_pad * n), column_blocks(a.H, vpt));
+    switch (vpt) {
+        case 1: launch_onepass_vpt<1>(a, ra, grid, s, c); break;
+        case 2: launch_onepass_vpt<2>(a, ra, grid, s, c); break;
+        case 4: launch_onepass_vpt<4>(a, ra, grid, s, c); break;
+        default: launch_onepass_vpt<8>(a, ra, grid, s, c); break;
+    }
     return hipGetLastError();
 }
 

@@ -40,11 +40,29 @@ inline RoutePlan plan_route(int32_t num_tokens) {
     return p;
 }
 
-// Scratch layout: rank[max_tokens * k] then hist[kMaxChunks * ep].
+// Scratch layout: rank[max_tokens * k] then hist[kMaxChunks * ep] (int32),
+// then, for a handle's own scratch, the single-pass dispatch's words:
+// rank words [min(max_items, kOnePassItems)] and hist words
+// [kMaxChunks * ep] (uint64, 8-byte aligned).
 inline int32_t *scratch_rank(void *scratch) { return static_cast<int32_t *>(scratch); }
 inline int32_t *scratch_hist(void *scratch, int64_t max_items) {
     return static_cast<int32_t *>(scratch) + max_items;
 }
+constexpr int64_t kOnePassWordItems = 32768;     // rank words: the single pass's largest batch
+inline int64_t scratch_words_offset(int64_t max_items, int ep) {
+    return ((max_items + (int64_t)kMaxChunks * ep) * 4 + 7) / 8 * 8;
+}
+inline int64_t scratch_words_count(int64_t max_items, int ep) {
+    return (max_items < kOnePassWordItems ? max_items : kOnePassWordItems) + (int64_t)kMaxChunks * ep;
+}
+inline uint64_t *scratch_rank_words(void *scratch, int64_t max_items, int ep) {
+    return reinterpret_cast<uint64_t *>(static_cast<char *>(scratch) + scratch_words_offset(max_items, ep));
+}
+inline uint64_t *scratch_hist_words(void *scratch, int64_t max_items, int ep) {
+    return scratch_rank_words(scratch, max_items, ep) +
+           (max_items < kOnePassWordItems ? max_items : kOnePassWordItems);
+}
+
 
 struct RouteArgs {
     const int32_t *ids;      // [T*k]
@@ -78,6 +96,15 @@ struct DispatchArgs {
     uint8_t *ws8;            // [ep, cap, H] e4m3 (fp8 payload)
     float *scales;           // [ep, cap]    row scales (fp8 payload)
     int32_t t_base;          // first token of this launch (set by launch_dispatch_copy)
+    // single-pass dispatch (onepass != 0): the first route_blocks blocks rank
+    // the chunks into rank_w / hist_w words of `epoch`; the others wait for
+    // the words they need, giving up after spin_limit polls
+    int32_t onepass;
+    int32_t route_blocks;
+    uint32_t epoch;
+    int32_t spin_limit;      // < 0: every wait gives up at once (tests of the give-up path)
+    uint64_t *rank_w;        // [T*k]
+    uint64_t *hist_w;        // [n_chunks * ep]
 };
 
 struct CombineArgs {
@@ -97,7 +124,21 @@ struct CombineArgs {
     int32_t out_cached;      // set by launch_combine: output store cache policy (see kernels.hip)
 };
 
+// Batches of more than kSmallItems and at most kOnePassItems copies in the
+// per-copy layout dispatch in one launch that ranks the chunks in its first
+// blocks (dispatch_onepass_kernel).
+constexpr int64_t kOnePassItems = kOnePassWordItems;
+inline bool dispatch_is_onepass(int32_t num_tokens, int32_t top_k, bool per_region) {
+    const int64_t items = (int64_t)num_tokens * top_k;
+    return !per_region && items > kSmallItems && items <= kOnePassItems;
+}
+// Polls of one word before a single-pass block gives up (each poll is a
+// device-scope load after a short sleep).
+constexpr int32_t kOnePassSpinLimit = 1 << 16;
+
 hipError_t launch_route(const RouteArgs &a, int32_t n_chunks, hipStream_t s);
+// The single-pass dispatch (see dispatch_onepass_kernel).
+hipError_t launch_dispatch_onepass(const DispatchArgs &a, const RouteArgs &ra, hipStream_t s);
 // Launches dispatch_small_kernel when dispatch_is_small(T, k) (no routing
 // kernel needed), dispatch_copy_kernel otherwise (after launch_route).
 hipError_t launch_dispatch_copy(const DispatchArgs &a, hipStream_t s);

@@ -64,6 +64,8 @@ extern "C" {
                                 /* moe_last_hip_error)                     */
 #define MOE_ERR_NOALLOC_SIZE (-6) /* a batch beyond the static scratch of  */
                                 /* moe_dispatch_noalloc                    */
+#define MOE_ERR_GAVE_UP   (-7)  /* a single-pass dispatch block gave up     */
+                                /* waiting (its tokens were not dispatched) */
 
 /* workspace layouts (moe_init) */
 #define MOE_LAYOUT_PER_COPY   0     /* one row per routed copy (t, j)          */
@@ -72,6 +74,7 @@ extern "C" {
 /* bits of the device status word (moe_sync_status) */
 #define MOE_STATUS_OVERFLOW  1
 #define MOE_STATUS_EXPERT_ID 2
+#define MOE_STATUS_GAVE_UP   4
 
 /* ---- limits ---------------------------------------------------------------- */
 #define MOE_MAX_EP          256     /* destination regions                     */
@@ -111,6 +114,10 @@ typedef struct moe_handle {
     int32_t num_tokens;          /* T of the last dispatch                     */
     int32_t runtime_max_tokens_per_rank; /* R of the last dispatch             */
     int32_t hip_error;           /* hipError_t behind the last MOE_ERR_HIP     */
+    /* single-pass dispatch (moe_init zeroes both)                         */
+    uint32_t onepass_epoch;      /* epoch of the last one (library use only)   */
+    int32_t  onepass_spin_limit; /* polls per word before a block gives up:   */
+                                 /* 0 the default, < 0 give up at once (tests) */
 } moe_handle;
 
 /* Bytes of the padded workspace [ep, cap, H] bf16: the receive buffer
@@ -182,8 +189,17 @@ int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
  * Copies past cap are dropped (slot_index -1) and set MOE_STATUS_OVERFLOW;
  * ids outside [-1, E) are dropped and set MOE_STATUS_EXPERT_ID; both are
  * reported by moe_sync_status.
- * Batches of at most 4096 routed copies (T * k) run as one kernel launch;
- * larger ones run the routing kernel, then the copy kernel.
+ * Batches of at most 4096 routed copies (T * k) run as one kernel launch.
+ * In the per-copy layout, batches of 4097 to 32768 copies also run as one
+ * launch whose first blocks rank the routing chunks into words tagged with
+ * the dispatch's epoch (the handle's onepass_epoch; the handle's first such
+ * dispatch, and the one after the epoch wraps, first clear the words with
+ * hipMemsetAsync), while the other blocks wait for the words they need.
+ * A block that waits too long (onepass_spin_limit polls of one word) gives
+ * up: it writes nothing for its token, whose slot_index entries read -1, and
+ * sets MOE_STATUS_GAVE_UP (moe_sync_status: MOE_ERR_GAVE_UP).  Under stream
+ * capture, and for larger batches, the other layout and the fp8 payload, the
+ * routing kernel runs first, then the copy kernel.
  * The workspace must not overlap x or topk_ids, and none of the three may
  * overlap the handle's device buffers (MOE_ERR_ARG).
  * Returns MOE_OK, MOE_ERR_ARG, MOE_ERR_PHASE (already dispatched) or

@@ -37,6 +37,21 @@ hipError_t launch_dispatch_copy(const DispatchArgs &a, hipStream_t) {
     ++launches;
     return hipSuccess;
 }
+static int onepass_launches = 0;
+hipError_t launch_dispatch_onepass(const DispatchArgs &a, const RouteArgs &ra, hipStream_t) {
+    // a mid-size bf16 per-copy batch whose words lie inside the scratch buffer
+    if (!a.onepass || a.fp8 || a.per_region || !dispatch_is_onepass(a.T, a.k, false)) std::abort();
+    if (a.epoch == 0 || a.spin_limit == 0 || ra.n_items != (int64_t)a.T * a.k) std::abort();
+    const char *lo = reinterpret_cast<const char *>(g_scratch);
+    const char *hi = lo + g_scratch_ints * 4;
+    const char *rw = reinterpret_cast<const char *>(a.rank_w), *hw = reinterpret_cast<const char *>(a.hist_w);
+    if (rw < lo || rw + (int64_t)a.T * a.k * 8 > hi || hw < lo || hw + (int64_t)a.n_chunks * a.ep * 8 > hi)
+        std::abort();
+    if (reinterpret_cast<uintptr_t>(rw) % 8 != 0 || hw < rw + (int64_t)a.T * a.k * 8) std::abort();
+    ++launches;
+    ++onepass_launches;
+    return hipSuccess;
+}
 hipError_t launch_combine(const CombineArgs &a, bool fused, hipStream_t) {
     if (a.T < 0 || a.k < 1 || (fused && (!a.residual || !a.gamma || !a.normed))) std::abort();
     // a partials reduction binds no handle: no slot_index, unweighted, every row p*T + t

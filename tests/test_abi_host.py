@@ -52,7 +52,7 @@ def test_handle_layout_and_constants_match_header(tmp_path):
             "int main(void){", 'printf("%zu\\n", sizeof(moe_handle));']
     prog += [f'printf("%zu\\n", offsetof(moe_handle, {f}));' for f in fields]
     consts = ["MOE_OK", "MOE_ERR_ARG", "MOE_ERR_PHASE", "MOE_ERR_OVERFLOW", "MOE_ERR_EXPERT_ID",
-              "MOE_ERR_HIP", "MOE_ERR_NOALLOC_SIZE", "MOE_NOALLOC_MAX_ITEMS", "MOE_STATUS_OVERFLOW", "MOE_STATUS_EXPERT_ID", "MOE_MAX_EP",
+              "MOE_ERR_HIP", "MOE_ERR_NOALLOC_SIZE", "MOE_ERR_GAVE_UP", "MOE_NOALLOC_MAX_ITEMS", "MOE_STATUS_OVERFLOW", "MOE_STATUS_EXPERT_ID", "MOE_STATUS_GAVE_UP", "MOE_MAX_EP",
               "MOE_MAX_TOP_K", "MOE_MAX_FUSED_HIDDEN", "MOE_MAX_HIDDEN", "MOE_MAX_TOKENS", "MOE_MAX_PARTIALS", "MOE_LAYOUT_PER_COPY",
               "MOE_LAYOUT_PER_REGION"]
     prog += [f'printf("%d\\n", (int){c});' for c in consts]
