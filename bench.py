@@ -699,7 +699,8 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-PROBE_KINDS = {"read": 0, "copy": 1, "write": 2, "rows": 3, "oneshot_write": 4, "oneshot_copy": 5}
+PROBE_KINDS = {"read": 0, "copy": 1, "write": 2, "rows": 3, "oneshot_write": 4, "oneshot_copy": 5,
+               "empty": 6}
 
 
 def _probe_library():
@@ -773,13 +774,40 @@ def ceilings(nbytes: int = 1 << 30, reps: int = 20) -> dict:
         out[name] = {"bytes": moved, "us_mean": round(ms * 1e3, 2), "gbs": round(gbs, 1),
                      "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1)}
         print(f"# {name:40s} {ms * 1e3:9.1f} us {gbs:8.1f} GB/s", file=sys.stderr, flush=True)
+    # the launch floor: a HIP graph of 100 launches of a kernel whose
+    # workgroups each store one word, replayed 20 times (the host's issue
+    # time stays out; the decode step's two kernels run near this floor)
+    floors = {}
+    for grid in (128, 512, 1024):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            gs = torch.cuda.current_stream(dev).cuda_stream
+            for _ in range(100):
+                rc = lib.moe_probe_stream(PROBE_KINDS["empty"], 0, ctypes.c_void_p(b.data_ptr()), None,
+                                          nbytes, grid, 0, 0, ctypes.c_void_p(gs))
+                if rc != 0:
+                    raise RuntimeError(f"moe_probe_stream(empty) returned {rc}")
+        graph.replay()
+        torch.cuda.synchronize(dev)
+        e0, e1 = hev.create(), hev.create()
+        hev.record(e0, sh)
+        for _ in range(20):
+            graph.replay()
+        hev.record(e1, sh)
+        torch.cuda.synchronize(dev)
+        floors[f"{grid} workgroups"] = round(hev.elapsed_ms(e0, e1) * 1e3 / 2000, 2)
+        hev.destroy(e0)
+        hev.destroy(e1)
+        del graph
+        print(f"# launch floor, {grid} workgroups: {floors[f'{grid} workgroups']:.2f} us per launch",
+              file=sys.stderr, flush=True)
     best = {}
     for name, rec in out.items():
         family = name.split(" grid=")[0].split(" vec/lane")[0].rsplit(" ", 1)[0] \
             if name.startswith("oneshot") else name.split(" grid=")[0]
         if family not in best or rec["gbs"] > best[family]["gbs"]:
             best[family] = {"variant": name, "gbs": rec["gbs"], "pct_of_peak": rec["pct_of_peak"]}
-    return {"ceilings": out, "best": best, "nbytes": nbytes, "reps": reps}
+    return {"ceilings": out, "best": best, "launch_floor_us": floors, "nbytes": nbytes, "reps": reps}
 
 
 def calibrate_copy(nbytes: int, reps: int) -> None:

@@ -26,6 +26,10 @@
 //                          lane i the vectors at i, i + 256, ...;
 //                          floor(bytes / (4096 * V)) workgroups (`grid` and
 //                          `row_bytes` unused).
+//   kind MOE_PROBE_EMPTY   `grid` workgroups of 256 lanes, each of whose lane 0
+//                          stores one 4-byte word to dst (dst needs grid * 4
+//                          bytes): the floor of a launch of that many
+//                          workgroups.
 //   nt != 0 marks the loads and stores non-temporal.
 //   bytes, row_bytes and both pointers must be multiples of 16; grid in
 //   [1, 1 << 20].  Returns 0, -1 for bad arguments (nothing launched), or the
@@ -136,6 +140,10 @@ void launch_oneshot(int v, unsigned blocks, u32x4 *d, const u32x4 *s, uint32_t v
     }
 }
 
+__global__ __launch_bounds__(kThreads) void probe_empty_kernel(uint32_t *dst) {
+    if (threadIdx.x == 0) dst[blockIdx.x] = blockIdx.x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -147,6 +155,7 @@ enum {
     MOE_PROBE_ROWS = 3,
     MOE_PROBE_ONESHOT_WRITE = 4,
     MOE_PROBE_ONESHOT_COPY = 5,
+    MOE_PROBE_EMPTY = 6,
 };
 
 int moe_probe_stream(int kind, int nt, void *dst, const void *src, int64_t bytes, int grid,
@@ -156,7 +165,8 @@ int moe_probe_stream(int kind, int nt, void *dst, const void *src, int64_t bytes
     const int64_t n = bytes / 16;
     const bool uses_src = kind == MOE_PROBE_READ || kind == MOE_PROBE_COPY || kind == MOE_PROBE_ONESHOT_COPY;
     if (uses_src && (src == nullptr || reinterpret_cast<uintptr_t>(src) % 16 != 0)) return -1;
-    const bool uses_grid = kind == MOE_PROBE_READ || kind == MOE_PROBE_COPY || kind == MOE_PROBE_WRITE;
+    const bool uses_grid = kind == MOE_PROBE_READ || kind == MOE_PROBE_COPY || kind == MOE_PROBE_WRITE ||
+                           kind == MOE_PROBE_EMPTY;
     if (uses_grid && (grid < 1 || grid > (1 << 20))) return -1;
     const uint32_t value = 0x3F803F80u;     // bf16 pairs of 1.0
     u32x4 *d = static_cast<u32x4 *>(dst);
@@ -215,6 +225,10 @@ int moe_probe_stream(int kind, int nt, void *dst, const void *src, int64_t bytes
         }
         break;
     }
+    case MOE_PROBE_EMPTY:
+        if ((int64_t)grid * 4 > bytes) return -1;
+        hipLaunchKernelGGL(probe_empty_kernel, dim3(grid), dim3(kThreads), 0, stream, static_cast<uint32_t *>(dst));
+        break;
     default:
         return -1;
     }

@@ -312,6 +312,8 @@ def test_stream_probe_library_rejects_bad_arguments_before_any_launch():
         (3, 0, dst, None, 1 << 20, 0, 100, 1),      # row not a multiple of 16
         (3, 0, dst, None, 1 << 20, 0, 16384, 0),    # no rows per workgroup
         (3, 0, dst, None, 1 << 13, 0, 16384, 1),    # not one whole row
+        (6, 0, dst, None, 1024, 512, 0, 0),         # empty launch: sink larger than dst
+        (6, 0, dst, None, 1 << 20, 0, 0, 0),        # empty launch: grid 0
         (7, 0, dst, src, 1 << 20, 1024, 0, 0),      # unknown kind
     ]
     for args in bad:
