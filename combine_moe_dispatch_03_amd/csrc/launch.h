@@ -48,7 +48,7 @@ inline int32_t *scratch_rank(void *scratch) { return static_cast<int32_t *>(scra
 inline int32_t *scratch_hist(void *scratch, int64_t max_items) {
     return static_cast<int32_t *>(scratch) + max_items;
 }
-constexpr int64_t kOnePassWordItems = 32768;     // rank words: the single pass's largest batch
+constexpr int64_t kOnePassWordItems = 65536;     // rank words: the single pass's largest batch
 inline int64_t scratch_words_offset(int64_t max_items, int ep) {
     return ((max_items + (int64_t)kMaxChunks * ep) * 4 + 7) / 8 * 8;
 }
@@ -128,6 +128,9 @@ struct CombineArgs {
 // per-copy layout dispatch in one launch that ranks the chunks in its first
 // blocks (dispatch_onepass_kernel).
 constexpr int64_t kOnePassItems = kOnePassWordItems;
+// Up to this many copies the single pass loads each source row before its
+// routing words, above it after them.
+constexpr int64_t kOnePassRowFirstItems = 32768;
 inline bool dispatch_is_onepass(int32_t num_tokens, int32_t top_k, bool per_region) {
     const int64_t items = (int64_t)num_tokens * top_k;
     return !per_region && items > kSmallItems && items <= kOnePassItems;

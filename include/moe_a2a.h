@@ -190,7 +190,7 @@ int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
  * ids outside [-1, E) are dropped and set MOE_STATUS_EXPERT_ID; both are
  * reported by moe_sync_status.
  * Batches of at most 4096 routed copies (T * k) run as one kernel launch.
- * In the per-copy layout, batches of 4097 to 32768 copies also run as one
+ * In the per-copy layout, batches of 4097 to 65536 copies also run as one
  * launch whose first blocks rank the routing chunks into words tagged with
  * the dispatch's epoch (the handle's onepass_epoch; the handle's first such
  * dispatch, and the one after the epoch wraps, first clear the words with

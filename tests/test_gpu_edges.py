@@ -81,7 +81,7 @@ ROUNDTRIP_CASES = [
     ("single_launch_short_ids", 256, 128, 8, 64, 8), # 2048 copies: one launch, 8 ids per lane
     ("single_launch_long_ids", 257, 128, 8, 64, 8),  # 2056 copies: one launch, 16 ids per lane
     ("single_launch_limit", 512, 128, 8, 64, 8),     # 4096 copies: the last one-launch size
-    ("two_kernel_threshold", 513, 128, 8, 64, 8),    # 4104 copies: routing kernel + copy
+    ("first_multi_block_size", 513, 128, 8, 64, 8),  # 4104 copies: the single pass
     ("single_launch_long_wide_rows", 300, 7168, 8, 256, 8),  # 2400 copies, whole-token blocks
     ("single_launch_short_wide_rows", 256, 7168, 8, 256, 8), # 2048 copies, blocks of 2 copies
     # the routing kernel loads its chunk's ids 4 tiles of 256 at a time:

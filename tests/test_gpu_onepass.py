@@ -1,11 +1,13 @@
-"""The single-pass dispatch (per-copy layout, bf16, 4097 to 32768 routed
+"""The single-pass dispatch (per-copy layout, bf16, 4097 to 65536 routed
 copies): its first blocks rank the routing chunks into words tagged with the
 dispatch's epoch, and the copy blocks wait for the words they need.
 
 * parity with the oracle (bit-exact counts, slot_index, src_index, rows and
   untouched padding) over shapes that take both forms of the chunk prefix
   (per region, and per copy when there are more regions than copies), a
-  region count that does not divide the block, invalid ids and overflow;
+  region count that does not divide the block, invalid ids and overflow,
+  with the source row loaded before the routing words (up to 32768 copies)
+  and after them (above);
 * a forced give-up (onepass_spin_limit < 0): every block gives up, the call
   reports MOE_ERR_GAVE_UP through moe_sync_status, every slot_index reads -1
   and no workspace row is written; the next dispatch on the handle is exact;
@@ -51,7 +53,11 @@ ONEPASS_CASES = [
     # (name, T, H, k, E, ep, cap or None = every copy fits)
     ("prefix_per_region", 1500, 256, 8, 64, 8, None),           # 12000 copies, ep <= k
     ("prefix_per_copy", 2048, 128, 8, 256, 16, None),           # 16384 copies, ep > k
-    ("largest_single_pass", 4096, 64, 8, 64, 8, None),          # 32768 copies
+    ("last_row_first_size", 4096, 64, 8, 64, 8, None),          # 32768 copies
+    ("first_row_after_size", 4097, 64, 8, 256, 16, None),       # 32776 copies, per-copy prefix
+    ("row_after_the_words", 6144, 128, 8, 256, 8, None),        # 49152 copies
+    ("largest_single_pass", 8192, 64, 8, 64, 8, None),          # 65536 copies
+    ("overflow_row_after", 5000, 64, 8, 64, 8, 4000),           # 40000 copies, cap below the mean
     ("regions_not_dividing_the_block", 5000, 64, 3, 24, 6, None),   # 15000 copies
     ("top12_ragged_chunks", 1100, 64, 12, 48, 8, None),         # 13200 copies
     ("first_single_pass_size", 513, 7168, 8, 256, 8, 1024),     # 4104 copies
@@ -66,7 +72,7 @@ def test_single_pass_matches_the_oracle(case):
     cap = cap or T * k
     h = moe.MoeA2A(T, H, k, E, ep, cap)
     rng = np.random.default_rng(11)
-    expect = moe.MOE_ERR_OVERFLOW if name == "overflow" else moe.MOE_OK
+    expect = moe.MOE_ERR_OVERFLOW if name.startswith("overflow") else moe.MOE_OK
     dispatch_and_check(h, rng, T, E, ep, cap, expect)
 
 
@@ -77,8 +83,9 @@ def test_single_pass_invalid_ids():
                        p_missing=0.05, p_bad=0.01)
 
 
-def test_forced_give_up_then_exact():
-    T, H, k, E, ep = 1024, 64, 8, 64, 8
+@pytest.mark.parametrize("T", [1024, 6000], ids=["row_first", "row_after"])
+def test_forced_give_up_then_exact(T):
+    H, k, E, ep = 64, 8, 64, 8
     h = moe.MoeA2A(T, H, k, E, ep, T * k)
     rng = np.random.default_rng(5)
     x = pins.random_bf16(rng, (T, H))
@@ -111,10 +118,11 @@ def test_epoch_wrap():
 
 def test_paths_in_turn_on_one_handle():
     H, k, E, ep = 64, 8, 64, 8
-    T_max = 4500
+    T_max = 8300
     h = moe.MoeA2A(T_max, H, k, E, ep, T_max * k)
     rng = np.random.default_rng(9)
-    # single pass, two kernels (more than 32768 copies), single launch (at most 4096)
-    for T in (1000, 4500, 300, 4096, 3000, 513, 512, 4097, 1500):
+    # single pass (row first up to 4096 tokens, row after above), two kernels
+    # (more than 65536 copies), single launch (at most 4096 copies)
+    for T in (1000, 8300, 300, 4500, 4096, 3000, 513, 512, 8192, 8193, 4097, 1500):
         say("paths", T)
         dispatch_and_check(h, rng, T, E, ep, T_max * k)
