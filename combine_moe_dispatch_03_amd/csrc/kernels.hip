@@ -361,8 +361,9 @@ __global__ __launch_bounds__(kThreads) void route_rank_kernel(RouteArgs a) {
 // `before` (copies of earlier tokens in region d) and its rank after them;
 // writes slot_index / src_index (when cb == 0) and, in copy_rows, the rows
 // this block must fill.  Under the per-region layout a copy whose region
-// already has a row for this token takes that row and fills nothing.  Ends
-// with a block barrier.
+// already has a row for this token takes that row and fills nothing.  One
+// block barrier: copy_rows is complete after it, and a later copy reads its
+// first copy's row from `rows` only after it.
 __device__ __forceinline__ void assign_rows(const DispatchArgs &a, int d, int tid, int cb,
                                             int64_t f, int before, int rank,
                                             const int32_t *dests, int32_t *rows,
@@ -371,8 +372,8 @@ __device__ __forceinline__ void assign_rows(const DispatchArgs &a, int d, int ti
     if (tid < a.k && d >= 0 && a.per_region)
         for (int j = 0; j < tid; ++j)
             if (dests[j] == d) { first = j; break; }
+    int row = -1;
     if (tid < a.k && first == tid) {
-        int row = -1;
         if (d >= 0) {
             const int s = before + rank;
             if (s < a.cap)
@@ -381,16 +382,11 @@ __device__ __forceinline__ void assign_rows(const DispatchArgs &a, int d, int ti
                 atomicOr(a.status, MOE_STATUS_OVERFLOW);
         }
         rows[tid] = row;
-        copy_rows[tid] = row;
         if (cb == 0 && row >= 0) a.src_index[row] = (int32_t)f;
     }
+    if (tid < a.k) copy_rows[tid] = first == tid ? row : -1;
     __syncthreads();
-    if (tid < a.k && first != tid) {
-        rows[tid] = rows[first];
-        copy_rows[tid] = -1;
-    }
-    if (tid < a.k && cb == 0) a.slot_index[f] = rows[tid];
-    __syncthreads();
+    if (tid < a.k && cb == 0) a.slot_index[f] = first == tid ? row : rows[first];
 }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
