@@ -973,7 +973,12 @@ __device__ __forceinline__ void gather_group(float (&acc)[VPT][8], const uint16_
 // Otherwise wave 0 first compacts the token's valid copies (slot_index >= 0) into LDS,
 // keeping j order, so only rows holding valid copies are ever read (padding
 // rows never are).  Under the per-region layout a row named by an earlier
-// copy of the token is dropped: each region's message is added once.  Rows
+// copy of the token is dropped: each region's message is added once.  Lane j
+// of wave 0 loads copy j's slot and gate together and compares rows with the
+// earlier lanes through shuffles, so the prologue is one round trip and one
+// block barrier (with a first barrier before the gates' loads, the decode
+// combine took 7.0 instead of 6.6 us after a cache-evicting read, the skewed
+// per-region one 86.9 instead of 86.4 us; others equal).  Rows
 // are then fetched JU at a time with every load of a group issued before the
 // first add, and no load under a branch (a branch around a load makes the
 // compiler wait for all outstanding loads).  Lanes
@@ -983,7 +988,6 @@ __device__ __forceinline__ void gather_group(float (&acc)[VPT][8], const uint16_
 // is read once).
 template <int VPT, int JU, bool WEIGHTED, bool FUSED, bool NT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
-    __shared__ int32_t all_rows[MOE_MAX_TOP_K];
     __shared__ int32_t rows[MOE_MAX_TOP_K];
     __shared__ float gates[MOE_MAX_TOP_K];
     __shared__ int32_t n_valid;
@@ -994,17 +998,19 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     const int cb = blockIdx.y;
     const int k = a.k;
 
-    if (tid < k) all_rows[tid] = a.partials ? tid * a.T + t : a.slot_index[(int64_t)t * k + tid];
-    __syncthreads();
-    if (tid < 64) {                             // wave 0: compact valid copies
+    if (tid < 64) {                             // wave 0 (k <= 64): compact valid copies
         int row = -1;
         float g = 0.0f;
-        if (tid < k) {
-            row = all_rows[tid];
+        if (tid < k) {                          // the copy's row and gate, in one round trip
+            row = a.partials ? tid * a.T + t : a.slot_index[(int64_t)t * k + tid];
             g = WEIGHTED ? a.w[(int64_t)t * k + tid] : 1.0f;
-            if (row >= 0 && a.per_region)       // a row already added for this token
-                for (int j = 0; j < tid; ++j)
-                    if (all_rows[j] == row) { row = -1; break; }
+        }
+        if (a.per_region) {                     // a row already added for this token
+            const int mine = row;
+            for (int j = 0; j + 1 < k; ++j) {
+                const int rj = __shfl(mine, j);
+                if (j < tid && mine >= 0 && rj == mine) row = -1;
+            }
         }
         const uint64_t valid = __ballot(row >= 0);
         if (row >= 0) {
