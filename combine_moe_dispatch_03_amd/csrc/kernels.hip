@@ -137,6 +137,14 @@ __device__ __forceinline__ void store_out16(__amdgpu_buffer_rsrc_t row, int64_t 
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Orders this wave's LDS accesses before the call against those after it
+// (between lanes of one wave; other waves are not waited for).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // base[r] += sum of hist[i] over i < n with i % ep == r (LDS, all threads).
 // When ep divides the block size every entry a thread visits belongs to the
 // same region, so the thread adds its entries in a register (loads in flight
@@ -842,11 +850,14 @@ __device__ __forceinline__ void accumulate(float (&acc)[VPT][8], const u32x4 (&r
 // copies of all earlier tokens itself: at most kSmallItems ids from L2,
 // loaded together with the source row, one LDS add per copy (under the
 // per-region layout one per ballot group of first copies, as in
-// route_rank_kernel).  A copy's rank among its own token's earlier copies to
-// the same region comes from the token's ids, so the slots follow the stable
-// order of the routed path.  Each token's first block flags the token's bad
-// ids; the last token's first block writes counts (the earlier tokens' copies
-// plus its own).
+// route_rank_kernel) into its wave's own row of counts, which the wave clears
+// itself, so one block barrier publishes the counts and the token's regions.
+// After it every wave sums the four rows for its copies' regions and adds
+// each copy's rank among its own token's earlier copies to the same region,
+// so the slots follow the stable order of the routed path.  Each token's
+// first block flags the token's bad ids and writes its index maps; the last
+// token's first block writes counts (the earlier tokens' copies plus its
+// own).
 // PER: earlier ids per lane, kSmallItemsShort / 256 or kSmallItems / 256 (the
 // smaller form keeps decode's register and load count down: 16 per lane made
 // the decode dispatch 6.3 -> 6.9 us).
@@ -855,14 +866,14 @@ static_assert(kSmallItems % kThreads == 0 && kSmallItemsShort % kThreads == 0,
 
 template <int VPT, int POLICY, bool FP8, int C, int PER>
 __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a) {
-    __shared__ int32_t cnt[MOE_MAX_EP];
+    __shared__ int32_t cnt[kWaves * MOE_MAX_EP];        // per wave: earlier copies per region
     __shared__ int32_t dests[MOE_MAX_TOP_K];
-    __shared__ int32_t rows[MOE_MAX_TOP_K];
-    __shared__ int32_t copy_rows[MOE_MAX_TOP_K];
+    __shared__ int32_t wave_rows[kWaves * MOE_MAX_TOP_K]; // per wave: the rows this block fills
     __shared__ float red[kWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int cb = blockIdx.y;
     const int ep = a.ep;
     const int n = (a.k + C - 1) / C;            // copy groups per token
@@ -894,7 +905,9 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
         off[q] = (int64_t)min(col[q], vpr - 1) * 8;
         v[q] = load16(src + off[q]);
     }
-    for (int r = tid; r < ep; r += kThreads) cnt[r] = 0;
+    int32_t *wave_cnt = cnt + wave * ep;        // this wave's counts: no other wave uses them
+    for (int r = lane; r < ep; r += 64) wave_cnt[r] = 0;
+    wave_sync();
     int d = -1;
     if (tid < a.k) {
         if (own_id >= 0 && own_id < a.n_experts)
@@ -903,7 +916,6 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
             atomicOr(a.status, MOE_STATUS_EXPERT_ID);
         dests[tid] = d;
     }
-    __syncthreads();
 
     // copies of the earlier tokens, per region
     if (a.per_region) {
@@ -916,34 +928,61 @@ __global__ __launch_bounds__(kThreads) void dispatch_small_kernel(DispatchArgs a
             int de = -1;
             if (i < mine && eid[p] >= 0 && eid[p] < a.n_experts) de = region_of(a, eid[p]);
             const uint64_t same = rank_group(a, de, i, i < mine, region_bits);
-            if (de >= 0 && (same >> lane) == 1ull) atomicAdd(&cnt[de], __popcll(same));
+            if (de >= 0 && (same >> lane) == 1ull) atomicAdd(&wave_cnt[de], __popcll(same));
         }
     } else {
 #pragma unroll
         for (int p = 0; p < PER; ++p)
-            if (eid[p] >= 0 && eid[p] < a.n_experts) atomicAdd(&cnt[region_of(a, eid[p])], 1);
+            if (eid[p] >= 0 && eid[p] < a.n_experts) atomicAdd(&wave_cnt[region_of(a, eid[p])], 1);
     }
-    // rank among the token's earlier copies to the same region (under the
-    // per-region layout a first copy's rank is 0 and the later ones share its
-    // row in assign_rows)
-    int rank = 0;
-    if (tid < a.k && d >= 0)
-        for (int j = 0; j < tid; ++j) rank += (dests[j] == d);
-    __syncthreads();
+    __syncthreads();                            // the only block barrier before the stores
 
+    // Row of copy j: its region's copies of earlier tokens (the four waves'
+    // counts) plus its rank among the token's earlier copies to that region.
+    // Under the per-region layout a token's copies to one region share the
+    // row of the first of them (rank 0), and only that one fills it.
+    auto row_of = [&](int j, bool &fills) -> int {
+        const int dj = dests[j];
+        fills = false;
+        if (dj < 0) return -1;
+        int rank = 0;
+        for (int i = 0; i < j; ++i) rank += (dests[i] == dj);
+        fills = !a.per_region || rank == 0;
+        if (a.per_region) rank = 0;
+        int s = rank;
+        for (int w = 0; w < kWaves; ++w) s += cnt[w * ep + dj];
+        return s < a.cap ? dj * a.cap + s : -1;
+    };
+    if (first_block && tid < a.k) {             // the token's index maps
+        bool fills;
+        const int row = row_of(tid, fills);
+        if (fills && d >= 0 && row < 0) atomicOr(a.status, MOE_STATUS_OVERFLOW);
+        a.slot_index[mine + tid] = row;
+        if (fills && row >= 0) a.src_index[row] = (int32_t)(mine + tid);
+    }
     if (first_block && t == a.T - 1) {          // totals: the earlier tokens' copies plus this one's
         for (int r = tid; r < ep; r += kThreads) {
             int own = 0;
             for (int j = 0; j < a.k; ++j) own += (dests[j] == r);
-            a.counts[r] = cnt[r] + (a.per_region ? (own > 0) : own);
+            int earlier = 0;
+            for (int w = 0; w < kWaves; ++w) earlier += cnt[w * ep + r];
+            a.counts[r] = earlier + (a.per_region ? (own > 0) : own);
         }
     }
-    assign_rows(a, d, tid, cb | grp, mine + tid, d < 0 ? 0 : cnt[d], rank, dests, rows, copy_rows);
+    // every wave finds the rows of this block's copies itself (no second
+    // block barrier)
     const int j0 = grp * C, j1 = min(a.k, j0 + C);
+    int32_t *rows_w = wave_rows + wave * MOE_MAX_TOP_K;
+    for (int j = j0 + lane; j < j1; j += 64) {
+        bool fills;
+        const int row = row_of(j, fills);
+        rows_w[j] = fills ? row : -1;
+    }
+    wave_sync();
     if constexpr (FP8)
-        store_rows_fp8<VPT, POLICY>(a, v, col, off, vpr, copy_rows, red, tid, j0, j1);
+        store_rows_fp8<VPT, POLICY>(a, v, col, off, vpr, rows_w, red, tid, j0, j1);
     else
-        store_rows_bf16<VPT, POLICY>(a, v, col, off, vpr, copy_rows, j0, j1);
+        store_rows_bf16<VPT, POLICY>(a, v, col, off, vpr, rows_w, j0, j1);
 }
 
 // G rows starting at compacted copy j0: all G x VPT loads, then the adds in
