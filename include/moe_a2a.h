@@ -126,9 +126,12 @@ typedef struct moe_handle {
 size_t moe_workspace_bytes(int32_t ep_size, int32_t max_tokens_per_rank, int32_t hidden);
 
 /* Bytes of routing scratch a handle needs (per-copy ranks and per-chunk
- * region histograms of the routing kernel); returns 0 for arguments outside
- * the limits.  Any contents are accepted: the routing kernel writes what the
- * copy kernel reads. */
+ * region histograms of the routing kernel, and the single-pass dispatch's
+ * epoch-tagged words: 8 bytes per routed copy up to 65536 copies and per
+ * chunk and region); returns 0 for arguments outside the limits.  Any
+ * contents are accepted: the routing kernel writes what the copy kernel
+ * reads, and a handle clears the words before its first single-pass
+ * dispatch. */
 size_t moe_scratch_bytes(int32_t max_tokens, int32_t top_k, int32_t ep_size);
 
 /*
@@ -368,9 +371,10 @@ int moe_route_counts(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens,
  * adapter" (ids outside the experts, a receive region past its capacity),
  * which a one-sided kernel cannot raise itself.
  *   bits  host, optional: receives the MOE_STATUS_* bits that were set
- * Returns MOE_ERR_EXPERT_ID or MOE_ERR_OVERFLOW if a kernel flagged one since
- * the last call (expert id first), MOE_OK otherwise, MOE_ERR_HIP on a
- * runtime failure.  The only call that synchronises.
+ * Returns MOE_ERR_EXPERT_ID, MOE_ERR_OVERFLOW or MOE_ERR_GAVE_UP if a kernel
+ * flagged one since the last call (in that order when several were; `bits`
+ * has them all), MOE_OK otherwise, MOE_ERR_HIP on a runtime failure.  The
+ * only call that synchronises.
  */
 int moe_sync_status(moe_handle *h, void *stream, int32_t *bits);
 
