@@ -8,7 +8,10 @@ overflow: reported, the copies past capacity dropped).  Dispatch must match
 bit for bit and the combine (weighted for the per-copy layout, the
 per-region rank-sum otherwise) bit for bit.  Twenty more cases run
 the fused residual + RMSNorm epilogue and twenty the FP8 payload (codes and
-scales bit-exact).
+scales bit-exact).  Twenty more draw 3000-9000 tokens with rows of at most
+128 elements, so that random shapes also reach the single pass with the row
+loaded after the routing words (32769-65536 per-copy copies) and the routing
+kernel + copy kernel above 65536.
 """
 import numpy as np
 import pytest
@@ -23,10 +26,10 @@ from gpu_harness import (assert_bf16_close, check_dispatch, expert_stage_gpu, ex
 pytestmark = pytest.mark.gpu
 
 
-def draw_case(seed):
+def draw_case(seed, t_range=(0, 700), h_steps=128):
     rng = np.random.default_rng(1000 + seed)
-    T = int(rng.integers(0, 701))
-    H = 8 * int(rng.integers(1, 129))
+    T = int(rng.integers(t_range[0], t_range[1] + 1))
+    H = 8 * int(rng.integers(1, h_steps + 1))
     k = int(rng.integers(1, 13))
     ep = int(rng.integers(1, 17))
     epr = int(rng.integers(1, 9))
@@ -42,9 +45,7 @@ def draw_case(seed):
     return dict(T=T, H=H, k=k, E=E, ep=ep, epr=epr, layout=layout, cap=cap, ids=ids, x=x, w=w, y=y)
 
 
-@pytest.mark.parametrize("seed", range(40))
-def test_random_shape_against_oracle(seed):
-    c = draw_case(seed)
+def dispatch_and_combine(c, seed):
     T, H, k, E, ep, epr, cap = c["T"], c["H"], c["k"], c["E"], c["ep"], c["epr"], c["cap"]
     say("random case", seed, {n: c[n] for n in ("T", "H", "k", "E", "ep", "layout", "cap")})
     orc = oracle.load()
@@ -66,6 +67,16 @@ def test_random_shape_against_oracle(seed):
         want = orc.combine(ref.ws, ref.slot_index, None, False, H, layout="region")
     assert_bf16_close(to_u16(got), want, f"random case {seed} combine")
     assert run.h.handle.phase == 0
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shape_against_oracle(seed):
+    dispatch_and_combine(draw_case(seed), seed)
+
+
+@pytest.mark.parametrize("seed", range(80, 100))
+def test_random_large_batch_against_oracle(seed):
+    dispatch_and_combine(draw_case(seed, t_range=(3000, 9000), h_steps=16), seed)
 
 
 @pytest.mark.parametrize("seed", range(40, 60))
