@@ -243,9 +243,16 @@ static moe::DispatchArgs dispatch_args(moe_handle *h, const Scratch &sc, const u
 }
 
 
+// True if `s` is being captured into a graph, and (conservatively) when the
+// query fails; a failed query's error is cleared so that the launch check
+// after the kernels does not report it as theirs.
 static bool capturing(hipStream_t s) {
     hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    return hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return st != hipStreamCaptureStatusNone;
 }
 
 static int dispatch_checks(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
