@@ -14,7 +14,8 @@ dispatch's epoch, and the copy blocks wait for the words they need.
 * the epoch wrapping: a dispatch at the last epoch and the one after it
   (which clears the words and starts again) are both exact;
 * single-pass, two-kernel and single-launch dispatches in turn on one
-  handle, each exact.
+  handle, each exact;
+* two handles dispatching and combining at once on two streams, each exact.
 """
 import numpy as np
 import pytest
@@ -23,7 +24,7 @@ import torch
 import combine_moe_dispatch_03_amd as moe
 import oracle
 import pins
-from gpu_harness import CANARY, GpuRun, check_dispatch, say, to_dev, to_dev_bf16
+from gpu_harness import CANARY, GpuRun, assert_bf16_close, check_dispatch, say, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -126,3 +127,44 @@ def test_paths_in_turn_on_one_handle():
     for T in (1000, 8300, 300, 4500, 4096, 3000, 513, 512, 8192, 8193, 4097, 1500):
         say("paths", T)
         dispatch_and_check(h, rng, T, E, ep, T_max * k)
+
+
+def test_two_handles_on_two_streams():
+    """Two handles, each on a stream of its own (default priority), dispatch
+    and combine at the same time, twice (epochs 1 and 2): each handle's words
+    are its own, and within each launch the routing blocks come first, so
+    both results are exact."""
+    H, k, E, ep = 64, 8, 64, 8
+    rng = np.random.default_rng(21)
+    orc = oracle.load()
+    cases = []
+    for T in (3000, 5000):                      # 24000 (row first) and 40000 (row after) copies
+        x = pins.random_bf16(rng, (T, H))
+        ids = routing(rng, T, k, E)
+        w = rng.random((T, k)).astype(np.float32)
+        h = moe.MoeA2A(T, H, k, E, ep, T * k)
+        ref = orc.dispatch(x, ids, ep, E // ep, T * k, layout="copy")
+        want = orc.combine(ref.ws, ref.slot_index, w, True, H)
+        cases.append(dict(T=T, x=x, ids=ids, h=h, ref=ref, want=want, xd=to_dev_bf16(x),
+                          idd=to_dev(ids), wd=to_dev(w), stream=torch.cuda.Stream(),
+                          out=torch.empty((T, H), dtype=torch.bfloat16, device="cuda")))
+    for rep in range(2):
+        say("two streams", rep)
+        for c in cases:
+            c["ws"] = c["h"].new_workspace(CANARY)
+            c["h"].src_index.fill_(-1)
+        torch.cuda.synchronize()
+        for c in cases:
+            moe.moe_dispatch(c["h"], c["xd"], c["idd"], c["T"], c["ws"], stream=c["stream"])
+        for c in cases:
+            c["stream"].synchronize()
+            code, bits = moe.moe_sync_status(c["h"], c["stream"])
+            assert code == moe.MOE_OK, (c["T"], code, bits)
+            assert c["h"].handle.onepass_epoch == rep + 1
+            check_dispatch(GpuRun(c["h"], c["ws"], None, None, code, bits), c["ref"], c["x"], k)
+        for c in cases:
+            moe.moe_combine(c["h"], c["ws"], c["wd"], True, out=c["out"], stream=c["stream"])
+        for c in cases:
+            c["stream"].synchronize()
+            got = c["out"].view(torch.int16).cpu().numpy().view(np.uint16)
+            assert_bf16_close(got, c["want"], f"two streams, T = {c['T']}")
