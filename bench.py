@@ -774,19 +774,18 @@ def ceilings(nbytes: int = 1 << 30, reps: int = 20) -> dict:
         out[name] = {"bytes": moved, "us_mean": round(ms * 1e3, 2), "gbs": round(gbs, 1),
                      "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1)}
         print(f"# {name:40s} {ms * 1e3:9.1f} us {gbs:8.1f} GB/s", file=sys.stderr, flush=True)
-    # the launch floor: a HIP graph of 100 launches of a kernel whose
-    # workgroups each store one word, replayed 20 times (the host's issue
-    # time stays out; the decode step's two kernels run near this floor)
-    floors = {}
-    for grid in (128, 512, 1024):
+    def graph_us(kind, nt, grid, rpb, nb):
+        """Microseconds per launch of a probe kernel, from a HIP graph of 100
+        launches replayed 20 times (the host's issue time stays out)."""
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             gs = torch.cuda.current_stream(dev).cuda_stream
             for _ in range(100):
-                rc = lib.moe_probe_stream(PROBE_KINDS["empty"], 0, ctypes.c_void_p(b.data_ptr()), None,
-                                          nbytes, grid, 0, 0, ctypes.c_void_p(gs))
+                rc = lib.moe_probe_stream(PROBE_KINDS[kind], nt, ctypes.c_void_p(b.data_ptr()),
+                                          ctypes.c_void_p(a.data_ptr()), nb, grid, 0, rpb,
+                                          ctypes.c_void_p(gs))
                 if rc != 0:
-                    raise RuntimeError(f"moe_probe_stream(empty) returned {rc}")
+                    raise RuntimeError(f"moe_probe_stream({kind}) returned {rc}")
         graph.replay()
         torch.cuda.synchronize(dev)
         e0, e1 = hev.create(), hev.create()
@@ -795,11 +794,26 @@ def ceilings(nbytes: int = 1 << 30, reps: int = 20) -> dict:
             graph.replay()
         hev.record(e1, sh)
         torch.cuda.synchronize(dev)
-        floors[f"{grid} workgroups"] = round(hev.elapsed_ms(e0, e1) * 1e3 / 2000, 2)
+        us = hev.elapsed_ms(e0, e1) * 1e3 / 2000
         hev.destroy(e0)
         hev.destroy(e1)
         del graph
+        return round(us, 2)
+
+    # the launch floor: launches of a kernel whose workgroups each store one
+    # word (the decode step's two kernels run near this floor)
+    floors = {}
+    for grid in (128, 512, 1024):
+        floors[f"{grid} workgroups"] = graph_us("empty", 0, grid, 0, nbytes)
         print(f"# launch floor, {grid} workgroups: {floors[f'{grid} workgroups']:.2f} us per launch",
+              file=sys.stderr, flush=True)
+    # the decode dispatch's bytes written alone: the 14.7 MB of rows of 128
+    # tokens x top-8 x 7168 written by a one-store-per-lane kernel (no loads),
+    # the floor under a dispatch that must first load its rows
+    decode_bytes = 128 * 8 * 7168 * 2
+    decode_write = {f"{v} vec/lane": graph_us("oneshot_write", 1, 0, v, decode_bytes) for v in (1, 2)}
+    for name, us in decode_write.items():
+        print(f"# decode-size write ({decode_bytes} B, non-temporal), {name}: {us:.2f} us per launch",
               file=sys.stderr, flush=True)
     best = {}
     for name, rec in out.items():
@@ -807,7 +821,8 @@ def ceilings(nbytes: int = 1 << 30, reps: int = 20) -> dict:
             if name.startswith("oneshot") else name.split(" grid=")[0]
         if family not in best or rec["gbs"] > best[family]["gbs"]:
             best[family] = {"variant": name, "gbs": rec["gbs"], "pct_of_peak": rec["pct_of_peak"]}
-    return {"ceilings": out, "best": best, "launch_floor_us": floors, "nbytes": nbytes, "reps": reps}
+    return {"ceilings": out, "best": best, "launch_floor_us": floors,
+            "decode_size_write_us": {"bytes": decode_bytes, **decode_write}, "nbytes": nbytes, "reps": reps}
 
 
 def calibrate_copy(nbytes: int, reps: int) -> None:
