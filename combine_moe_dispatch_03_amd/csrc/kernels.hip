@@ -1,7 +1,7 @@
 // gfx950 kernels of the MoE dispatch / combine path.
 //
 // Nothing here is a dense contraction, so nothing uses MFMA: the path is
-// bound by HBM bandwidth.  Four kernels:
+// bound by HBM bandwidth.  Five kernels:
 //
 //  route_rank_kernel     per chunk of tokens: each routed copy's rank among
 //                        the chunk's copies to the same region (a stable
@@ -16,6 +16,10 @@
 //  dispatch_small_kernel the whole dispatch in one launch for small batches
 //                        (decode): each block counts the earlier copies
 //                        itself instead of reading route_rank_kernel's output.
+//  dispatch_onepass_kernel routing and copy in one launch for mid-size
+//                        batches (per-copy layout, bf16): its first blocks do
+//                        route_rank_kernel's work and publish it as
+//                        epoch-tagged words, which the copy blocks wait for.
 //  combine_kernel        per token (x column block): gathers the k rows
 //                        (routed copies, or the partials of an all-reduce),
 //                        accumulates in fp32 in j order, narrows once to
