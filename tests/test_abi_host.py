@@ -318,3 +318,18 @@ def test_stream_probe_library_rejects_bad_arguments_before_any_launch():
     ]
     for args in bad:
         assert probe(*args, None) == -1, args
+
+
+def test_scratch_holds_the_single_pass_words(lib):
+    """The scratch a handle needs: ranks (int32 per routed copy) and chunk
+    histograms (int32 per chunk and region, 64 chunks), then, 8-byte aligned,
+    the single-pass dispatch's 64-bit words: one per routed copy up to its
+    largest batch of 65536 copies, and one per chunk and region; rounded up to
+    256 bytes."""
+    def expected(items, ep):
+        offset = ((items + 64 * ep) * 4 + 7) // 8 * 8
+        words = min(items, 65536) + 64 * ep
+        return (offset + words * 8 + 255) // 256 * 256
+
+    for T, k, ep in ((4096, 8, 8), (8192, 8, 16), (8193, 8, 8), (100000, 2, 4), (7, 3, 5), (1, 1, 1)):
+        assert lib.moe_scratch_bytes(T, k, ep) == expected(T * k, ep), (T, k, ep)
