@@ -145,10 +145,10 @@ class HipEvents:
 def dispatch_kernels(items: int, layout: str, payload: str) -> str:
     """The kernels one dispatch call launches for `items` routed copies
     (the library's size thresholds: single launch up to 4096 copies; the
-    single-pass kernel for the per-copy bf16 layout up to 65536)."""
+    single-pass kernel for the per-copy layout, either payload, up to 65536)."""
     if items <= 4096:
         return "dispatch_small_kernel"
-    if layout == "copy" and payload == "bf16" and items <= 65536:
+    if layout == "copy" and items <= 65536:
         return "dispatch_onepass_kernel (routing blocks + copy blocks, one launch)"
     return "route_rank_kernel + dispatch_copy_kernel"
 

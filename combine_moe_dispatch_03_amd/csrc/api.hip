@@ -298,7 +298,7 @@ static int dispatch_launch(moe_handle *h, const Scratch &sc, moe::DispatchArgs d
                            const int32_t *topk_ids, int32_t num_tokens, int32_t R, hipStream_t s,
                            bool words = false) {
     moe::RoutePlan plan = moe::plan_route(num_tokens);
-    if (words && !da.fp8 && moe::dispatch_is_onepass(num_tokens, h->top_k, da.per_region) &&
+    if (words && moe::dispatch_is_onepass(num_tokens, h->top_k, da.per_region) &&
         !capturing(s)) {
         uint64_t *rw = moe::scratch_rank_words(sc.base, sc.max_items, h->ep_size);
         // The handle's words are cleared on its first single-pass dispatch
@@ -392,7 +392,7 @@ int moe_dispatch_fp8(moe_handle *h, const uint16_t *x, const int32_t *topk_ids,
     da.fp8 = 1;
     da.ws8 = workspace;
     da.scales = scales;
-    return dispatch_launch(h, sc, da, topk_ids, num_tokens, R, static_cast<hipStream_t>(stream));
+    return dispatch_launch(h, sc, da, topk_ids, num_tokens, R, static_cast<hipStream_t>(stream), true);
 }
 
 int moe_route_counts(moe_handle *h, const int32_t *topk_ids, int32_t num_tokens, void *stream) {

@@ -194,15 +194,15 @@ int moe_init(moe_handle *h, int32_t max_tokens, int32_t hidden, int32_t top_k,
  * reported by moe_sync_status.
  * Batches of at most 4096 routed copies (T * k) run as one kernel launch.
  * In the per-copy layout, batches of 4097 to 65536 copies also run as one
- * launch whose first blocks rank the routing chunks into words tagged with
+ * launch (bf16 and fp8 payloads alike) whose first blocks rank the routing chunks into words tagged with
  * the dispatch's epoch (the handle's onepass_epoch; the handle's first such
  * dispatch, and the one after the epoch wraps, first clear the words with
  * hipMemsetAsync), while the other blocks wait for the words they need.
  * A block that waits too long (onepass_spin_limit polls of one word) gives
  * up: it writes nothing for its token, whose slot_index entries read -1, and
  * sets MOE_STATUS_GAVE_UP (moe_sync_status: MOE_ERR_GAVE_UP).  Under stream
- * capture, and for larger batches, the other layout and the fp8 payload, the
- * routing kernel runs first, then the copy kernel.
+ * capture, and for larger batches and the other layout, the routing kernel
+ * runs first, then the copy kernel.
  * The workspace must not overlap x or topk_ids, and none of the three may
  * overlap the handle's device buffers (MOE_ERR_ARG).
  * Returns MOE_OK, MOE_ERR_ARG, MOE_ERR_PHASE (already dispatched) or
@@ -249,7 +249,10 @@ int moe_dispatch_noalloc(moe_handle *h, const uint16_t *x, const int32_t *topk_i
  *   scales     device [ep, cap] fp32, 4-byte aligned; scales[r*cap + s] is
  *              the scale of row (r, s), written for valid rows only
  * Other arguments, outputs (counts, slot_index, src_index), errors and the
- * phase as moe_dispatch; requires H <= MOE_MAX_FUSED_HIDDEN; workspace,
+ * phase as moe_dispatch, with the same launch choices (one launch up to
+ * 4096 copies; the single pass, with its epoch words and give-up, for 4097
+ * to 65536 per-copy copies outside capture; routing then copy kernels
+ * otherwise); requires H <= MOE_MAX_FUSED_HIDDEN; workspace,
  * scales, x and topk_ids must not overlap each other (x and topk_ids
  * excepted) or the handle's device buffers (MOE_ERR_ARG).  The combine
  * that follows reads bf16 expert outputs from a buffer of the same

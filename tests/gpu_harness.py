@@ -125,3 +125,41 @@ def expert_stage_gpu_by_row(run: GpuRun, rows_by_copy: np.ndarray) -> None:
         n = min(int(counts[r]), h.cap)
         if n:
             flat[r * h.cap: r * h.cap + n] = yd[src[r, :n].long()]
+
+
+FP8_FILL = 0x7F            # e4m3 NaN: marks workspace bytes that must stay untouched
+
+
+def fp8_check(x, ids, E, ep, cap, R=None, layout="copy", epoch=None):
+    """Dispatch x with the FP8 payload on a fresh handle and compare codes,
+    scales, counts, slot_index and src_index with the oracle bit for bit;
+    rows past a region's count keep their NaN fill.  `epoch`, when given, is
+    the single-pass epoch the handle must hold afterwards (1 after one
+    single-pass dispatch, 0 when the call took another path)."""
+    orc = oracle.load()
+    T, H = x.shape
+    k = ids.shape[1]
+    ref, ref_scales = orc.dispatch_fp8(x, ids, ep, E // ep, cap, layout=layout)
+    h = moe.MoeA2A(R or max(T, 1), H, k, E, ep, cap, layout=layout)
+    ws = h.new_workspace_fp8(FP8_FILL)
+    scales = h.new_scales()
+    moe.moe_dispatch_fp8(h, to_dev_bf16(x), to_dev(ids), R or max(T, 1), ws, scales)
+    code, bits = moe.moe_sync_status(h)
+    assert bits == ref.status, (bits, ref.status)
+    assert np.array_equal(h.counts.cpu().numpy(), ref.counts)
+    assert np.array_equal(h.slot_index_view().cpu().numpy(), ref.slot_index)
+    src = h.src_index_view().cpu().numpy()
+    sc = scales.cpu().numpy()
+    for r in range(ep):
+        n = min(int(ref.counts[r]), cap)
+        assert np.array_equal(src[r, :n], ref.src_index[r, :n])
+        got = ws[r, :n].cpu().numpy()
+        bad = np.argwhere(got != ref.ws[r, :n])
+        assert bad.size == 0, (r, bad[:3], got[tuple(bad[0])], ref.ws[r, :n][tuple(bad[0])])
+        assert np.array_equal(sc[r, :n].view(np.uint32), ref_scales[r, :n].view(np.uint32))
+        if n < cap:
+            assert bool((ws[r, n:] == FP8_FILL).all()) and np.isnan(sc[r, n:]).all()
+    assert h.handle.phase == 1
+    if epoch is not None:
+        assert h.handle.onepass_epoch == epoch, h.handle.onepass_epoch
+    return ref

@@ -39,8 +39,9 @@ hipError_t launch_dispatch_copy(const DispatchArgs &a, hipStream_t) {
 }
 static int onepass_launches = 0;
 hipError_t launch_dispatch_onepass(const DispatchArgs &a, const RouteArgs &ra, hipStream_t) {
-    // a mid-size bf16 per-copy batch whose words lie inside the scratch buffer
-    if (!a.onepass || a.fp8 || a.per_region || !dispatch_is_onepass(a.T, a.k, false)) std::abort();
+    // a mid-size per-copy batch whose words lie inside the scratch buffer
+    if (!a.onepass || a.per_region || !dispatch_is_onepass(a.T, a.k, false)) std::abort();
+    if (a.fp8 && (!a.ws8 || !a.scales)) std::abort();
     if (a.epoch == 0 || a.spin_limit == 0 || ra.n_items != (int64_t)a.T * a.k) std::abort();
     const char *lo = reinterpret_cast<const char *>(g_scratch);
     const char *hi = lo + g_scratch_ints * 4;
@@ -236,6 +237,9 @@ int main() {
                                                nullptr) == MOE_ERR_HIP);
     CHECK(moe_last_hip_error() == (int)hipErrorInvalidValue);
     moe::fail_partials = 0;
-    std::printf("sanitized ABI driver: ok (%d launches, sync_status rc %d)\n", moe::launches, rc);
+    // with no device the capture query fails, which the library reads as
+    // capture: every routed dispatch here takes the two-kernel path
+    std::printf("sanitized ABI driver: ok (%d launches, %d single-pass, sync_status rc %d)\n",
+                moe::launches, moe::onepass_launches, rc);
     return 0;
 }

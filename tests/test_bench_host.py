@@ -86,12 +86,14 @@ def test_unknown_workload_exits_with_a_message():
 
 def test_dispatch_kernels_follow_the_library_thresholds():
     """The roofline's kernel label names the path the library takes: one
-    launch up to 4096 copies, the single-pass kernel for the per-copy bf16
-    layout up to 65536, the routing + copy kernels otherwise."""
+    launch up to 4096 copies, the single-pass kernel for the per-copy layout
+    (bf16 or fp8) up to 65536, the routing + copy kernels otherwise."""
     assert bench.dispatch_kernels(1024, "copy", "bf16") == "dispatch_small_kernel"
     assert bench.dispatch_kernels(4096, "region", "fp8") == "dispatch_small_kernel"
     assert bench.dispatch_kernels(32768, "copy", "bf16").startswith("dispatch_onepass_kernel")
     assert bench.dispatch_kernels(65536, "copy", "bf16").startswith("dispatch_onepass_kernel")
     assert bench.dispatch_kernels(65544, "copy", "bf16") == "route_rank_kernel + dispatch_copy_kernel"
     assert bench.dispatch_kernels(32768, "region", "bf16") == "route_rank_kernel + dispatch_copy_kernel"
-    assert bench.dispatch_kernels(16384, "copy", "fp8") == "route_rank_kernel + dispatch_copy_kernel"
+    assert bench.dispatch_kernels(16384, "copy", "fp8").startswith("dispatch_onepass_kernel")
+    assert bench.dispatch_kernels(65544, "copy", "fp8") == "route_rank_kernel + dispatch_copy_kernel"
+    assert bench.dispatch_kernels(16384, "region", "fp8") == "route_rank_kernel + dispatch_copy_kernel"

@@ -3,51 +3,19 @@
 Codes, per-row scales, counts, slot_index and src_index must match the
 oracle bit for bit (the quantisation is fp32 arithmetic plus a
 nearest-even conversion on both sides); padding bytes and scales keep their
-NaN fill.  Full prefill / decode / skewed shapes, both layouts and both
-dispatch paths, plus rows that exercise zero, subnormal and saturating codes.
+NaN fill.  Full prefill / decode / skewed shapes, both layouts and every
+dispatch path (single launch, single pass, routing then copy), plus rows
+that exercise zero, subnormal and saturating codes.
 """
 import numpy as np
 import pytest
-import torch
 
-import combine_moe_dispatch_03_amd as moe
 import oracle
 import pins
 import synth
-from gpu_harness import say, to_dev, to_dev_bf16
+from gpu_harness import fp8_check, say
 
 pytestmark = pytest.mark.gpu
-
-FILL = 0x7F            # e4m3 NaN: marks workspace bytes that must stay untouched
-
-
-def fp8_check(x, ids, E, ep, cap, R=None, layout="copy"):
-    orc = oracle.load()
-    T, H = x.shape
-    k = ids.shape[1]
-    ref, ref_scales = orc.dispatch_fp8(x, ids, ep, E // ep, cap, layout=layout)
-    h = moe.MoeA2A(R or max(T, 1), H, k, E, ep, cap, layout=layout)
-    ws = h.new_workspace_fp8(FILL)
-    scales = h.new_scales()
-    moe.moe_dispatch_fp8(h, to_dev_bf16(x), to_dev(ids), R or max(T, 1), ws, scales)
-    code, bits = moe.moe_sync_status(h)
-    assert bits == ref.status, (bits, ref.status)
-    assert np.array_equal(h.counts.cpu().numpy(), ref.counts)
-    assert np.array_equal(h.slot_index_view().cpu().numpy(), ref.slot_index)
-    src = h.src_index_view().cpu().numpy()
-    sc = scales.cpu().numpy()
-    for r in range(ep):
-        n = min(int(ref.counts[r]), cap)
-        assert np.array_equal(src[r, :n], ref.src_index[r, :n])
-        got = ws[r, :n].cpu().numpy()
-        bad = np.argwhere(got != ref.ws[r, :n])
-        assert bad.size == 0, (r, bad[:3], got[tuple(bad[0])], ref.ws[r, :n][tuple(bad[0])])
-        assert np.array_equal(sc[r, :n].view(np.uint32), ref_scales[r, :n].view(np.uint32))
-        if n < cap:
-            assert bool((ws[r, n:] == FILL).all()) and np.isnan(sc[r, n:]).all()
-    assert h.handle.phase == 1
-    return ref
-
 
 @pytest.mark.parametrize("name,layout", [("prefill", "copy"), ("decode", "copy"),
                                          ("skewed", "copy"), ("prefill", "region"),
@@ -92,12 +60,14 @@ def test_fp8_ragged_and_two_kernel_shapes(T, H):
 
 
 @pytest.mark.parametrize("k", [8, 6, 3])
-def test_fp8_split_blocks(k):
+@pytest.mark.parametrize("many", [False, True], ids=["single_launch", "routed"])
+def test_fp8_split_blocks(k, many):
     # rows of 8 KB and more: the fp8 copy runs four copies per block (two
     # blocks a token at top-8 and top-6, the second partial for top-6; one
-    # partial block at top-3); enough tokens for the two-kernel path
+    # partial block at top-3); 2100 to 2400 copies take the single launch,
+    # 6000 and more the single pass (per copy) or the two kernels (per region)
     H, E, ep = 4096, 64, 8
-    T = max(300, 2100 // k)
+    T = 6000 // k + 1 if many else max(300, 2100 // k)
     say("fp8 split blocks", T, H, k)
     rng = np.random.default_rng(100 + k)
     x = pins.random_bf16(rng, (T, H))

@@ -21,7 +21,8 @@ import oracle
 import pins
 import synth
 from gpu_harness import (assert_bf16_close, check_dispatch, expert_stage_gpu, expert_stage_gpu_by_row,
-                         expert_stage_oracle, gpu_dispatch, say, to_dev, to_dev_bf16, to_u16)
+                         expert_stage_oracle, fp8_check, gpu_dispatch, say, to_dev, to_dev_bf16,
+                         to_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -103,7 +104,6 @@ def test_random_shape_fused_epilogue(seed):
 
 @pytest.mark.parametrize("seed", range(60, 80))
 def test_random_shape_fp8_dispatch(seed):
-    from test_gpu_fp8 import fp8_check
     c = draw_case(seed)
     say("random fp8 case", seed, {n: c[n] for n in ("T", "H", "k", "E", "ep", "layout", "cap")})
     fp8_check(c["x"], c["ids"], c["E"], c["ep"], c["cap"], R=max(c["T"], 1), layout=c["layout"])
