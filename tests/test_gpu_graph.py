@@ -12,7 +12,7 @@ import torch
 
 import combine_moe_dispatch_03_amd as moe
 import synth
-from gpu_harness import say, to_dev, to_dev_bf16, to_u16
+from gpu_harness import FP8_FILL, say, to_dev, to_dev_bf16, to_u16
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +73,56 @@ def test_graph_replays_match_eager(name, layout, fused):
             got.append(to_u16(res_out))
         for a, b in zip(got, want):
             assert np.array_equal(a, b), f"replay {rep} differs"
+    assert moe.moe_sync_status(h) == (moe.MOE_OK, 0)
+
+
+def test_fp8_graph_replays_match_eager():
+    """The fp8 dispatch at 16,384 copies: eagerly the single pass, captured
+    the routing kernel + copy kernel (a captured epoch would be stale on
+    replay).  Every replay's codes, scales (padding fill included) and index
+    maps equal the eager call's bit for bit."""
+    wl = synth.BY_NAME["fused"]
+    say("graph", "fp8", wl.T * wl.k, "copies")
+    inp = synth.make_inputs(wl, 1)
+    x, ids = to_dev_bf16(inp.x), to_dev(inp.ids)
+    h = moe.MoeA2A(wl.R, wl.H, wl.k, wl.E, wl.ep, wl.cap)
+    ws = h.new_workspace_fp8(FP8_FILL)
+    scales = h.new_scales()
+
+    def step():
+        moe.moe_dispatch_fp8(h, x, ids, wl.R, ws, scales)
+        moe.moe_reset(h)
+
+    def snapshot():                                   # on the GPU: the workspace is 940 MB
+        return [ws.clone(), scales.view(torch.int32).clone(), h.counts.clone(),
+                h.slot_index_view().clone(), h.src_index.clone()]
+
+    step()                                            # eager: the single pass
+    torch.cuda.synchronize()
+    assert moe.moe_sync_status(h) == (moe.MOE_OK, 0)
+    assert h.handle.onepass_epoch == 1
+    want = snapshot()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                        # warm the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    assert h.handle.onepass_epoch == 2                # the capture took no epoch
+
+    for rep in range(4):
+        ws.fill_(FP8_FILL)                            # eager work between replays
+        scales.fill_(float("nan"))
+        h.slot_index.fill_(-7)
+        h.src_index.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(snapshot(), want)):
+            assert torch.equal(a, b), f"replay {rep} differs in output {i}"
     assert moe.moe_sync_status(h) == (moe.MOE_OK, 0)
 
 

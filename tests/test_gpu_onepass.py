@@ -18,7 +18,7 @@ they need.
 * the epoch wrapping: a dispatch at the last epoch and the one after it
   (which clears the words and starts again) are both exact;
 * single-pass, two-kernel and single-launch dispatches in turn on one
-  handle, each exact;
+  handle, each exact, for either payload;
 * two handles dispatching and combining at once on two streams, each exact.
 """
 import numpy as np
@@ -189,6 +189,42 @@ def test_paths_in_turn_on_one_handle():
     for T in (1000, 8300, 300, 4500, 4096, 3000, 513, 512, 8192, 8193, 4097, 1500):
         say("paths", T)
         dispatch_and_check(h, rng, T, E, ep, T_max * k)
+
+
+def test_fp8_paths_in_turn_on_one_handle():
+    """fp8 dispatches on one handle through the single pass, the two kernels
+    and the single launch in turn: codes, scales and index maps bit-exact
+    each time, the epoch advancing on single-pass calls only."""
+    H, k, E, ep = 64, 8, 64, 8
+    T_max = 8300
+    cap = T_max * k
+    h = moe.MoeA2A(T_max, H, k, E, ep, cap)
+    rng = np.random.default_rng(23)
+    orc = oracle.load()
+    epoch = 0
+    for T in (1000, 8300, 300, 4097, 512, 8193, 6000):
+        say("fp8 paths", T)
+        x = pins.random_bf16(rng, (T, H))
+        ids = routing(rng, T, k, E, p_missing=0.02)
+        ws = h.new_workspace_fp8(FP8_FILL)
+        scales = h.new_scales()
+        moe.moe_dispatch_fp8(h, to_dev_bf16(x), to_dev(ids), T, ws, scales)
+        code, bits = moe.moe_sync_status(h)
+        assert code == moe.MOE_OK, (T, code, bits)
+        epoch += 4096 < T * k <= 65536
+        assert h.handle.onepass_epoch == epoch, (T, h.handle.onepass_epoch)
+        ref, ref_scales = orc.dispatch_fp8(x, ids, ep, E // ep, cap, layout="copy")
+        counts = h.counts.cpu().numpy()
+        assert np.array_equal(counts, ref.counts)
+        assert np.array_equal(h.slot_index_view().cpu().numpy(), ref.slot_index)
+        got, sc, src = ws.cpu().numpy(), scales.cpu().numpy(), h.src_index_view().cpu().numpy()
+        for r in range(ep):
+            n = int(counts[r])
+            assert np.array_equal(src[r, :n], ref.src_index[r, :n])
+            assert np.array_equal(got[r, :n], ref.ws[r, :n])
+            assert np.array_equal(sc[r, :n].view(np.uint32), ref_scales[r, :n].view(np.uint32))
+            assert bool((got[r, n:] == FP8_FILL).all()) and np.isnan(sc[r, n:]).all()
+        moe.moe_reset(h)
 
 
 def test_two_handles_on_two_streams():
