@@ -17,7 +17,7 @@
 //                        (decode): each block counts the earlier copies
 //                        itself instead of reading route_rank_kernel's output.
 //  dispatch_onepass_kernel routing and copy in one launch for mid-size
-//                        batches (per-copy layout, bf16): its first blocks do
+//                        batches (per-copy layout, bf16 or fp8): its first blocks do
 //                        route_rank_kernel's work and publish it as
 //                        epoch-tagged words, which the copy blocks wait for.
 //  combine_kernel        per token (x column block): gathers the k rows
