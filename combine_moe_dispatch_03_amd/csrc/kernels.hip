@@ -686,10 +686,12 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
 // lanes read their rank and histogram words, each polled until it carries
 // the epoch (a block of an early chunk needs only the chunks before its
 // own), and it loads its source row before those reads (ROW_FIRST) or after
-// them.  Measured: up to 32768 copies the row first is faster (4096 tokens,
-// hidden 7168, top-8: 86.4 us against 89.2); above that the row after the
-// words, which leaves HBM to the routing blocks' id reads while the first
-// copy blocks wait (8192 tokens, 65536 copies: step 333 us against 341).
+// them.  Measured: for 28673 to 32768 copies the row first is faster (4096
+// tokens, hidden 7168, top-8: dispatch 86.4 us against 89.2, step 167.5
+// against 169.4); elsewhere the row after the words, which leaves HBM to the
+// routing blocks' id reads while the first copy blocks wait (8192 tokens,
+// 65536 copies: step 333 us against 341; 2048 to 3072 tokens: steps level
+// or faster, the dispatch after a cache-evicting read 2 to 4 us faster).
 // A block that has polled a word spin_limit times without the epoch gives
 // up: it sets MOE_STATUS_GAVE_UP, its token's index maps read -1 and it
 // writes no row, so every block ends.  Copy block 0, column block 0 also
@@ -1319,15 +1321,20 @@ namespace {
 template <int VPT, int C>
 void launch_onepass_c(const DispatchArgs &a, const RouteArgs &ra, dim3 grid, hipStream_t s) {
     if (!a.per_region) {
-        const int64_t written = (int64_t)a.T * a.k * a.H * (int64_t)sizeof(uint16_t);
-        if ((int64_t)a.T * a.k > kOnePassRowFirstItems)
+        const int64_t items = (int64_t)a.T * a.k;
+        const int64_t written = items * a.H * (int64_t)sizeof(uint16_t);
+        const bool row_first = items > kOnePassRowFirstFrom && items <= kOnePassRowFirstItems;
+        if (items > kOnePassRowFirstItems || (written > kCopyWriteThroughBytes && !row_first))
             hipLaunchKernelGGL((dispatch_onepass_kernel<VPT, kCopyPolicy, C, false, false>), grid, dim3(kThreads), 0,
                                s, a, ra);
         else if (written > kCopyWriteThroughBytes)
             hipLaunchKernelGGL((dispatch_onepass_kernel<VPT, kCopyPolicy, C, true, false>), grid, dim3(kThreads), 0,
                                s, a, ra);
-        else
+        else if (row_first)
             hipLaunchKernelGGL((dispatch_onepass_kernel<VPT, kPolicyNT, C, true, false>), grid, dim3(kThreads), 0, s,
+                               a, ra);
+        else
+            hipLaunchKernelGGL((dispatch_onepass_kernel<VPT, kPolicyNT, C, false, false>), grid, dim3(kThreads), 0, s,
                                a, ra);
         return;
     }

@@ -128,8 +128,10 @@ struct CombineArgs {
 // per-copy layout dispatch in one launch that ranks the chunks in its first
 // blocks (dispatch_onepass_kernel).
 constexpr int64_t kOnePassItems = kOnePassWordItems;
-// Up to this many copies the single pass loads each source row before its
-// routing words, above it after them.
+// The single pass loads each source row before its routing words for
+// batches of more than kOnePassRowFirstFrom and at most kOnePassRowFirstItems
+// copies, after them otherwise.
+constexpr int64_t kOnePassRowFirstFrom = 28672;
 constexpr int64_t kOnePassRowFirstItems = 32768;
 inline bool dispatch_is_onepass(int32_t num_tokens, int32_t top_k, bool per_region) {
     const int64_t items = (int64_t)num_tokens * top_k;

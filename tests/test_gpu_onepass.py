@@ -7,8 +7,8 @@ they need.
   untouched padding) over shapes that take both forms of the chunk prefix
   (per region, and per copy when there are more regions than copies), a
   region count that does not divide the block, invalid ids and overflow,
-  with the source row loaded before the routing words (up to 32768 copies)
-  and after them (above);
+  with the source row loaded before the routing words (28673 to 32768
+  copies) and after them (below and above);
 * the fp8 payload on the same kernel: codes, scales and index maps bit-exact
   against the oracle over row-after sizes up to the largest, wide rows split
   over blocks, ragged top-k and overflow;
@@ -59,6 +59,8 @@ ONEPASS_CASES = [
     # (name, T, H, k, E, ep, cap or None = every copy fits)
     ("prefix_per_region", 1500, 256, 8, 64, 8, None),           # 12000 copies, ep <= k
     ("prefix_per_copy", 2048, 128, 8, 256, 16, None),           # 16384 copies, ep > k
+    ("last_row_after_below", 3584, 128, 8, 64, 8, None),        # 28672 copies, row after
+    ("first_row_first_size", 3585, 64, 8, 256, 16, None),       # 28680 copies, row first
     ("last_row_first_size", 4096, 64, 8, 64, 8, None),          # 32768 copies
     ("first_row_after_size", 4097, 64, 8, 256, 16, None),       # 32776 copies, per-copy prefix
     ("row_after_the_words", 6144, 128, 8, 256, 8, None),        # 49152 copies
