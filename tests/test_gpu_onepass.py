@@ -70,6 +70,8 @@ ONEPASS_CASES = [
     ("top12_ragged_chunks", 1100, 64, 12, 48, 8, None),         # 13200 copies
     ("first_single_pass_size", 513, 7168, 8, 256, 8, 1024),     # 4104 copies
     ("overflow", 1024, 64, 8, 64, 8, 700),                      # cap below the busiest region
+    ("largest_hidden", 600, 16384, 8, 64, 8, 1024),             # 4800 copies, rows of 32 KB
+    ("ragged_hidden", 3000, 1000, 8, 64, 8, None),              # 24000 copies, 125 vectors a row
 ]
 
 
@@ -92,6 +94,8 @@ FP8_CASES = [
     ("fp8_wide_rows", 600, 7168, 8, 256, 8, 1024),              # 4800 copies, rows split over blocks
     ("fp8_top6_ragged", 1100, 2048, 6, 48, 8, None),            # 6600 copies
     ("fp8_overflow", 5000, 64, 8, 64, 8, 4000),                 # 40000 copies, cap below the mean
+    ("fp8_ragged_hidden", 700, 1000, 8, 64, 8, None),           # 5600 copies, 125 vectors a row
+    ("fp8_largest_hidden", 600, 16384, 8, 64, 8, 1024),         # 4800 copies, 8 vectors a lane
 ]
 
 
