@@ -690,8 +690,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_copy_kernel(DispatchArgs a)
 // tokens, hidden 7168, top-8: dispatch 86.4 us against 89.2, step 167.5
 // against 169.4); elsewhere the row after the words, which leaves HBM to the
 // routing blocks' id reads while the first copy blocks wait (8192 tokens,
-// 65536 copies: step 333 us against 341; 2048 to 3072 tokens: steps level
-// or faster, the dispatch after a cache-evicting read 2 to 4 us faster).
+// 65536 copies: step 333 us against 341; 1536 to 3584 tokens: steps 0.5 to
+// 1.5 us faster, the dispatch after a cache-evicting read 2 to 4 us faster).
 // A block that has polled a word spin_limit times without the epoch gives
 // up: it sets MOE_STATUS_GAVE_UP, its token's index maps read -1 and it
 // writes no row, so every block ends.  Copy block 0, column block 0 also
