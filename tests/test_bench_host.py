@@ -97,3 +97,28 @@ def test_dispatch_kernels_follow_the_library_thresholds():
     assert bench.dispatch_kernels(16384, "copy", "fp8").startswith("dispatch_onepass_kernel")
     assert bench.dispatch_kernels(65544, "copy", "fp8") == "route_rank_kernel + dispatch_copy_kernel"
     assert bench.dispatch_kernels(16384, "region", "fp8") == "route_rank_kernel + dispatch_copy_kernel"
+
+
+def _launch_constant(name):
+    import re
+    src = open(os.path.join(ROOT, "combine_moe_dispatch_03_amd", "csrc", "launch.h")).read()
+    m = re.search(r"constexpr\s+\w+\s+" + name + r"\s*=\s*(\w+);", src)
+    assert m, name
+    v = m.group(1)
+    return int(v) if v.isdigit() else _launch_constant(v)
+
+
+def test_dispatch_kernels_match_the_library_constants():
+    """The thresholds bench.py names kernels by are the library's own
+    (launch.h), read from the source so that the two cannot drift apart."""
+    small, onepass = _launch_constant("kSmallItems"), _launch_constant("kOnePassItems")
+    assert bench.dispatch_kernels(small, "copy", "bf16") == "dispatch_small_kernel"
+    assert bench.dispatch_kernels(small + 1, "copy", "bf16").startswith("dispatch_onepass_kernel")
+    assert bench.dispatch_kernels(small + 1, "copy", "fp8").startswith("dispatch_onepass_kernel")
+    assert bench.dispatch_kernels(onepass, "copy", "bf16").startswith("dispatch_onepass_kernel")
+    assert bench.dispatch_kernels(onepass + 1, "copy", "bf16") == "route_rank_kernel + dispatch_copy_kernel"
+    assert bench.dispatch_kernels(small + 1, "region", "bf16") == "route_rank_kernel + dispatch_copy_kernel"
+    # the single pass's row-first window lies inside its range
+    lo, hi = _launch_constant("kOnePassRowFirstFrom"), _launch_constant("kOnePassRowFirstItems")
+    assert small < lo < hi <= onepass
+
