@@ -107,3 +107,11 @@ def test_random_shape_fp8_dispatch(seed):
     c = draw_case(seed)
     say("random fp8 case", seed, {n: c[n] for n in ("T", "H", "k", "E", "ep", "layout", "cap")})
     fp8_check(c["x"], c["ids"], c["E"], c["ep"], c["cap"], R=max(c["T"], 1), layout=c["layout"])
+
+
+@pytest.mark.parametrize("seed", range(100, 110))
+def test_random_large_fp8_dispatch(seed):
+    # 3,000-9,000 tokens: the fp8 single pass, or the two kernels, by size and layout
+    c = draw_case(seed, t_range=(3000, 9000), h_steps=16)
+    say("random large fp8 case", seed, {n: c[n] for n in ("T", "H", "k", "E", "ep", "layout", "cap")})
+    fp8_check(c["x"], c["ids"], c["E"], c["ep"], c["cap"], R=max(c["T"], 1), layout=c["layout"])
