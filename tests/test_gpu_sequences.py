@@ -6,7 +6,8 @@
   a combine or by moe_reset: nothing a call leaves in the handle's scratch or
   index buffers leaks into the next (bit-exact every time);
 * top-k from 1 to 64 with one to 256 regions and ragged routing chunks, on
-  both paths;
+  every dispatch path (single launch up to 4096 copies; above, the single
+  pass in the per-copy layout and the two kernels in the per-region one);
 * graph replays with new routing written into the captured ids buffer
   between replays: every replay recomputes the routing from the ids.
 """
@@ -57,11 +58,11 @@ def test_consecutive_dispatches_of_varying_size():
 
 CHUNK_CASES = [
     # (name, T, H, k, E, ep); the routing kernel's chunks hold ceil(T / 64) tokens
-    ("top1_routed", 3000, 24, 1, 8, 4),
-    ("top3_routed_ragged_chunks", 1413, 40, 3, 24, 6),
-    ("top6_single_launch", 301, 16, 6, 36, 6),
-    ("top33_routed", 77, 16, 33, 66, 11),
-    ("top64_256_regions", 100, 16, 64, 512, 256),
+    ("top1_routed", 5000, 24, 1, 8, 4),                 # 5000 copies
+    ("top3_routed_ragged_chunks", 1413, 40, 3, 24, 6),  # 4239 copies
+    ("top6_single_launch", 301, 16, 6, 36, 6),          # 1806 copies
+    ("top33_routed", 150, 16, 33, 66, 11),              # 4950 copies
+    ("top64_256_regions", 100, 16, 64, 512, 256),       # 6400 copies
     ("one_region", 300, 16, 8, 8, 1),
     ("ragged_tail_one_token", 64 * 5 + 1, 16, 8, 64, 8),
 ]
@@ -84,6 +85,10 @@ def test_chunk_shapes(case, layout):
     assert code == moe.MOE_OK and bits == 0
     ref = orc.dispatch(x, ids, ep, E // ep, cap, layout=layout)
     check_dispatch(GpuRun(h, ws, None, None, code, bits), ref, x, k)
+    if "routed" in name:                        # past the single-launch limit
+        assert T * k > 4096
+    single_pass = layout == "copy" and 4096 < T * k <= 65536
+    assert h.handle.onepass_epoch == int(single_pass)
 
 
 def test_graph_replays_with_new_routing():
