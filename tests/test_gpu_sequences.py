@@ -7,7 +7,8 @@
   index buffers leaks into the next (bit-exact every time);
 * top-k from 1 to 64 with one to 256 regions and ragged routing chunks, on
   every dispatch path (single launch up to 4096 copies; above, the single
-  pass in the per-copy layout and the two kernels in the per-region one);
+  pass in the per-copy layout, the two kernels in the per-region one and,
+  through moe_dispatch_noalloc, in the per-copy one);
 * graph replays with new routing written into the captured ids buffer
   between replays: every replay recomputes the routing from the ids.
 """
@@ -89,6 +90,28 @@ def test_chunk_shapes(case, layout):
         assert T * k > 4096
     single_pass = layout == "copy" and 4096 < T * k <= 65536
     assert h.handle.onepass_epoch == int(single_pass)
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
+def test_chunk_shapes_two_kernels(case):
+    """The same shapes in the per-copy layout through moe_dispatch_noalloc,
+    which always runs the routing kernel then the copy kernel above 4096
+    copies (the single pass needs a handle's own words)."""
+    name, T, H, k, E, ep = case
+    say("chunk shape, two kernels", name, T, H, k, E, ep)
+    orc = oracle.load()
+    rng = np.random.default_rng(zlib.crc32(name.encode()) + 1)
+    x = pins.random_bf16(rng, (T, H))
+    ids = routing(rng, T, k, E, 0.1)
+    cap = T * k
+    h = moe.MoeA2A(T, H, k, E, ep, cap, scratch=False)
+    ws = h.new_workspace(CANARY)
+    moe.moe_dispatch_noalloc(h, to_dev_bf16(x), to_dev(ids), T, ws)
+    code, bits = moe.moe_sync_status(h)
+    assert code == moe.MOE_OK and bits == 0
+    ref = orc.dispatch(x, ids, ep, E // ep, cap, layout="copy")
+    check_dispatch(GpuRun(h, ws, None, None, code, bits), ref, x, k)
+    assert h.handle.onepass_epoch == 0
 
 
 def test_graph_replays_with_new_routing():
