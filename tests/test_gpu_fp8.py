@@ -50,7 +50,9 @@ def test_fp8_rows_with_zero_subnormal_and_extreme_values():
 
 
 @pytest.mark.parametrize("T,H", [(37, 136), (5, 16384), (2500, 64)])
-def test_fp8_ragged_and_two_kernel_shapes(T, H):
+def test_fp8_ragged_and_larger_shapes(T, H):
+    # 7500 copies at T = 2500: the single pass (per copy) and the two kernels
+    # (per region); the others one launch
     say("fp8 shapes", T, H)
     rng = np.random.default_rng(T + H)
     x = pins.random_bf16(rng, (T, H))

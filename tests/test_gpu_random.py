@@ -1,7 +1,7 @@
 """Seeded random shapes through the HIP path, each compared with the oracle.
 
-Forty cases drawn from a fixed seed: 0-700 tokens (both the single-launch
-and the routed dispatch), hidden sizes from 8 to 1024 in steps of 8, top-1 to
+Forty cases drawn from a fixed seed: 0-700 tokens (the single-launch
+dispatch, the single pass and the two kernels), hidden sizes from 8 to 1024 in steps of 8, top-1 to
 top-12, 1 to 16 regions of 1 to 8 experts, both layouts, unrouted copies and
 repeated experts, and now and then a capacity too small for the routing (an
 overflow: reported, the copies past capacity dropped).  Dispatch must match
