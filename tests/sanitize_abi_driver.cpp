@@ -3,9 +3,13 @@
 // UndefinedBehaviorSanitizer by test_sanitizers.py.  The kernel launchers are
 // replaced by stubs that check the argument blocks against the caller's
 // buffers and count launches, so no GPU is needed; moe_sync_status runs into
-// the HIP runtime and must either succeed or report MOE_ERR_HIP.
+// the HIP runtime and must either succeed or report MOE_ERR_HIP.  The stream
+// capture query and the memset are stand-ins defined here (the executable's
+// own definitions come before the runtime's), so that the single-pass branch
+// (its epochs and the clearing of its words) runs on the host as well.
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <vector>
 
 #include "launch.h"
@@ -16,6 +20,25 @@ static int64_t g_scratch_ints = 0;
 
 static bool in_scratch(const int32_t *p, int64_t n) {
     return p >= g_scratch && n >= 0 && (p - g_scratch) + n <= g_scratch_ints;
+}
+
+// -1: the capture query fails (as it does with no device: the library then
+// takes the capture-safe path), 0: the stream is not capturing, 1: it is.
+static int g_capture = -1;
+static int g_memsets = 0;                     // memsets that landed in the scratch buffer
+extern "C" hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus *st) {
+    if (g_capture < 0) return hipErrorNoDevice;
+    *st = g_capture ? hipStreamCaptureStatusActive : hipStreamCaptureStatusNone;
+    return hipSuccess;
+}
+extern "C" hipError_t hipMemsetAsync(void *dst, int value, size_t bytes, hipStream_t) {
+    // the only device memory the dispatch clears is the single pass's words,
+    // inside the scratch buffer (host memory here)
+    const int32_t *p = static_cast<const int32_t *>(dst);
+    if (bytes % 4 != 0 || !in_scratch(p, (int64_t)(bytes / 4))) std::abort();
+    std::memset(dst, value, bytes);
+    ++g_memsets;
+    return hipSuccess;
 }
 
 namespace moe {
@@ -124,6 +147,46 @@ int main() {
     const int rc = moe_sync_status(&h, nullptr, &bits);
     CHECK(rc == MOE_ERR_HIP || rc == MOE_OK);
     CHECK(rc != MOE_ERR_HIP || h.hip_error != 0);
+
+    // the single pass: a mid-size per-copy batch on a stream that is not
+    // capturing; the handle's first single-pass dispatch clears the words,
+    // later ones only take the next epoch, the one after the last epoch
+    // clears them again; under capture, and for the per-region layout, the
+    // routing kernel and the copy kernel instead
+    {
+        g_capture = 0;
+        moe_handle p;
+        CHECK(moe_init(&p, T, H, k, E, ep, T, MOE_LAYOUT_PER_COPY, counts.data(), src.data(),
+                       slot.data(), status.data(), scratch.data(), sb) == MOE_OK);
+        const int m0 = g_memsets, o0 = moe::onepass_launches;
+        LAUNCHES(moe_dispatch(&p, x, ids, T, T, ws, nullptr), 1);
+        CHECK(p.onepass_epoch == 1 && g_memsets == m0 + 1 && moe::onepass_launches == o0 + 1);
+        CHECK(moe_dispatch(&p, x, ids, T, T, ws, nullptr) == MOE_ERR_PHASE && p.onepass_epoch == 1);
+        LAUNCHES(moe_combine(&p, ws, nullptr, 0, out, nullptr), 1);
+        LAUNCHES(moe_dispatch_fp8(&p, x, ids, T, T, ws8, scales, nullptr), 1);
+        CHECK(p.onepass_epoch == 2 && g_memsets == m0 + 1 && moe::onepass_launches == o0 + 2);
+        CHECK(moe_reset(&p) == MOE_OK);
+        LAUNCHES(moe_dispatch(&p, x, ids, 512, 512, ws, nullptr), 1);   // 4096 copies: single launch
+        CHECK(p.onepass_epoch == 2 && moe::onepass_launches == o0 + 2);
+        CHECK(moe_reset(&p) == MOE_OK);
+        p.onepass_epoch = 0x7FFFFFFF;
+        LAUNCHES(moe_dispatch(&p, x, ids, 513, 600, ws, nullptr), 1);   // after the last epoch
+        CHECK(p.onepass_epoch == 1 && g_memsets == m0 + 2);
+        CHECK(moe_reset(&p) == MOE_OK);
+        g_capture = 1;
+        LAUNCHES(moe_dispatch(&p, x, ids, T, T, ws, nullptr), 2);
+        CHECK(moe_reset(&p) == MOE_OK);
+        LAUNCHES(moe_dispatch_fp8(&p, x, ids, T, T, ws8, scales, nullptr), 2);
+        CHECK(moe_reset(&p) == MOE_OK);
+        CHECK(p.onepass_epoch == 1 && g_memsets == m0 + 2 && moe::onepass_launches == o0 + 3);
+        g_capture = 0;
+        moe_handle q;
+        CHECK(moe_init(&q, T, H, k, E, ep, T, MOE_LAYOUT_PER_REGION, counts.data(), src.data(),
+                       slot.data(), status.data(), scratch.data(), sb) == MOE_OK);
+        LAUNCHES(moe_dispatch(&q, x, ids, T, T, ws, nullptr), 2);
+        CHECK(q.onepass_epoch == 0 && moe::onepass_launches == o0 + 3);
+        g_capture = -1;
+    }
 
     // per-region layout rejects a weighted combine
     moe_handle g;
@@ -237,8 +300,8 @@ int main() {
                                                nullptr) == MOE_ERR_HIP);
     CHECK(moe_last_hip_error() == (int)hipErrorInvalidValue);
     moe::fail_partials = 0;
-    // with no device the capture query fails, which the library reads as
-    // capture: every routed dispatch here takes the two-kernel path
+    // outside the block above the capture query fails, which the library
+    // reads as capture: those routed dispatches take the two-kernel path
     std::printf("sanitized ABI driver: ok (%d launches, %d single-pass, sync_status rc %d)\n",
                 moe::launches, moe::onepass_launches, rc);
     return 0;

@@ -5,7 +5,9 @@
   bad ids, the limits, both layouts, every e4m3 code, special values);
 * the host side of the C ABI (api.hip) built with host-only sanitizers
   against stub kernel launchers, driven through its argument checks, phase
-  machine and HIP-error path.
+  machine, HIP-error path and the single-pass branch (epochs, the clearing
+  of its words, the fallback under capture), with the capture query and the
+  memset stood in for by the driver.
 GPU code is never built with a sanitizer here.
 """
 import os
