@@ -1219,6 +1219,7 @@ constexpr int64_t kCopyWriteThroughBytes = int64_t(128) << 20;
 // lanes).
 constexpr int kCopiesPerBlock = 2;
 constexpr int kCopiesPerBlockFp8 = 4;
+constexpr int64_t kOnePassFp8WholeTokenItems = 8192;
 // Smaller rows (under 8 KB of bf16) keep one block per token: after a cache-
 // evicting read, T = 4096, H = 2048, top-8 copies ran at 48.8 % of the HBM
 // peak split in pairs against 60.8 % whole (T = 32768: 54.9 % against 68.7 %;
@@ -1353,8 +1354,13 @@ void launch_onepass_vpt(const DispatchArgs &a, const RouteArgs &ra, dim3 grid, h
 
 // The fp8 payload: whole rows in a block (one column block), copies per
 // block as in the copy kernel (every copy of a token under kSplitMinHidden,
-// four above), the row loaded after the routing words, and non-temporal
-// stores.  Measured against the routing kernel + copy kernel (dispatch us
+// four above) except that batches of at most kOnePassFp8WholeTokenItems
+// copies keep a whole token per block (H = 7168, top-8, step / dispatch
+// after a cache-evicting read, us, three runs each: 640 tokens 25.7 / 14.8
+// -> 25.3 / 13.7; 1024 tokens 39.0 / 21.4 -> 38.5 / 18.4; at 2048 tokens
+// four per block stay ahead, 78.5 / 32.9 against 79.8 / 34.1; the bf16
+// payload lost at 640-1024 tokens), the row loaded after the routing words,
+// and non-temporal stores.  Measured against the routing kernel + copy kernel (dispatch us
 // warm / cold, two runs each): 4096 tokens, H = 7168, top-8
 // 49.5 / 57.75 -> 48.5 / 57.7; 2048 tokens 30.05 / 33.45 -> 28.8 / 33.2;
 // skewed 8192 tokens 92.1 / 109.4 -> 90.25 / 110.05; 1024 tokens
@@ -1373,7 +1379,8 @@ hipError_t launch_dispatch_onepass(const DispatchArgs &args, const RouteArgs &ra
     DispatchArgs a = args;
     a.t_base = 0;
     if (a.fp8) {
-        const int c = a.H < kSplitMinHidden ? MOE_MAX_TOP_K : kCopiesPerBlockFp8;
+        const bool whole = a.H < kSplitMinHidden || (int64_t)a.T * a.k <= kOnePassFp8WholeTokenItems;
+        const int c = whole ? MOE_MAX_TOP_K : kCopiesPerBlockFp8;
         const int n = (a.k + c - 1) / c;
         const int64_t t_pad = ((int64_t)a.T + 7) / 8 * 8;
         a.route_blocks = (a.n_chunks + 7) / 8 * 8;   // keeps the copy blocks' XCD grouping

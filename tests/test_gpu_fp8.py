@@ -67,9 +67,10 @@ def test_fp8_split_blocks(k, many):
     # rows of 8 KB and more: the fp8 copy runs four copies per block (two
     # blocks a token at top-8 and top-6, the second partial for top-6; one
     # partial block at top-3); 2100 to 2400 copies take the single launch,
-    # 6000 and more the single pass (per copy) or the two kernels (per region)
+    # 9000 and more the single pass (per copy; four copies a block above
+    # 8192 copies) or the two kernels (per region)
     H, E, ep = 4096, 64, 8
-    T = 6000 // k + 1 if many else max(300, 2100 // k)
+    T = 9000 // k + 1 if many else max(300, 2100 // k)
     say("fp8 split blocks", T, H, k)
     rng = np.random.default_rng(100 + k)
     x = pins.random_bf16(rng, (T, H))

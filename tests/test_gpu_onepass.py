@@ -91,7 +91,10 @@ FP8_CASES = [
     ("fp8_prefix_per_region", 1500, 256, 8, 64, 8, None),       # 12000 copies
     ("fp8_prefix_per_copy", 2048, 128, 8, 256, 16, None),       # 16384 copies, ep > k
     ("fp8_largest_single_pass", 8192, 64, 8, 64, 8, None),      # 65536 copies
-    ("fp8_wide_rows", 600, 7168, 8, 256, 8, 1024),              # 4800 copies, rows split over blocks
+    ("fp8_wide_rows", 600, 7168, 8, 256, 8, 1024),              # 4800 copies, a whole token a block
+    ("fp8_last_whole_token_size", 1024, 4096, 8, 64, 8, None),  # 8192 copies
+    ("fp8_first_split_size", 1025, 4096, 8, 64, 8, None),       # 8200 copies, four a block
+    ("fp8_split_top6", 1500, 7168, 6, 48, 8, None),             # 9000 copies, blocks of 4 + 2
     ("fp8_top6_ragged", 1100, 2048, 6, 48, 8, None),            # 6600 copies
     ("fp8_overflow", 5000, 64, 8, 64, 8, 4000),                 # 40000 copies, cap below the mean
     ("fp8_ragged_hidden", 700, 1000, 8, 64, 8, None),           # 5600 copies, 125 vectors a row
