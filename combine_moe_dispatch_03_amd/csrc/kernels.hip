@@ -1220,6 +1220,7 @@ constexpr int64_t kCopyWriteThroughBytes = int64_t(128) << 20;
 constexpr int kCopiesPerBlock = 2;
 constexpr int kCopiesPerBlockFp8 = 4;
 constexpr int64_t kOnePassFp8WholeTokenItems = 8192;
+constexpr int64_t kRegionWholeTokenItems = 8192;
 // Smaller rows (under 8 KB of bf16) keep one block per token: after a cache-
 // evicting read, T = 4096, H = 2048, top-8 copies ran at 48.8 % of the HBM
 // peak split in pairs against 60.8 % whole (T = 32768: 54.9 % against 68.7 %;
@@ -1429,9 +1430,16 @@ hipError_t launch_dispatch_copy(const DispatchArgs &args, hipStream_t s) {
     // T = 512 roundtrip 25.9 -> 25.0 us, T = 384 step 20.6 -> 19.7 us, other
     // sizes unchanged; 4 copies per block measured the same at T = 512 but
     // 0.8 us slower at T = 448.
-    const bool small_long = dispatch_is_small(a.T, a.k) && (int64_t)a.T * a.k > kSmallItemsShort;
-    const int c = (a.H < kSplitMinHidden || small_long) ? MOE_MAX_TOP_K
-                                                        : a.fp8 ? kCopiesPerBlockFp8 : kCopiesPerBlock;
+    // The routed copy of the per-region layout takes a whole token per block
+    // up to kRegionWholeTokenItems copies (H = 7168, top-8, step / dispatch
+    // after a cache-evicting read, us, three runs each: 640 tokens
+    // 25.4 / 19.1 -> 25.2 / 17.1; 1024 tokens 37.5 / 24.6 -> 37.1 / 22.8;
+    // fp8 1024 tokens 31.2 / 17.8 -> 30.9 / 17.4, 640 tokens level).
+    const int64_t items = (int64_t)a.T * a.k;
+    const bool small_long = dispatch_is_small(a.T, a.k) && items > kSmallItemsShort;
+    const bool region_whole = a.per_region && !dispatch_is_small(a.T, a.k) && items <= kRegionWholeTokenItems;
+    const int c = (a.H < kSplitMinHidden || small_long || region_whole) ? MOE_MAX_TOP_K
+                  : a.fp8 ? kCopiesPerBlockFp8 : kCopiesPerBlock;
     const int n = (a.k + c - 1) / c;
     const int64_t t_pad = ((int64_t)a.T + 7) / 8 * 8;
     const int vpt = a.fp8 ? full_row_vpt(a.H) : streaming_vpt(t_pad * n, a.H);

@@ -80,6 +80,19 @@ def test_fp8_split_blocks(k, many):
     fp8_check(x, ids, E, ep, T, layout="region")
 
 
+@pytest.mark.parametrize("T", [1024, 1025])
+def test_fp8_block_sizes_around_8192_copies(T):
+    # up to 8192 copies a whole token per block (the single pass per copy,
+    # the routed copy per region), four copies per block above
+    H, k, E, ep = 4096, 8, 64, 8
+    say("fp8 block sizes", T)
+    rng = np.random.default_rng(300 + T)
+    x = pins.random_bf16(rng, (T, H))
+    ids = rng.integers(-1, E, size=(T, k)).astype(np.int32)
+    fp8_check(x, ids, E, ep, T * k, epoch=1)
+    fp8_check(x, ids, E, ep, T, layout="region", epoch=0)
+
+
 def test_fp8_bad_ids_and_overflow():
     say("fp8 bad ids / overflow")
     rng = np.random.default_rng(9)

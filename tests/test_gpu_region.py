@@ -74,13 +74,15 @@ REGION_EDGE_CASES = [
     ("top1", 33, 256, 1, 16, 8, 0.1),
     ("wide_rows", 5, 16384, 8, 32, 4, 0.1),
     ("two_kernel_path", 1200, 64, 8, 64, 8, 0.05),
+    ("whole_token_blocks_last_size", 1024, 4096, 8, 64, 8, 0.05),   # 8192 copies
+    ("pair_blocks_first_size", 1025, 4096, 8, 64, 8, 0.05),         # 8200 copies
     ("max_topk", 24, 64, 64, 512, 256, 0.0),
     ("tile_groups_wave_form", 9000, 16, 8, 64, 8, 0.05),     # k divides 64: ballot test
     ("tile_groups_k6", 12000, 16, 6, 36, 6, 0.05),           # k = 6: ids re-read
-    # rows of 8 KB and more: two copies per copy-kernel block
-    ("pairs_region_sums_16", 400, 4096, 8, 64, 16, 0.05),    # regions = 2 x copies
-    ("pairs_region_sums", 300, 4104, 7, 28, 4, 0.1),         # fewer regions, ragged row
-    ("pairs_copy_sums_32_regions", 300, 4096, 8, 64, 32, 0.05),   # regions > 2 x copies
+    # rows of 8 KB and more, above 8192 copies: two copies per copy-kernel block
+    ("pairs_region_sums_16", 1100, 4096, 8, 64, 16, 0.05),   # regions = 2 x copies
+    ("pairs_region_sums", 1200, 4104, 7, 28, 4, 0.1),        # fewer regions, ragged row
+    ("pairs_copy_sums_32_regions", 1100, 4096, 8, 64, 32, 0.05),  # regions > 2 x copies
     ("copy_sums_small_rows", 1200, 64, 4, 128, 64, 0.05),    # whole-token blocks, per-copy sums
 ]
 
