@@ -1221,6 +1221,7 @@ constexpr int kCopiesPerBlock = 2;
 constexpr int kCopiesPerBlockFp8 = 4;
 constexpr int64_t kOnePassFp8WholeTokenItems = 8192;
 constexpr int64_t kRegionWholeTokenItems = 8192;
+constexpr int64_t kRegionWholeTokenItemsFp8 = 16384;
 // Smaller rows (under 8 KB of bf16) keep one block per token: after a cache-
 // evicting read, T = 4096, H = 2048, top-8 copies ran at 48.8 % of the HBM
 // peak split in pairs against 60.8 % whole (T = 32768: 54.9 % against 68.7 %;
@@ -1431,13 +1432,18 @@ hipError_t launch_dispatch_copy(const DispatchArgs &args, hipStream_t s) {
     // sizes unchanged; 4 copies per block measured the same at T = 512 but
     // 0.8 us slower at T = 448.
     // The routed copy of the per-region layout takes a whole token per block
-    // up to kRegionWholeTokenItems copies (H = 7168, top-8, step / dispatch
-    // after a cache-evicting read, us, three runs each: 640 tokens
-    // 25.4 / 19.1 -> 25.2 / 17.1; 1024 tokens 37.5 / 24.6 -> 37.1 / 22.8;
-    // fp8 1024 tokens 31.2 / 17.8 -> 30.9 / 17.4, 640 tokens level).
+    // up to kRegionWholeTokenItems copies, the fp8 payload up to
+    // kRegionWholeTokenItemsFp8 (H = 7168, top-8, step / dispatch after a
+    // cache-evicting read, us, three runs each: 640 tokens 25.4 / 19.1 ->
+    // 25.2 / 17.1; 1024 tokens 37.5 / 24.6 -> 37.1 / 22.8; 1536 tokens
+    // 51.9 / 31.7 -> 52.9 / 32.9 and 2048 tokens 75.5 / 39.4 -> 76.8 / 41.4
+    // stay in pairs; fp8 1024 tokens 31.2 / 17.8 -> 30.9 / 17.4, 1536
+    // tokens 43.3 / 23.8 -> 43.6 / 21.1, 2048 tokens 64.4 / 27.8 ->
+    // 64.2 / 25.1).
     const int64_t items = (int64_t)a.T * a.k;
     const bool small_long = dispatch_is_small(a.T, a.k) && items > kSmallItemsShort;
-    const bool region_whole = a.per_region && !dispatch_is_small(a.T, a.k) && items <= kRegionWholeTokenItems;
+    const bool region_whole = a.per_region && !dispatch_is_small(a.T, a.k) &&
+                              items <= (a.fp8 ? kRegionWholeTokenItemsFp8 : kRegionWholeTokenItems);
     const int c = (a.H < kSplitMinHidden || small_long || region_whole) ? MOE_MAX_TOP_K
                   : a.fp8 ? kCopiesPerBlockFp8 : kCopiesPerBlock;
     const int n = (a.k + c - 1) / c;

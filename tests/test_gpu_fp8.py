@@ -80,10 +80,11 @@ def test_fp8_split_blocks(k, many):
     fp8_check(x, ids, E, ep, T, layout="region")
 
 
-@pytest.mark.parametrize("T", [1024, 1025])
-def test_fp8_block_sizes_around_8192_copies(T):
-    # up to 8192 copies a whole token per block (the single pass per copy,
-    # the routed copy per region), four copies per block above
+@pytest.mark.parametrize("T", [1024, 1025, 2048, 2049])
+def test_fp8_block_sizes_at_the_whole_token_limits(T):
+    # a whole token per block up to 8192 copies in the single pass (per
+    # copy) and up to 16384 in the routed copy (per region), four copies
+    # per block above
     H, k, E, ep = 4096, 8, 64, 8
     say("fp8 block sizes", T)
     rng = np.random.default_rng(300 + T)
