@@ -1221,7 +1221,7 @@ constexpr int kCopiesPerBlock = 2;
 constexpr int kCopiesPerBlockFp8 = 4;
 constexpr int64_t kOnePassFp8WholeTokenItems = 8192;
 constexpr int64_t kRegionWholeTokenItems = 8192;
-constexpr int64_t kRegionWholeTokenItemsFp8 = 16384;
+constexpr int64_t kRegionWholeTokenItemsFp8 = 24576;
 // Smaller rows (under 8 KB of bf16) keep one block per token: after a cache-
 // evicting read, T = 4096, H = 2048, top-8 copies ran at 48.8 % of the HBM
 // peak split in pairs against 60.8 % whole (T = 32768: 54.9 % against 68.7 %;
@@ -1439,7 +1439,8 @@ hipError_t launch_dispatch_copy(const DispatchArgs &args, hipStream_t s) {
     // 51.9 / 31.7 -> 52.9 / 32.9 and 2048 tokens 75.5 / 39.4 -> 76.8 / 41.4
     // stay in pairs; fp8 1024 tokens 31.2 / 17.8 -> 30.9 / 17.4, 1536
     // tokens 43.3 / 23.8 -> 43.6 / 21.1, 2048 tokens 64.4 / 27.8 ->
-    // 64.2 / 25.1).
+    // 64.2 / 25.1, 3072 tokens 77.5 / 36.7 -> 76.7 / 36.5; at 4096 tokens
+    // four per block stay, 98.9 / 45.8 against 98.2 / 47.1).
     const int64_t items = (int64_t)a.T * a.k;
     const bool small_long = dispatch_is_small(a.T, a.k) && items > kSmallItemsShort;
     const bool region_whole = a.per_region && !dispatch_is_small(a.T, a.k) &&

@@ -80,10 +80,10 @@ def test_fp8_split_blocks(k, many):
     fp8_check(x, ids, E, ep, T, layout="region")
 
 
-@pytest.mark.parametrize("T", [1024, 1025, 2048, 2049])
+@pytest.mark.parametrize("T", [1024, 1025, 3072, 3073])
 def test_fp8_block_sizes_at_the_whole_token_limits(T):
     # a whole token per block up to 8192 copies in the single pass (per
-    # copy) and up to 16384 in the routed copy (per region), four copies
+    # copy) and up to 24576 in the routed copy (per region), four copies
     # per block above
     H, k, E, ep = 4096, 8, 64, 8
     say("fp8 block sizes", T)
